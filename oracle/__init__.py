@@ -1,0 +1,152 @@
+"""fp64 CPU oracle for fused attention — TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package. The GPU library never calls it and shares no code with it.
+
+The arithmetic lives in attn_oracle.c (plain loops, fp64, three-pass safe
+softmax with an explicit causal mask; its header gives the definition and
+the page citations). This wrapper only widens the stored inputs to float64
+exactly, builds the C file with gcc when needed, and marshals arrays.
+
+Inputs are numpy arrays: float32/float64 values, or uint16 arrays holding
+bfloat16 bit patterns. Outputs are float64.
+
+Parity pins live in tests/test_oracle_pins.py; every function here is pinned
+there (page-printed values, closed forms, a library special case, brute
+force on tiny inputs).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_attn_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = False) -> str:
+    """Compile attn_oracle.c into _attn_oracle.so (gcc, no FMA contraction)."""
+    if (not force and os.path.exists(_LIB_PATH)
+            and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC)):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+           "-fPIC", "-shared", "-pthread", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(build())
+            dp = ctypes.POINTER(ctypes.c_double)
+            ip = ctypes.POINTER(ctypes.c_int)
+            i, d = ctypes.c_int, ctypes.c_double
+            lib.oracle_prefill_causal.argtypes = [dp, dp, dp, i, i, i, i, i, d, ip, i,
+                                                  dp, dp, dp, i]
+            lib.oracle_decode_gqa.argtypes = [dp, dp, dp, i, i, i, i, i, i, d, dp, dp, dp, i]
+            lib.oracle_decode_mla.argtypes = [dp, dp, i, i, i, i, i, i, d, dp, dp, i]
+            for f in (lib.oracle_prefill_causal, lib.oracle_decode_gqa, lib.oracle_decode_mla):
+                f.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+def widen(x: np.ndarray) -> np.ndarray:
+    """Stored values → float64, exactly. uint16 means bfloat16 bit patterns."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        f32 = (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        return np.ascontiguousarray(f32, dtype=np.float64)
+    if x.dtype in (np.float32, np.float64):
+        return np.ascontiguousarray(x, dtype=np.float64)
+    raise TypeError("oracle inputs must be float32/float64 or bf16 bits (uint16)")
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def prefill_causal(q, k, v, scale, rows=None, return_p=False, threads=None):
+    """Causal prefill with N queries against N keys.
+
+    q [B,Hq,N,D], k/v [B,Hkv,N,D]. `rows` selects query rows to evaluate
+    (default: all). Returns (o [B,Hq,R,D], lse [B,Hq,R]) and p [B,Hq,R,N]
+    when return_p is set, R = len(rows).
+    """
+    q = np.asarray(q)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, D) and v.shape == (B, Hkv, N, D)
+    rows = np.arange(N, dtype=np.int32) if rows is None else np.asarray(rows, dtype=np.int32)
+    R = rows.shape[0]
+    if R < 1 or rows.min() < 0 or rows.max() >= N:
+        raise ValueError("query rows must lie in [0, N)")
+    q64 = widen(q[:, :, rows, :])
+    k64, v64 = widen(k), widen(v)
+    o = np.empty((B, Hq, R, D))
+    lse = np.empty((B, Hq, R))
+    p = np.empty((B, Hq, R, N)) if return_p else None
+    rc = _load().oracle_prefill_causal(
+        _ptr(q64), _ptr(k64), _ptr(v64), B, Hq, Hkv, N, D, float(scale),
+        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), R, _ptr(o), _ptr(lse),
+        _ptr(p) if p is not None else None, threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_prefill_causal rejected its arguments")
+    return (o, lse, p) if return_p else (o, lse)
+
+
+def decode_gqa(q, k_cache, v_cache, kv_len, scale, return_p=False, threads=None):
+    """Single-query decode. q [B,Hq,D]; caches [B,Hkv,kv_cap,D] (only the
+    first kv_len slots are read). Returns (o [B,Hq,D], lse [B,Hq]) [+ p]."""
+    q = np.asarray(q)
+    B, Hq, D = q.shape
+    _, Hkv, kv_cap, _ = k_cache.shape
+    q64 = widen(q)
+    # only the filled prefix is widened (and read)
+    k64 = widen(k_cache[:, :, :kv_len])
+    v64 = widen(v_cache[:, :, :kv_len])
+    o = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    p = np.empty((B, Hq, kv_len)) if return_p else None
+    rc = _load().oracle_decode_gqa(
+        _ptr(q64), _ptr(k64), _ptr(v64), B, Hq, Hkv, int(kv_len), int(kv_len), D,
+        float(scale), _ptr(o), _ptr(lse), _ptr(p) if p is not None else None,
+        threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_decode_gqa rejected its arguments")
+    return (o, lse, p) if return_p else (o, lse)
+
+
+def decode_mla_absorbed(q, ckv, kv_len, dv, scale, threads=None):
+    """Absorbed-MLA decode. q [B,Hq,Dqk]; ckv [B,kv_cap,Dqk]; key = whole
+    row, value = first dv channels. Returns (o [B,Hq,dv], lse [B,Hq])."""
+    q = np.asarray(q)
+    B, Hq, Dqk = q.shape
+    q64 = widen(q)
+    c64 = widen(ckv[:, :kv_len])
+    o = np.empty((B, Hq, dv))
+    lse = np.empty((B, Hq))
+    rc = _load().oracle_decode_mla(
+        _ptr(q64), _ptr(c64), B, Hq, int(kv_len), int(kv_len), Dqk, int(dv),
+        float(scale), _ptr(o), _ptr(lse), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_decode_mla rejected its arguments")
+    return o, lse

@@ -1,0 +1,272 @@
+/*
+ * attn_oracle.c — plain, slow fp64 CPU reference for scaled-dot-product
+ * attention. TEST INFRASTRUCTURE ONLY: it is called by the tests, by the
+ * smoke check and by the bench's CPU-baseline leg, never by the product path.
+ * It shares no code with the GPU library.
+ *
+ * Pages, cited by title and section:
+ *  [p1] "AI Infra 入门：RMSNorm、Softmax、Causal Mask、Sampling 的数学与底层优化"
+ *  [p2] "05 · Tích vô hướng, Softmax và toán của Attention" (inference-notes)
+ *  [p3] "MLA 矩阵乘法吸收的数值稳定性治理" (gsyq.cn)
+ *  [p4] "Bộ 06 · Bên trong model" (inference-notes revision cards)
+ *  [p5] "第11节：Attention 实现（Flash vs Fallback）" (minimind course notes)
+ *
+ * What it computes, for one query row q against keys K[0..n) and values
+ * V[0..n), all held exactly in double:
+ *
+ *   s_j  = scale · Σ_t q_t · K_jt        dot product, ÷√d folded into scale
+ *                                        [p2] §1, [p5] §4
+ *   s_j  = −∞ where the explicit mask is set (future key j > i)
+ *                                        [p1] §3, [p4] Q2, [p5] §3
+ *   pass 1  m   = max_j s_j              safe softmax, [p1] §2, [p4] Q1
+ *   pass 2  ℓ   = Σ_j exp(s_j − m)
+ *   pass 3  P_j = exp(s_j − m) / ℓ ;  O_d = Σ_j P_j · V_jd     [p2] §3
+ *   LSE = m + ln ℓ   natural log, so softmax_j = exp(s_j − LSE)  [p1] §3
+ *
+ * These are the three passes of the safe softmax (maximum, denominator,
+ * result) that [p1] §3 contrasts with the one-pass online form: the oracle
+ * states the definition, the GPU kernels implement the online algorithm.
+ *
+ * Prefill builds a dense boolean mask M[r][j] = (j > row_r) for the rows it
+ * evaluates (the full N×N matrix when all rows are asked for) and sets the
+ * score to −∞ where it is set, in the order of the fallback flow of [p5] §6
+ * (scores, causal mask, softmax, weighted values; no padding, no dropout).
+ * Decode uses no mask (the single query sees only history, [p1] §3) and
+ * reads only the first kv_len cache slots, never unfilled ones ([p4] Q3).
+ *
+ * GQA: query head hq reads K/V head hq / (Hq/Hkv): contiguous groups of
+ * Hq/Hkv query heads share one K/V head ([p2] §4).
+ * MLA absorbed: one latent head shared by every query head; the key is the
+ * whole Dqk-wide row (latent | rope), the value its first Dv channels
+ * ([p3] §一, §三).
+ *
+ * Parallelism: rows are independent; they are split into contiguous ranges
+ * over `threads` POSIX threads. Summation order inside a row is fixed
+ * (ascending t, ascending j), so results do not depend on the thread count.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared -pthread -lm (no fused
+ * multiply-add contraction, no fast-math reassociation).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* One query row against n keys (three-pass safe softmax). `mask` is NULL or
+ * n flags (nonzero = masked). `s` is caller scratch of n doubles. `p_out`
+ * is NULL or n doubles receiving the softmax weights. */
+static void attend_row(const double *q, const double *k, long k_stride, int dk,
+                       const double *v, long v_stride, int dv, int n,
+                       const unsigned char *mask, double scale, double *s,
+                       double *o, double *lse, double *p_out)
+{
+    for (int j = 0; j < n; ++j) {
+        double dot = 0.0;
+        const double *kj = k + (long)j * k_stride;
+        for (int t = 0; t < dk; ++t)
+            dot += q[t] * kj[t];
+        s[j] = scale * dot;
+        if (mask && mask[j])
+            s[j] = -INFINITY;
+    }
+    /* pass 1: row maximum */
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j)
+        if (s[j] > m)
+            m = s[j];
+    /* pass 2: denominator */
+    double l = 0.0;
+    for (int j = 0; j < n; ++j)
+        l += exp(s[j] - m);
+    /* pass 3: normalised weights and weighted sum of values */
+    for (int d = 0; d < dv; ++d)
+        o[d] = 0.0;
+    for (int j = 0; j < n; ++j) {
+        double p = exp(s[j] - m) / l;
+        if (p_out)
+            p_out[j] = p;
+        const double *vj = v + (long)j * v_stride;
+        for (int d = 0; d < dv; ++d)
+            o[d] += p * vj[d];
+    }
+    *lse = m + log(l);
+}
+
+/* ------------------------------------------------------------ threading --- */
+typedef void (*row_fn)(void *ctx, long unit, double *scratch);
+
+typedef struct {
+    row_fn fn;
+    void *ctx;
+    long begin, end;
+    int scratch_n;
+} range_job;
+
+static void *run_range(void *arg)
+{
+    range_job *job = (range_job *)arg;
+    double *scratch = (double *)malloc(sizeof(double) * (size_t)(job->scratch_n > 0 ? job->scratch_n : 1));
+    if (!scratch)
+        return (void *)1;
+    for (long u = job->begin; u < job->end; ++u)
+        job->fn(job->ctx, u, scratch);
+    free(scratch);
+    return NULL;
+}
+
+static int run_units(row_fn fn, void *ctx, long units, int scratch_n, int threads)
+{
+    if (threads < 1)
+        threads = 1;
+    if (threads > units)
+        threads = units > 0 ? (int)units : 1;
+    range_job *jobs = (range_job *)calloc((size_t)threads, sizeof(range_job));
+    pthread_t *tids = (pthread_t *)calloc((size_t)threads, sizeof(pthread_t));
+    if (!jobs || !tids) {
+        free(jobs);
+        free(tids);
+        return -1;
+    }
+    int rc = 0;
+    for (int t = 0; t < threads; ++t) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].begin = units * t / threads;
+        jobs[t].end = units * (t + 1) / threads;
+        jobs[t].scratch_n = scratch_n;
+    }
+    for (int t = 1; t < threads; ++t)
+        if (pthread_create(&tids[t], NULL, run_range, &jobs[t]) != 0)
+            rc = -1;
+    if (run_range(&jobs[0]) != NULL)
+        rc = -1;
+    for (int t = 1; t < threads; ++t) {
+        void *ret = NULL;
+        pthread_join(tids[t], &ret);
+        if (ret != NULL)
+            rc = -1;
+    }
+    free(jobs);
+    free(tids);
+    return rc;
+}
+
+/* --------------------------------------------------------------- prefill --- */
+typedef struct {
+    const double *q, *k, *v;
+    int B, Hq, Hkv, N, D, n_rows;
+    double scale;
+    const unsigned char *mask; /* [n_rows][N] */
+    double *o, *lse, *p;
+} prefill_ctx;
+
+static void prefill_unit(void *vctx, long unit, double *scratch)
+{
+    prefill_ctx *c = (prefill_ctx *)vctx;
+    long r = unit % c->n_rows;
+    long bh = unit / c->n_rows;
+    int hq = (int)(bh % c->Hq);
+    int b = (int)(bh / c->Hq);
+    int hkv = hq / (c->Hq / c->Hkv);
+    const double *q = c->q + ((long)bh * c->n_rows + r) * c->D;
+    const double *k = c->k + ((long)b * c->Hkv + hkv) * (long)c->N * c->D;
+    const double *v = c->v + ((long)b * c->Hkv + hkv) * (long)c->N * c->D;
+    attend_row(q, k, c->D, c->D, v, c->D, c->D, c->N, c->mask + r * (long)c->N,
+               c->scale, scratch, c->o + ((long)bh * c->n_rows + r) * c->D,
+               c->lse + (long)bh * c->n_rows + r,
+               c->p ? c->p + ((long)bh * c->n_rows + r) * c->N : NULL);
+}
+
+/* Causal prefill, N queries against N keys (mask M[i][j] = j > i).
+ * q:   [B][Hq][n_rows][D]  — only the evaluated rows, in `rows` order
+ * k,v: [B][Hkv][N][D]
+ * rows: n_rows query indices in [0, N)
+ * o: [B][Hq][n_rows][D], lse: [B][Hq][n_rows], p: NULL or [B][Hq][n_rows][N]
+ * Returns 0, or -1 on bad arguments / allocation failure. */
+int oracle_prefill_causal(const double *q, const double *k, const double *v,
+                          int B, int Hq, int Hkv, int N, int D, double scale,
+                          const int *rows, int n_rows, double *o, double *lse,
+                          double *p, int threads)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1 || n_rows < 1 || Hq % Hkv)
+        return -1;
+    unsigned char *mask = (unsigned char *)malloc((size_t)n_rows * (size_t)N);
+    if (!mask)
+        return -1;
+    for (long r = 0; r < n_rows; ++r) {
+        if (rows[r] < 0 || rows[r] >= N) {
+            free(mask);
+            return -1;
+        }
+        for (int j = 0; j < N; ++j)
+            mask[r * N + j] = (unsigned char)(j > rows[r]);
+    }
+    prefill_ctx c = {q, k, v, B, Hq, Hkv, N, D, n_rows, scale, mask, o, lse, p};
+    int rc = run_units(prefill_unit, &c, (long)B * Hq * n_rows, N, threads);
+    free(mask);
+    return rc;
+}
+
+/* ------------------------------------------------------------ GQA decode --- */
+typedef struct {
+    const double *q, *k, *v;
+    int B, Hq, Hkv, kv_len, kv_cap, D;
+    double scale;
+    double *o, *lse, *p;
+} decode_ctx;
+
+static void decode_unit(void *vctx, long unit, double *scratch)
+{
+    decode_ctx *c = (decode_ctx *)vctx;
+    int hq = (int)(unit % c->Hq);
+    int b = (int)(unit / c->Hq);
+    int hkv = hq / (c->Hq / c->Hkv);
+    const double *k = c->k + ((long)b * c->Hkv + hkv) * (long)c->kv_cap * c->D;
+    const double *v = c->v + ((long)b * c->Hkv + hkv) * (long)c->kv_cap * c->D;
+    attend_row(c->q + unit * c->D, k, c->D, c->D, v, c->D, c->D, c->kv_len, NULL,
+               c->scale, scratch, c->o + unit * c->D, c->lse + unit,
+               c->p ? c->p + unit * c->kv_len : NULL);
+}
+
+/* Single-query decode over a K/V cache filled to kv_len (no mask).
+ * q: [B][Hq][D]; k,v: [B][Hkv][kv_cap][D]; o: [B][Hq][D]; lse: [B][Hq];
+ * p: NULL or [B][Hq][kv_len]. */
+int oracle_decode_gqa(const double *q, const double *k, const double *v,
+                      int B, int Hq, int Hkv, int kv_len, int kv_cap, int D,
+                      double scale, double *o, double *lse, double *p, int threads)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv || kv_len < 1 || kv_len > kv_cap)
+        return -1;
+    decode_ctx c = {q, k, v, B, Hq, Hkv, kv_len, kv_cap, D, scale, o, lse, p};
+    return run_units(decode_unit, &c, (long)B * Hq, kv_len, threads);
+}
+
+/* ----------------------------------------------------- MLA absorbed decode --- */
+typedef struct {
+    const double *q, *c;
+    int B, Hq, kv_len, kv_cap, Dqk, Dv;
+    double scale;
+    double *o, *lse;
+} mla_ctx;
+
+static void mla_unit(void *vctx, long unit, double *scratch)
+{
+    mla_ctx *c = (mla_ctx *)vctx;
+    int b = (int)(unit / c->Hq);
+    const double *lat = c->c + (long)b * c->kv_cap * c->Dqk;
+    /* key = the whole row (latent | rope); value = its first Dv channels */
+    attend_row(c->q + unit * c->Dqk, lat, c->Dqk, c->Dqk, lat, c->Dqk, c->Dv,
+               c->kv_len, NULL, c->scale, scratch, c->o + unit * c->Dv,
+               c->lse + unit, NULL);
+}
+
+/* q: [B][Hq][Dqk]; ckv: [B][kv_cap][Dqk]; o: [B][Hq][Dv]; lse: [B][Hq]. */
+int oracle_decode_mla(const double *q, const double *ckv, int B, int Hq,
+                      int kv_len, int kv_cap, int Dqk, int Dv, double scale,
+                      double *o, double *lse, int threads)
+{
+    if (B < 1 || Hq < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk || kv_len < 1 || kv_len > kv_cap)
+        return -1;
+    mla_ctx c = {q, ckv, B, Hq, kv_len, kv_cap, Dqk, Dv, scale, o, lse};
+    return run_units(mla_unit, &c, (long)B * Hq, kv_len, threads);
+}

@@ -1,0 +1,67 @@
+"""Seeded generators: storage rounding, determinism, workload structure."""
+import numpy as np
+import torch
+
+import workloads
+
+
+def test_bf16_rounding_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        np.float32([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3.0e-39, 65504.0])])
+    ours = workloads.round_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    back = workloads.bf16_bits_as_f32(ours)
+    np.testing.assert_array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_generators_are_deterministic():
+    a = workloads.gen_prefill(1, 4, 2, 33, 16, seed=5)
+    b = workloads.gen_prefill(1, 4, 2, 33, 16, seed=5)
+    c = workloads.gen_prefill(1, 4, 2, 33, 16, seed=6)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v)):
+        np.testing.assert_array_equal(x, y)
+    assert not np.array_equal(a.q, c.q)
+
+
+def test_outlier_rows_are_exactly_scaled():
+    base = workloads.gen_prefill(1, 4, 2, 1000, 32, seed=9)
+    out = workloads.gen_prefill(1, 4, 2, 1000, 32, seed=9, outlier_frac=0.01, outlier_mult=8.0)
+    assert out.outlier_rows.shape == (1, 2, 10)
+    for h in range(2):
+        sel = out.outlier_rows[0, h]
+        assert len(set(sel.tolist())) == 10
+        kb = workloads.bf16_bits_as_f32(base.k[0, h])
+        ko = workloads.bf16_bits_as_f32(out.k[0, h])
+        np.testing.assert_array_equal(ko[sel], kb[sel] * 8)
+        rest = np.setdiff1d(np.arange(1000), sel)
+        np.testing.assert_array_equal(ko[rest], kb[rest])
+    np.testing.assert_array_equal(out.q, base.q)
+
+
+def test_decode_poison_tail():
+    w = workloads.gen_decode_gqa(2, 8, 2, 100, D=64, kv_cap=128, seed=1)
+    assert np.all(w.k[:, :, 100:] == workloads.BF16_NAN_BITS)
+    assert np.all(np.isfinite(workloads.bf16_bits_as_f32(w.k[:, :, :100])))
+
+
+def test_mla_balanced_storage_is_unit_range():
+    """Channel balancing leaves the stored latent channels at unit scale even
+    though the model-side magnitudes span 1e-4..1e2."""
+    w = workloads.gen_decode_mla(1, 8, 256, seed=3)
+    assert w.s.min() >= 1e-4 and w.s.max() <= 1e2
+    assert np.log10(w.s.max() / w.s.min()) > 4
+    c = workloads.bf16_bits_as_f32(w.ckv[0, :256, :512])
+    rms = np.sqrt((c.astype(np.float64) ** 2).mean(0))
+    assert 0.8 < rms.min() and rms.max() < 1.25
+
+
+def test_named_workload_shapes():
+    assert workloads.WORKLOADS["decode_gqa_llama3_8b_4k"]["Hq"] == 32
+    w = workloads.make("decode_gqa_llama3_8b_4k", B=1, kv_len=64)
+    assert w.q.shape == (1, 32, 128) and w.k.shape == (1, 8, 64, 128)
+    # algorithmic bytes of the full GQA decode workload
+    assert workloads.decode_gqa_bytes(8, 32, 8, 4096, 128) == 134_349_824
+    assert workloads.prefill_causal_flops(4, 32, 4096, 128) == 549_890_031_616
+    assert workloads.decode_mla_bytes(16, 128, 32768, 576, 512) == 608_444_416

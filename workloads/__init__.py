@@ -1,0 +1,271 @@
+"""Seeded synthetic inputs for the attention hot path.
+
+This module is shared by the CPU oracle (tests, bench baseline) and the GPU
+path. It holds no attention arithmetic: only random draws, storage rounding
+to bfloat16, the fixed shapes of the five workloads, and the algorithmic
+flop / byte counts used to price a launch against a roofline.
+
+Every array is drawn with numpy's PCG64 from a fixed seed. Inputs are N(0,1)
+draws in float32, rounded once to bfloat16 with round-to-nearest-even when
+the workload stores bf16. bf16 arrays are returned as their raw uint16 bit
+patterns, so both sides start from exactly the same stored values.
+
+Workload shapes follow the pages:
+  * 05 · Tích vô hướng, Softmax và toán của Attention (inference-notes), §4:
+    Llama-3-8B decode, 32 query heads sharing 8 K/V heads, d=128, 4096-token
+    context, 128 KiB of K/V per token.
+  * MLA 矩阵乘法吸收的数值稳定性治理 (gsyq.cn), §一 and §二.1: 512-dim latent
+    cache, per-channel magnitudes spanning 1e-4..1e2, a static diagonal
+    channel scale S applied as q·S⁻¹ and S·c.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16_NAN_BITS = np.uint16(0x7FC0)
+
+
+# ---------------------------------------------------------------- storage ---
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 (or float64) values to bfloat16, nearest-even; return bits.
+
+    Inputs must be finite. float64 is first rounded to float32; the draws
+    here are float32 already, so that step is exact for them.
+    """
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    u = x32.view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+def _rng(seed: int, n_children: int):
+    return [np.random.Generator(np.random.PCG64(s))
+            for s in np.random.SeedSequence(seed).spawn(n_children)]
+
+
+def _normal(rng, shape, chunk=1 << 24) -> np.ndarray:
+    """N(0,1) float32 draws, generated in chunks to bound peak memory."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    return out.reshape(shape)
+
+
+def _normal_bf16(rng, shape, chunk=1 << 24) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = round_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+# -------------------------------------------------------------- workloads ---
+@dataclass
+class Prefill:
+    """Causal prefill inputs. q [B,Hq,N,D]; k, v [B,Hkv,N,D]; D innermost."""
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    D: int
+    dtype: str            # "bf16" (uint16 bits) or "f32"
+    scale: float
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    outlier_rows: np.ndarray | None = None   # [B,Hkv,n_out] key rows scaled ×8
+
+
+@dataclass
+class DecodeGQA:
+    """Single-query GQA decode. q [B,Hq,D]; k_cache, v_cache [B,Hkv,kv_cap,D] bf16."""
+    B: int
+    Hq: int
+    Hkv: int
+    kv_len: int
+    kv_cap: int
+    D: int
+    scale: float
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+
+
+@dataclass
+class DecodeMLA:
+    """Absorbed MLA decode. q [B,Hq,Dqk]; ckv [B,kv_cap,Dqk] bf16.
+
+    Each row is [latent (Dv) | rope (Dqk-Dv)]. The latent part is stored
+    channel-balanced: q holds q̃·S⁻¹ and ckv holds S·c, S = diag(s).
+    V is the latent part of ckv (its first Dv channels).
+    """
+    B: int
+    Hq: int
+    kv_len: int
+    kv_cap: int
+    Dqk: int
+    Dv: int
+    scale: float
+    q: np.ndarray
+    ckv: np.ndarray
+    s: np.ndarray = field(default=None)   # channel scale, [Dv] float64
+
+
+def gen_prefill(B, Hq, Hkv, N, D, dtype="bf16", seed=0, scale=None,
+                outlier_frac=0.0, outlier_mult=8.0) -> Prefill:
+    """Q, K, V i.i.d. N(0,1). With outlier_frac > 0, per (b, hkv) a seeded
+    set of round(outlier_frac·N) distinct key rows is multiplied by
+    outlier_mult after rounding (a power of two keeps that exact)."""
+    rq, rk, rv, ro = _rng(seed, 4)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if dtype == "bf16":
+        q = _normal_bf16(rq, (B, Hq, N, D))
+        k = _normal_bf16(rk, (B, Hkv, N, D))
+        v = _normal_bf16(rv, (B, Hkv, N, D))
+    elif dtype == "f32":
+        q = _normal(rq, (B, Hq, N, D))
+        k = _normal(rk, (B, Hkv, N, D))
+        v = _normal(rv, (B, Hkv, N, D))
+    else:
+        raise ValueError(dtype)
+    rows = None
+    n_out = int(round(outlier_frac * N))
+    if n_out > 0:
+        rows = np.stack([np.stack([np.sort(ro.choice(N, n_out, replace=False))
+                                   for _ in range(Hkv)]) for _ in range(B)])
+        for b in range(B):
+            for h in range(Hkv):
+                sel = rows[b, h]
+                if dtype == "bf16":
+                    k[b, h, sel] = round_to_bf16_bits(bf16_bits_as_f32(k[b, h, sel]) * outlier_mult)
+                else:
+                    k[b, h, sel] = k[b, h, sel] * np.float32(outlier_mult)
+    return Prefill(B, Hq, Hkv, N, D, dtype, float(scale), q, k, v, rows)
+
+
+def gen_decode_gqa(B, Hq, Hkv, kv_len, D=128, kv_cap=None, seed=0, scale=None,
+                   poison_tail=True) -> DecodeGQA:
+    """One query token per sequence; K/V cache of capacity kv_cap filled to
+    kv_len. Slots past kv_len hold NaN when poison_tail is set, so a kernel
+    that reads them produces NaN."""
+    if kv_cap is None:
+        kv_cap = kv_len
+    rq, rk, rv = _rng(seed, 3)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    q = _normal_bf16(rq, (B, Hq, D))
+    k = np.empty((B, Hkv, kv_cap, D), np.uint16)
+    v = np.empty((B, Hkv, kv_cap, D), np.uint16)
+    k[:, :, :kv_len] = _normal_bf16(rk, (B, Hkv, kv_len, D))
+    v[:, :, :kv_len] = _normal_bf16(rv, (B, Hkv, kv_len, D))
+    fill = BF16_NAN_BITS if poison_tail else np.uint16(0)
+    k[:, :, kv_len:] = fill
+    v[:, :, kv_len:] = fill
+    return DecodeGQA(B, Hq, Hkv, kv_len, kv_cap, D, float(scale), q, k, v)
+
+
+def gen_decode_mla(B, Hq, kv_len, Dqk=576, Dv=512, kv_cap=None, seed=0,
+                   scale=None, mag_lo=1e-4, mag_hi=1e2, poison_tail=True) -> DecodeMLA:
+    """Absorbed-MLA decode inputs, channel-balanced before storage.
+
+    s_k = 10^U(log10 mag_lo, log10 mag_hi) per latent channel. The model-side
+    absorbed query is q̃ = q_u ⊙ s and the latent is c = c_u ⊘ s (so logits
+    stay O(1)); what is stored is bf16(q̃ ⊙ s⁻¹) and bf16(s ⊙ c). The rope
+    channels (Dqk - Dv of them) are N(0,1) and not scaled. Default scale is
+    1/√192 (128 no-rope + 64 rope dims of the pre-absorption head).
+    """
+    if kv_cap is None:
+        kv_cap = kv_len
+    rq, rc, rs = _rng(seed, 3)
+    if scale is None:
+        scale = 1.0 / math.sqrt(128 + 64)
+    s = 10.0 ** rs.uniform(math.log10(mag_lo), math.log10(mag_hi), size=Dv)
+    qn = _normal(rq, (B, Hq, Dqk)).astype(np.float64)
+    q_tilde = qn[..., :Dv] * s                      # raw absorbed query
+    qn[..., :Dv] = q_tilde / s                      # q̃·S⁻¹
+    q = round_to_bf16_bits(qn)
+    ckv = np.empty((B, kv_cap, Dqk), np.uint16)
+    for b in range(B):                              # per batch to bound memory
+        cn = _normal(rc, (kv_len, Dqk)).astype(np.float64)
+        c_raw = cn[:, :Dv] / s                      # raw latent
+        cn[:, :Dv] = s * c_raw                      # S·c
+        ckv[b, :kv_len] = round_to_bf16_bits(cn)
+    ckv[:, kv_len:] = BF16_NAN_BITS if poison_tail else np.uint16(0)
+    return DecodeMLA(B, Hq, kv_len, kv_cap, Dqk, Dv, float(scale), q, ckv, s)
+
+
+# ------------------------------------------------- the five named workloads ---
+WORKLOADS = {
+    "prefill_f32_tiny": dict(
+        kind="prefill", B=1, Hq=2, Hkv=2, N=64, D=64, dtype="f32", seed=1001,
+        scale=1.0 / 8.0),
+    "decode_gqa_llama3_8b_4k": dict(
+        kind="decode_gqa", B=8, Hq=32, Hkv=8, kv_len=4096, D=128, seed=1002,
+        scale=1.0 / math.sqrt(128)),
+    "prefill_bf16_4k": dict(
+        kind="prefill", B=4, Hq=32, Hkv=8, N=4096, D=128, dtype="bf16", seed=1003,
+        scale=1.0 / math.sqrt(128)),
+    "prefill_bf16_32k_outliers": dict(
+        kind="prefill", B=1, Hq=32, Hkv=8, N=32768, D=128, dtype="bf16", seed=1004,
+        scale=1.0 / math.sqrt(128), outlier_frac=0.01, outlier_mult=8.0),
+    "decode_mla_absorbed_32k": dict(
+        kind="decode_mla", B=16, Hq=128, kv_len=32768, Dqk=576, Dv=512, seed=1005,
+        scale=1.0 / math.sqrt(128 + 64)),
+}
+
+
+def make(name: str, **overrides):
+    """Build a named workload (overrides change shapes for scaled-down cases)."""
+    cfg = dict(WORKLOADS[name])
+    cfg.update(overrides)
+    kind = cfg.pop("kind")
+    if kind == "prefill":
+        return gen_prefill(**cfg)
+    if kind == "decode_gqa":
+        return gen_decode_gqa(**cfg)
+    if kind == "decode_mla":
+        return gen_decode_mla(**cfg)
+    raise ValueError(kind)
+
+
+# ------------------------------------------ algorithmic work per launch ---
+def prefill_causal_flops(B, Hq, N, D):
+    """Flops of the unmasked (i, j≤i) pairs only: 2·D for q·k plus 2·D for
+    p·v per pair. Skipped tiles and masked diagonal entries are not counted."""
+    return 4 * D * (N * (N + 1) // 2) * B * Hq
+
+
+def prefill_min_bytes(B, Hq, Hkv, N, D, elt=2):
+    """Compulsory HBM bytes: Q, K, V read once, O written once, fp32 LSE."""
+    return elt * N * D * (2 * B * Hq + 2 * B * Hkv) + 4 * B * Hq * N
+
+
+def decode_gqa_bytes(B, Hq, Hkv, kv_len, D, elt=2):
+    """K and V rows up to kv_len read once, q read, O written, fp32 LSE."""
+    return elt * (2 * B * Hkv * kv_len * D + 2 * B * Hq * D) + 4 * B * Hq
+
+
+def decode_gqa_flops(B, Hq, kv_len, D):
+    return 4 * B * Hq * kv_len * D
+
+
+def decode_mla_bytes(B, Hq, kv_len, Dqk, Dv, elt=2):
+    """Latent rows read once (V is a prefix of each row), q, O, fp32 LSE."""
+    return elt * (B * kv_len * Dqk + B * Hq * Dqk + B * Hq * Dv) + 4 * B * Hq
+
+
+def decode_mla_flops(B, Hq, kv_len, Dqk, Dv):
+    return 2 * B * Hq * kv_len * (Dqk + Dv)
