@@ -1,0 +1,162 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) fused-attention library libattn.so.
+ *
+ * Every entry point computes scaled-dot-product attention with a one-pass
+ * online softmax and also returns the per-row log-sum-exp:
+ *
+ *   O_i   = Σ_j softmax_j(scale · q_i·k_j + mask_ij) · v_j
+ *   LSE_i = ln Σ_j exp(scale · q_i·k_j + mask_ij)        (natural log)
+ *
+ * The pages that define the operation (cited by title and section):
+ *  - "05 · Tích vô hướng, Softmax và toán của Attention" (inference-notes):
+ *    §1 dot product and the 1/√d scale, §2 softmax, §3 one head one token,
+ *    §4 GQA (four query heads share one K/V head), §6 online softmax.
+ *  - "AI Infra 入门：RMSNorm、Softmax、Causal Mask、Sampling 的数学与底层优化":
+ *    §3 causal mask (−∞ for j > i; tiles above the diagonal skipped, only
+ *    diagonal tiles masked), online softmax with running max and running
+ *    sum rescaled by exp(m_old − m_new), LSE and split-K merging.
+ *  - "Bộ 06 · Bên trong model": Q2 (−∞ not 0; cached K/V are exact),
+ *    Q3 (attend only the filled part of a preallocated cache).
+ *  - "MLA 矩阵乘法吸收的数值稳定性治理": §一 absorption into the query,
+ *    §二 channel scale S and FP32 on-chip accumulation, §五 low-precision
+ *    storage with high-precision accumulation.
+ *
+ * Conventions shared by all entry points
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    owned by the caller, contiguous, innermost dimension last (row-major).
+ *  - bf16 tensors use the bfloat16 storage format; all products are
+ *    accumulated in fp32 and the output is rounded once (round to nearest
+ *    even). LSE is fp32.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and runs
+ *    asynchronously; no entry point synchronises or allocates memory.
+ *  - Arguments are validated on the host before anything is enqueued. On
+ *    any non-OK status nothing is launched and no output is touched;
+ *    attn_last_error() then holds a description (thread-local).
+ *  - No C++ exception crosses this interface.
+ *  - NaN or Inf in the inputs propagate to the outputs; they are not
+ *    detected.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                  */
+    ATTN_ERR_BAD_SHAPE = 2,    /* a size is out of range or inconsistent      */
+    ATTN_ERR_UNSUPPORTED = 3,  /* valid but not implemented (dtype, head dim) */
+    ATTN_ERR_WORKSPACE = 4,    /* workspace missing or too small              */
+    ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} attn_status;
+
+typedef enum attn_dtype {
+    ATTN_BF16 = 0,
+    ATTN_FP32 = 1
+} attn_dtype;
+
+/*
+ * Causal prefill: N queries attend to the same N positions with the causal
+ * mask (key j is visible to query i iff j <= i).
+ *
+ *   q   [B, Hq,  N, D]   dtype
+ *   k   [B, Hkv, N, D]   dtype
+ *   v   [B, Hkv, N, D]   dtype
+ *   o   [B, Hq,  N, D]   dtype (output)
+ *   lse [B, Hq,  N]      fp32  (output, natural log)
+ *
+ * Query head hq uses K/V head hq / (Hq/Hkv) (contiguous GQA groups).
+ * dtype ATTN_BF16: D in {64, 128}; MFMA bf16 products, fp32 accumulation.
+ * dtype ATTN_FP32: D in {64, 128}; fp32 throughout.
+ * Errors: NULL pointer → ATTN_ERR_NULL_POINTER; B, Hq, Hkv, N < 1 or
+ * Hq % Hkv != 0 or a tensor above 2^31 elements → ATTN_ERR_BAD_SHAPE;
+ * other D or dtype → ATTN_ERR_UNSUPPORTED; launch failure → ATTN_ERR_HIP.
+ */
+attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
+                                const void *v, void *o, float *lse, int B,
+                                int Hq, int Hkv, int N, int D, float scale,
+                                hipStream_t stream);
+
+/*
+ * Single-query GQA decode over a bf16 K/V cache (no mask: the one query sees
+ * every cached position). Only the first kv_len slots are read; slots
+ * kv_len..kv_cap-1 are never touched (they may hold anything). kv_len counts
+ * the current token: its K/V must already be in the cache.
+ *
+ *   q        [B, Hq, D]               bf16
+ *   k_cache  [B, Hkv, kv_cap, D]      bf16
+ *   v_cache  [B, Hkv, kv_cap, D]      bf16
+ *   o        [B, Hq, D]               bf16 (output)
+ *   lse      [B, Hq]                  fp32 (output, natural log)
+ *   workspace: device memory of at least attn_decode_gqa_workspace_bytes()
+ *              bytes, zero-filled by the caller before its FIRST use. Each
+ *              call leaves its counters at zero again, so later calls need
+ *              no clearing. Calls that may run concurrently must not share a
+ *              workspace.
+ *
+ * The cache is split into chunks processed by separate workgroups, each
+ * producing a partial (O, running max, running sum); the partials are merged
+ * through their log-sum-exp by the last workgroup of each (b, K/V head) to
+ * finish. The split depends only on the shape, so results are bitwise
+ * reproducible.
+ * D must be 128 and Hq/Hkv at most 16.
+ * Errors: NULL pointer → ATTN_ERR_NULL_POINTER; B, Hq, Hkv < 1, Hq % Hkv,
+ * kv_len < 1 or kv_len > kv_cap → ATTN_ERR_BAD_SHAPE; other D or group size
+ * → ATTN_ERR_UNSUPPORTED; workspace NULL or too small → ATTN_ERR_WORKSPACE;
+ * launch failure → ATTN_ERR_HIP.
+ */
+attn_status attn_decode_gqa(const void *q, const void *k_cache,
+                            const void *v_cache, void *o, float *lse, int B,
+                            int Hq, int Hkv, int kv_len, int kv_cap, int D,
+                            float scale, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace attn_decode_gqa needs for this shape (0 if invalid). */
+size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len,
+                                       int D);
+
+/*
+ * Absorbed MLA decode: every query head attends to one shared latent cache.
+ * Each cached row is [latent (Dv) | rope (Dqk − Dv)]; the key is the whole
+ * row and the value is its latent part, so the value is read from the same
+ * bytes as the key. The query is the absorbed query (W_UK folded in) with
+ * its rope part appended. Channel balancing (query ·S⁻¹, latent ·S) is done
+ * by the caller before storage; O is returned in the same S-scaled latent
+ * space (S⁻¹ belongs to the output projection outside this call).
+ *
+ *   q    [B, Hq, Dqk]         bf16
+ *   ckv  [B, kv_cap, Dqk]     bf16 (only the first kv_len rows are read)
+ *   o    [B, Hq, Dv]          bf16 (output)
+ *   lse  [B, Hq]              fp32 (output, natural log)
+ *   workspace: as for attn_decode_gqa, sized by
+ *              attn_decode_mla_workspace_bytes().
+ *
+ * (Dqk, Dv) must be (576, 512); Hq must be a multiple of 16.
+ * All products accumulate in fp32; the output is rounded once.
+ * Errors as for attn_decode_gqa; other (Dqk, Dv) or Hq → ATTN_ERR_UNSUPPORTED.
+ */
+attn_status attn_decode_mla_absorbed(const void *q, const void *ckv, void *o,
+                                     float *lse, int B, int Hq, int kv_len,
+                                     int kv_cap, int Dqk, int Dv, float scale,
+                                     void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* Bytes of workspace attn_decode_mla_absorbed needs (0 if invalid). */
+size_t attn_decode_mla_workspace_bytes(int B, int Hq, int kv_len, int Dqk,
+                                       int Dv);
+
+/* Static, human-readable name of a status code. */
+const char *attn_status_string(attn_status s);
+
+/* Description of the last non-OK status returned on this thread ("" if none). */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_H */

@@ -1,0 +1,88 @@
+"""GQA and absorbed-MLA decode on the GPU (through the C ABI) against the
+fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import check_bf16, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gqa(gpu, w, ws=None):
+    o, lse = gpu.attn_decode_gqa(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), w.kv_len, w.scale,
+                                 ws=ws)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,kv_len,kv_cap", [
+    (1, 4, 1, 1, 8), (2, 8, 2, 5, 64), (2, 32, 8, 255, 300), (1, 8, 8, 256, 256),
+    (3, 16, 4, 257, 512), (2, 32, 8, 1000, 1024), (1, 16, 1, 4095, 4100),
+    (1, 32, 2, 3000, 3000), (4, 24, 8, 777, 800), (1, 2, 1, 70000, 70001)])
+def test_decode_gqa_matches_oracle(gpu, B, Hq, Hkv, kv_len, kv_cap):
+    """Ragged lengths, every group size 1..16 (3 is padded to 4), one and many
+    splits; slots past kv_len hold NaN and must never be read."""
+    w = workloads.gen_decode_gqa(B, Hq, Hkv, kv_len, D=128, kv_cap=kv_cap, seed=kv_len + Hq,
+                                 poison_tail=True)
+    o, lse = _gqa(gpu, w)
+    o_ref, lse_ref = oracle.decode_gqa(w.q, w.k, w.v, w.kv_len, w.scale)
+    check_bf16(host(o), o_ref, host(lse), lse_ref, "gqa %s" % ((B, Hq, Hkv, kv_len),))
+
+
+def test_decode_gqa_llama3_workload_and_repeat(gpu):
+    """The Llama-3-8B-shaped workload in full (B=8, 32/8 heads, 4096 keys);
+    three calls reusing one workspace give bit-identical results (the split
+    counters reset themselves)."""
+    w = workloads.make("decode_gqa_llama3_8b_4k")
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    outs = [gpu.attn_decode_gqa(q, k, v, w.kv_len, w.scale) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
+    o_ref, lse_ref = oracle.decode_gqa(w.q, w.k, w.v, w.kv_len, w.scale)
+    check_bf16(host(outs[0][0]), o_ref, host(outs[0][1]), lse_ref, "decode_gqa_llama3_8b_4k")
+
+
+def test_decode_matches_prefill_rows(gpu):
+    """A cached decode step for token t equals row t of a causal prefill over
+    the same tokens (earlier rows never see later tokens)."""
+    w = workloads.gen_prefill(1, 8, 2, 300, 128, dtype="bf16", seed=12)
+    o_p, l_p = gpu.attn_prefill_causal(dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v), w.scale)
+    for t in (0, 1, 63, 64, 299):
+        o_d, l_d = gpu.attn_decode_gqa(dev_bf16(w.q[:, :, t]), dev_bf16(w.k), dev_bf16(w.v), t + 1,
+                                       w.scale)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.prefill_causal(w.q, w.k, w.v, w.scale, rows=[t])
+        check_bf16(host(o_d), o_ref[:, :, 0], host(l_d), l_ref[:, :, 0], "decode t=%d" % t)
+        check_bf16(host(o_d), host(o_p[:, :, t]), host(l_d), host(l_p[:, :, t]), "vs prefill t=%d" % t)
+
+
+def _mla(gpu, w):
+    o, lse = gpu.attn_decode_mla_absorbed(dev_bf16(w.q), dev_bf16(w.ckv), w.kv_len, w.Dv, w.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("B,Hq,kv_len,kv_cap", [
+    (1, 16, 1, 32), (2, 16, 31, 64), (1, 128, 33, 40), (2, 32, 1000, 1024), (1, 128, 5000, 5000),
+    (1, 144, 70, 100)])
+def test_decode_mla_matches_oracle(gpu, B, Hq, kv_len, kv_cap):
+    w = workloads.gen_decode_mla(B, Hq, kv_len, kv_cap=kv_cap, seed=kv_len + Hq)
+    o, lse = _mla(gpu, w)
+    o_ref, lse_ref = oracle.decode_mla_absorbed(w.q, w.ckv, w.kv_len, w.Dv, w.scale)
+    check_bf16(host(o), o_ref, host(lse), lse_ref, "mla %s" % ((B, Hq, kv_len),))
+
+
+def test_decode_mla_32k_workload_sampled_batches(gpu):
+    """The full MLA workload (B=16, 128 heads, 32768 latent rows of 576,
+    balanced channels); every output finite; the oracle checks two batches."""
+    w = workloads.make("decode_mla_absorbed_32k")
+    o, lse = _mla(gpu, w)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    bs = [0, w.B - 1]
+    o_ref, lse_ref = oracle.decode_mla_absorbed(w.q[bs], w.ckv[bs], w.kv_len, w.Dv, w.scale)
+    check_bf16(host(o[bs]), o_ref, host(lse[bs]), lse_ref, "decode_mla_absorbed_32k")

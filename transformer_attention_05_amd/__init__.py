@@ -1,0 +1,198 @@
+"""MI355X (gfx950) fused attention: thin Python binding over libattn.so.
+
+The functions carry the names of the C ABI (include/attn.h) and do argument
+marshalling only: every step of attention runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream, nothing else. There is
+no fallback: if libattn.so is missing or fails to load, every call raises.
+
+    o, lse = attn_prefill_causal(q, k, v, scale)                  # [B,H,N,D]
+    o, lse = attn_decode_gqa(q, k_cache, v_cache, kv_len, scale)  # q [B,Hq,D]
+    o, lse = attn_decode_mla_absorbed(q, ckv, kv_len, 512, scale) # q [B,Hq,576]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_OK, ATTN_BF16, ATTN_FP32 = 0, 0, 1
+
+_lib = None
+_lock = threading.Lock()
+_workspaces: dict = {}
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from libattn.so (carries the status code)."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree libattn.so (built by build.py); raise if absent."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libattn.so not found at %s: build it with "
+                "`python -m transformer_attention_05_amd.build`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.attn_prefill_causal.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        lib.attn_decode_mla_absorbed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        lib.attn_decode_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.attn_decode_mla_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.attn_decode_gqa_workspace_bytes.restype = sz
+        lib.attn_decode_mla_workspace_bytes.restype = sz
+        for fn in (lib.attn_prefill_causal, lib.attn_decode_gqa, lib.attn_decode_mla_absorbed):
+            fn.restype = ctypes.c_int
+        lib.attn_status_string.argtypes = [i]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int, lib) -> None:
+    if status != ATTN_OK:
+        name = lib.attn_status_string(status).decode()
+        raise AttnError(status, "%s: %s" % (name, lib.attn_last_error().decode()))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %d-d tensor" % (name, ndim))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-initialised workspace of at least nbytes for (device, stream).
+
+    The kernels leave their counters at zero after every call, so one
+    buffer serves every later call on the same stream; calls on different
+    streams get different buffers.
+    """
+    dev = torch.device(device)
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def attn_prefill_causal(q, k, v, scale=None, out=None, lse=None):
+    """Causal prefill. q [B,Hq,N,D], k/v [B,Hkv,N,D] (bf16 or fp32, same
+    dtype). Returns (o [B,Hq,N,D] same dtype, lse [B,Hq,N] fp32)."""
+    lib = load()
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, dtype, 4)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, N, D] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "out", dtype, 4)
+    _need(l, "lse", torch.float32, 3)
+    st = lib.attn_prefill_causal(ATTN_BF16 if dtype == torch.bfloat16 else ATTN_FP32,
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
+                                 B, Hq, Hkv, N, D, float(scale), _stream(q.device))
+    _check(st, lib)
+    return o, l
+
+
+def attn_decode_gqa_workspace_bytes(B, Hq, Hkv, kv_len, D=128) -> int:
+    return int(load().attn_decode_gqa_workspace_bytes(B, Hq, Hkv, kv_len, D))
+
+
+def attn_decode_gqa(q, k_cache, v_cache, kv_len, scale=None, out=None, lse=None, ws=None):
+    """Single-query GQA decode. q [B,Hq,D] bf16; caches [B,Hkv,kv_cap,D] bf16
+    filled to kv_len. Returns (o [B,Hq,D] bf16, lse [B,Hq] fp32)."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, Hq, D = q.shape
+    _, Hkv, kv_cap, _ = k_cache.shape
+    if k_cache.shape != (B, Hkv, kv_cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, Hkv, kv_cap, D] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "out", torch.bfloat16, 3)
+    _need(l, "lse", torch.float32, 2)
+    need = lib.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, int(kv_len), D)
+    w = workspace(need, q.device) if ws is None else ws
+    st = lib.attn_decode_gqa(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
+                             B, Hq, Hkv, int(kv_len), kv_cap, D, float(scale),
+                             _ptr(w), w.numel() * w.element_size(), _stream(q.device))
+    _check(st, lib)
+    return o, l
+
+
+def attn_decode_mla_workspace_bytes(B, Hq, kv_len, Dqk=576, Dv=512) -> int:
+    return int(load().attn_decode_mla_workspace_bytes(B, Hq, kv_len, Dqk, Dv))
+
+
+def attn_decode_mla_absorbed(q, ckv, kv_len, dv=512, scale=None, out=None, lse=None, ws=None):
+    """Absorbed MLA decode. q [B,Hq,Dqk] bf16 (absorbed, channel-balanced
+    query | rope), ckv [B,kv_cap,Dqk] bf16 (balanced latent | rope). Value =
+    first dv channels of each cached row. Returns (o [B,Hq,dv] bf16, lse)."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(ckv, "ckv", torch.bfloat16, 3)
+    B, Hq, Dqk = q.shape
+    kv_cap = ckv.shape[1]
+    if ckv.shape != (B, kv_cap, Dqk):
+        raise ValueError("ckv must be [B, kv_cap, Dqk] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(128 + 64)
+    o = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "out", torch.bfloat16, 3)
+    _need(l, "lse", torch.float32, 2)
+    need = lib.attn_decode_mla_workspace_bytes(B, Hq, int(kv_len), Dqk, dv)
+    w = workspace(need, q.device) if ws is None else ws
+    st = lib.attn_decode_mla_absorbed(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), B, Hq, int(kv_len),
+                                      kv_cap, Dqk, dv, float(scale), _ptr(w),
+                                      w.numel() * w.element_size(), _stream(q.device))
+    _check(st, lib)
+    return o, l
+
+
+def status_string(status: int) -> str:
+    return load().attn_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().attn_last_error().decode()

@@ -1,0 +1,57 @@
+"""Build libattn.so in-tree with hipcc for gfx950.
+
+    python -m transformer_attention_05_amd.build
+
+Every source is compiled for gfx950 only, with packed-fp32 instruction
+selection disabled (-Xclang -target-feature -Xclang -packed-fp32-ops: the
+host pass warns that it does not know the feature, which is harmless).
+Objects go to _build/, the library to the package directory.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+ROOT = os.path.dirname(PKG)
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libattn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["attn_api.cpp", "decode_gqa.hip", "prefill_bf16.hip", "prefill_f32.hip",
+           "decode_mla.hip"]
+FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [l for l in (r.stdout + r.stderr).splitlines()
+            if "packed-fp32-ops" not in l and l.strip()]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, "\n".join(msgs)))
+    if verbose and msgs:
+        print("\n".join(msgs), file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libattn.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+                   check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

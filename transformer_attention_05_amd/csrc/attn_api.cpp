@@ -1,0 +1,161 @@
+// C-ABI entry points of libattn.so: argument validation on the host (nothing
+// is enqueued on error), status reporting, and dispatch to the gfx950 kernels.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status fail(attn_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+attn_status ok()
+{
+    g_last_error[0] = '\0';
+    return ATTN_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+constexpr long long kMaxElems = (1ll << 31) - 1;
+
+attn_status from_hip(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(attn_status s)
+{
+    switch (s) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_NULL_POINTER: return "ATTN_ERR_NULL_POINTER";
+        case ATTN_ERR_BAD_SHAPE: return "ATTN_ERR_BAD_SHAPE";
+        case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+        case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+        case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    }
+    return "ATTN_ERR_UNKNOWN";
+}
+
+const char *attn_last_error(void) { return g_last_error; }
+
+attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
+                                const void *v, void *o, float *lse, int B, int Hq,
+                                int Hkv, int N, int D, float scale, hipStream_t stream)
+{
+    if (!q || !k || !v || !o || !lse)
+        return fail(ATTN_ERR_NULL_POINTER, "attn_prefill_causal: NULL tensor pointer");
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_prefill_causal: B, Hq, Hkv, N, D must be >= 1");
+    if (Hq % Hkv)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_prefill_causal: Hq (%d) not a multiple of Hkv (%d)", Hq, Hkv);
+    if ((long long)B * Hq * N * D > kMaxElems)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_prefill_causal: tensor exceeds 2^31 elements");
+    if (dtype != ATTN_BF16 && dtype != ATTN_FP32)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_causal: unknown dtype %d", (int)dtype);
+    if (D != 64 && D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_causal: head dim %d not in {64, 128}", D);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_causal: tensors must be 16-byte aligned");
+    if (dtype == ATTN_BF16)
+        return from_hip(attn::launch_prefill_bf16(q, k, v, o, lse, B, Hq, Hkv, N, D, scale, stream),
+                        "attn_prefill_causal");
+    return from_hip(attn::launch_prefill_f32((const float *)q, (const float *)k, (const float *)v,
+                                             (float *)o, lse, B, Hq, Hkv, N, D, scale, stream),
+                    "attn_prefill_causal");
+}
+
+size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len, int D)
+{
+    attn::GqaPlan p;
+    if (D != 128 || !attn::gqa_plan(B, Hq, Hkv, kv_len, &p)) return 0;
+    return p.ws_total;
+}
+
+attn_status attn_decode_gqa(const void *q, const void *k_cache, const void *v_cache, void *o,
+                            float *lse, int B, int Hq, int Hkv, int kv_len, int kv_cap, int D,
+                            float scale, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream)
+{
+    if (!q || !k_cache || !v_cache || !o || !lse)
+        return fail(ATTN_ERR_NULL_POINTER, "attn_decode_gqa: NULL tensor pointer");
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: B, Hq, Hkv, D must be >= 1");
+    if (Hq % Hkv)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: Hq (%d) not a multiple of Hkv (%d)", Hq, Hkv);
+    if (kv_len < 1 || kv_len > kv_cap)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: need 1 <= kv_len (%d) <= kv_cap (%d)", kv_len, kv_cap);
+    if ((long long)B * Hkv * kv_cap * D > kMaxElems)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: cache exceeds 2^31 elements");
+    if (D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: head dim %d (only 128)", D);
+    if (Hq / Hkv > 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: group size %d above 16", Hq / Hkv);
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(o) || !aligned4(lse))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: tensors must be 16-byte aligned (o, lse: 4)");
+    attn::GqaPlan p;
+    attn::gqa_plan(B, Hq, Hkv, kv_len, &p);
+    if (!workspace || workspace_bytes < p.ws_total || !aligned16(workspace))
+        return fail(ATTN_ERR_WORKSPACE, "attn_decode_gqa: workspace needs %zu bytes (got %zu)",
+                    p.ws_total, workspace ? workspace_bytes : (size_t)0);
+    return from_hip(attn::launch_decode_gqa(p, q, k_cache, v_cache, o, lse, B, Hq, Hkv, kv_len,
+                                            kv_cap, scale, workspace, stream),
+                    "attn_decode_gqa");
+}
+
+size_t attn_decode_mla_workspace_bytes(int B, int Hq, int kv_len, int Dqk, int Dv)
+{
+    attn::MlaPlan p;
+    if (Dqk != 576 || Dv != 512 || !attn::mla_plan(B, Hq, kv_len, &p)) return 0;
+    return p.ws_total;
+}
+
+attn_status attn_decode_mla_absorbed(const void *q, const void *ckv, void *o, float *lse,
+                                     int B, int Hq, int kv_len, int kv_cap, int Dqk, int Dv,
+                                     float scale, void *workspace, size_t workspace_bytes,
+                                     hipStream_t stream)
+{
+    if (!q || !ckv || !o || !lse)
+        return fail(ATTN_ERR_NULL_POINTER, "attn_decode_mla_absorbed: NULL tensor pointer");
+    if (B < 1 || Hq < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: bad B, Hq, Dqk or Dv");
+    if (kv_len < 1 || kv_len > kv_cap)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: need 1 <= kv_len (%d) <= kv_cap (%d)",
+                    kv_len, kv_cap);
+    if ((long long)B * kv_cap * Dqk > kMaxElems)
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: cache exceeds 2^31 elements");
+    if (Dqk != 576 || Dv != 512)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: (Dqk, Dv) = (%d, %d), only (576, 512)",
+                    Dqk, Dv);
+    if (Hq % 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: Hq (%d) not a multiple of 16", Hq);
+    if (!aligned16(q) || !aligned16(ckv) || !aligned16(o) || !aligned4(lse))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: tensors must be 16-byte aligned");
+    attn::MlaPlan p;
+    attn::mla_plan(B, Hq, kv_len, &p);
+    if (!workspace || workspace_bytes < p.ws_total || !aligned16(workspace))
+        return fail(ATTN_ERR_WORKSPACE, "attn_decode_mla_absorbed: workspace needs %zu bytes (got %zu)",
+                    p.ws_total, workspace ? workspace_bytes : (size_t)0);
+    return from_hip(attn::launch_decode_mla(p, q, ckv, o, lse, B, Hq, kv_len, kv_cap, scale,
+                                            workspace, stream),
+                    "attn_decode_mla_absorbed");
+}
+
+}  // extern "C"
