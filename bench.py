@@ -1,0 +1,260 @@
+"""Benchmark of the fused-attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--quick]
+
+Headline (the JSON line's `value`): single-query GQA decode of the
+Llama-3-8B-shaped workload (B=8, 32 query heads over 8 K/V heads, 4096 cached
+tokens, d=128, bf16 cache, fp32 accumulation), in K/V-cache GB/s: the
+algorithmic bytes of one call (K and V rows read once, q read, O and LSE
+written) divided by the time per call. Inputs are resident in HBM before the
+timed region; consecutive steps rotate over several copies of the cache whose
+total size exceeds twice the 256 MB Infinity Cache, so each step streams from
+HBM rather than from the last-level cache.
+
+The same line also carries:
+  * "roofline": the decode kernel's achieved bandwidth per launch (HIP events
+    around every launch on the launch stream) against the 8 TB/s HBM peak,
+    with the counter-measured HBM traffic when a matching counter summary is
+    present under profiles/ (null otherwise);
+  * "cpu_baseline": the fp64 oracle timed on this host's cores over repeated
+    full passes of the same workload (a reported baseline, not a target);
+  * "workloads": every named workload timed the same way, each priced against
+    its roofline (prefill: unmasked-pair flops vs 2.5 PFLOP/s dense bf16 MFMA;
+    decode: algorithmic bytes vs 8 TB/s HBM).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+MALL_BYTES = 256 << 20
+METRIC = "prefill TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% of HBM peak)"
+HEADLINE = "decode_gqa_llama3_8b_4k"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gqa_llama3_8b_4k_counters.json")
+DECODE_SRC = os.path.join(ROOT, "transformer_attention_05_amd", "csrc", "decode_gqa.hip")
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--counters", action="store_true",
+                    help="few headline launches + a calibration copy, for rocprofv3 --pmc runs")
+    return ap.parse_args()
+
+
+def _rotation(nbytes_per_set: int) -> int:
+    """Copies needed so the rotation footprint exceeds twice the MALL."""
+    return max(2, -(-2 * MALL_BYTES // max(1, nbytes_per_set)) + 1)
+
+
+def _time_calls(torch, calls, steps, warmup):
+    """Warm up, then time `steps` calls bracketed by synchronisation; each
+    call also gets its own event pair on the current (launch) stream.
+    Returns (total seconds, mean per-launch seconds)."""
+    n = len(calls)
+    for i in range(warmup):
+        calls[i % n]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        calls[i % n]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    per = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
+    return total, per
+
+
+def _upload_bf16(torch, bits, dev):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _upload_f32(torch, x, dev):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+
+def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
+    """Time one named workload; returns a result dict."""
+    cfg = workloads.WORKLOADS[name]
+    w = workloads.make(name)
+    kind = cfg["kind"]
+    if kind == "decode_gqa":
+        q, k, v = (_upload_bf16(torch, x, dev) for x in (w.q, w.k, w.v))
+        nbytes = workloads.decode_gqa_bytes(w.B, w.Hq, w.Hkv, w.kv_len, w.D)
+        sets = [(q, k, v)] + [(q, k.clone(), v.clone()) for _ in range(_rotation(2 * k.numel() * 2) - 1)]
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+        calls = [lambda s=s: attn.attn_decode_gqa(s[0], s[1], s[2], w.kv_len, w.scale, out=o, lse=lse)
+                 for s in sets]
+        work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
+        kernel = "decode_gqa_kernel"
+    elif kind == "decode_mla":
+        q, c = _upload_bf16(torch, w.q, dev), _upload_bf16(torch, w.ckv, dev)
+        nbytes = workloads.decode_mla_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv)
+        sets = [(q, c)] + [(q, c.clone()) for _ in range(_rotation(c.numel() * 2) - 1)]
+        o = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+        calls = [lambda s=s: attn.attn_decode_mla_absorbed(s[0], s[1], w.kv_len, w.Dv, w.scale,
+                                                           out=o, lse=lse) for s in sets]
+        work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
+        kernel = "decode_mla_kernel (+ merge_mla_kernel)"
+    else:
+        up = _upload_bf16 if w.dtype == "bf16" else _upload_f32
+        q, k, v = (up(torch, x, dev) for x in (w.q, w.k, w.v))
+        flops = workloads.prefill_causal_flops(w.B, w.Hq, w.N, w.D)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+        calls = [lambda: attn.attn_prefill_causal(q, k, v, w.scale, out=o, lse=lse)]
+        work = flops / 1e12
+        unit = "TFLOP/s"
+        if w.dtype == "bf16":
+            peak, bound, kernel = MFMA_BF16_PEAK_TFLOPS, "mfma", "prefill_bf16_kernel"
+        else:
+            peak, bound, kernel = FP32_VALU_PEAK_TFLOPS, "alu", "prefill_f32_kernel"
+        nsteps = max(5, min(steps, int(2e12 // max(flops, 1)) + 5))
+        steps, warmup = nsteps, min(warmup, 5)
+    total, per = _time_calls(torch, calls, steps, warmup)
+    rate = work / (total / steps)
+    achieved = work / per
+    return dict(kernel=kernel, steps=steps, ms_per_call=1e3 * total / steps,
+                ms_per_launch=1e3 * per, value=rate, unit=unit, bound=bound,
+                achieved=achieved, peak=peak, frac=achieved / peak,
+                work_per_call=(nbytes if unit == "GB/s" else flops))
+
+
+def _traffic(per_launch_s):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current decode kernel source (else None)."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != src:
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(workloads, seconds):
+    """The fp64 oracle on this host over repeated full passes of the headline
+    workload; GB/s of the same algorithmic bytes."""
+    import oracle
+    w = workloads.make(HEADLINE)
+    nbytes = workloads.decode_gqa_bytes(w.B, w.Hq, w.Hkv, w.kv_len, w.D)
+    threads = oracle.default_threads()
+    oracle.decode_gqa(w.q[:1, :, :], w.k[:1, :, :64], w.v[:1, :, :64], 64, w.scale, threads=threads)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_gqa(w.q, w.k, w.v, w.kv_len, w.scale, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=reps * nbytes / el / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample="%d full passes of %s (B=8, Hq=32, Hkv=8, kv_len=4096, d=128) in %.1f s, "
+                       "fp64, bf16 inputs widened per pass" % (reps, HEADLINE, el))
+
+
+CALIB_BYTES = 512 << 20
+
+
+def counters_run(torch, attn, workloads, dev):
+    """Launch the headline decode kernel 5 times (one input set per launch,
+    so every launch streams from HBM) and one plain copy of CALIB_BYTES, whose
+    FETCH_SIZE / WRITE_SIZE calibrate the counters against a known size."""
+    w = workloads.make(HEADLINE)
+    q = _upload_bf16(torch, w.q, dev)
+    k0, v0 = _upload_bf16(torch, w.k, dev), _upload_bf16(torch, w.v, dev)
+    sets = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(4)]
+    torch.cuda.synchronize()
+    for k, v in sets:
+        attn.attn_decode_gqa(q, k, v, w.kv_len, w.scale)
+        torch.cuda.synchronize()
+        print("decode launch done", flush=True)
+    src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    scrub = torch.empty((1 << 30) // 4, dtype=torch.float32, device=dev).fill_(2.0)  # evict src
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del scrub
+    print("calibration copy of %d bytes done" % CALIB_BYTES, flush=True)
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import transformer_attention_05_amd as attn
+    import workloads
+    attn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if a.counters:
+        counters_run(torch, attn, workloads, dev)
+        return
+
+    head = bench_workload(torch, attn, workloads, HEADLINE, a.steps, a.warmup, dev)
+    print("headline %s: %.1f GB/s per call, %.1f GB/s per launch (%.3f ms)" % (
+        HEADLINE, head["value"], head["achieved"], head["ms_per_launch"]), file=sys.stderr, flush=True)
+    results = {HEADLINE: head}
+    if not a.quick:
+        for name in workloads.WORKLOADS:
+            if name == HEADLINE:
+                continue
+            torch.cuda.empty_cache()
+            r = bench_workload(torch, attn, workloads, name, a.steps, a.warmup, dev)
+            results[name] = r
+            print("%s: %.2f %s (%.1f %% of %s peak), %.3f ms" % (
+                name, r["value"], r["unit"], 100 * r["frac"], r["bound"], r["ms_per_call"]),
+                file=sys.stderr, flush=True)
+
+    cpu = None if a.no_cpu_baseline else cpu_baseline(workloads, a.cpu_seconds)
+    w = workloads.WORKLOADS[HEADLINE]
+    line = {
+        "metric": METRIC, "value": round(head["value"], 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": head["steps"], "warmup": a.warmup, "ms_per_step": round(head["ms_per_call"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"],
+                   "kv_len": w["kv_len"], "D": w["D"], "cache_dtype": "bf16",
+                   "accumulate": "fp32", "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": head["kernel"],
+                     "achieved": round(head["achieved"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["frac"], 4), "traffic": _traffic(head["ms_per_launch"]),
+                     "bytes_per_launch": head["work_per_call"]},
+        "cpu_baseline": None if cpu is None else {k: (round(v, 4) if isinstance(v, float) else v)
+                                                  for k, v in cpu.items()},
+        "workloads": {n: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
+                      for n, r in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

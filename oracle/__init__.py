@@ -63,10 +63,16 @@ def _load():
 
 
 def default_threads() -> int:
+    """Cores this process may use: its affinity mask, capped by
+    OMP_NUM_THREADS when that is set (a shared host's per-job CPU share)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def widen(x: np.ndarray) -> np.ndarray:

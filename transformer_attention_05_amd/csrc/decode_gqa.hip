@@ -20,10 +20,11 @@
 //     (4 keys × 256 B = 1 KiB contiguous per wave load) and gets that key's
 //     weights for every head from a per-wave LDS table.
 // The waves' (m, ℓ, O) are merged in LDS; with one split the workgroup
-// writes O/ℓ and LSE directly, otherwise it writes its partial to the
-// workspace and the last workgroup of the (b, hkv) pair to finish merges all
-// partials through their log-sum-exp (split-K merge, "AI Infra 入门…", §3).
-// Slots at or past kv_len are never read.
+// writes O/ℓ and LSE directly, otherwise it writes its partial (m, ℓ, Õ) to
+// the workspace and a second kernel merges the partials through their
+// log-sum-exp (split-K merge, "AI Infra 入门…", §3). No workgroup waits for
+// another and no cross-workgroup fence is needed: the kernel boundary orders
+// the partial writes before the merge. Slots at or past kv_len are never read.
 #include "common.h"
 #include "launch.h"
 
@@ -37,12 +38,11 @@ constexpr int kChunk = kWaves * kWaveKeys;  // 256 keys per workgroup step
 constexpr int kTargetGroups = 1024;         // workgroups per launch the split aims at
 
 template <int GP>
-__global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
+__global__ __launch_bounds__(256, GP >= 16 ? 1 : 2) void decode_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, uint16_t *__restrict__ o, float *__restrict__ lse,
     int Hq, int Hkv, int G, int kv_len, int kv_cap, float scale_log2, int splits,
-    int split_keys, unsigned *__restrict__ counters, float *__restrict__ ws_ml,
-    float *__restrict__ ws_part)
+    int split_keys, float *__restrict__ ws_ml, float *__restrict__ ws_part)
 {
     const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -55,7 +55,6 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     __shared__ float p_lds[kWaves][kWaveKeys * GP + GP];
     __shared__ float red_o[kWaves][GP][kD];
     __shared__ float red_m[kWaves][GP], red_l[kWaves][GP];
-    __shared__ unsigned last_flag;
 
     // qᵀ as the MFMA B operand: column = head (lane % 16), 8 d per lane.
     const int hcol = lane & 15, quad = lane >> 4;
@@ -195,14 +194,13 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
             acc = fmaf(f, red_o[w][h][d], acc);
             l = fmaf(f, red_l[w][h], l);
         }
+        if (h >= G) continue;
+        const size_t row = (size_t)b * Hq + hkv * G + h;
         if (splits == 1) {
-            if (h < G) {
-                const size_t row = (size_t)b * Hq + hkv * G + h;
-                o[row * kD + d] = (uint16_t)(pack_bf16x2(acc / l, 0.f) & 0xffffu);
-                if (d == 0) lse[row] = (M + log2_fast(l)) * kLn2;
-            }
+            o[row * kD + d] = (uint16_t)(pack_bf16x2(acc / l, 0.f) & 0xffffu);
+            if (d == 0) lse[row] = (M + log2_fast(l)) * kLn2;
         } else {
-            const size_t slot = ((size_t)bh * splits + split) * GP + h;
+            const size_t slot = row * splits + split;
             ws_part[slot * kD + d] = acc;
             if (d == 0) {
                 ws_ml[2 * slot] = M;
@@ -210,32 +208,6 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
             }
         }
     }
-    if (splits == 1) return;
-
-    // ---- split-K: the last workgroup of this (b, hkv) merges all partials
-    __threadfence();  // release this split's partial device-wide
-    __syncthreads();
-    if (tid == 0) last_flag = (atomicAdd(&counters[bh], 1u) == (unsigned)(splits - 1));
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();  // acquire the other splits' partials
-    for (int idx = tid; idx < G * kD; idx += 256) {
-        const int h = idx / kD, d = idx % kD;
-        const size_t slot0 = (size_t)bh * splits * GP + h;
-        float M = -INFINITY;
-        for (int s = 0; s < splits; ++s) M = fmaxf(M, ws_ml[2 * (slot0 + (size_t)s * GP)]);
-        float acc = 0.f, l = 0.f;
-        for (int s = 0; s < splits; ++s) {
-            const size_t slot = slot0 + (size_t)s * GP;
-            const float f = exp2_fast(ws_ml[2 * slot] - M);
-            acc = fmaf(f, ws_part[slot * kD + d], acc);
-            l = fmaf(f, ws_ml[2 * slot + 1], l);
-        }
-        const size_t row = (size_t)b * Hq + hkv * G + h;
-        o[row * kD + d] = (uint16_t)(pack_bf16x2(acc / l, 0.f) & 0xffffu);
-        if (d == 0) lse[row] = (M + log2_fast(l)) * kLn2;
-    }
-    if (tid == 0) counters[bh] = 0u;  // ready for the next call
 }
 
 }  // namespace
@@ -256,10 +228,10 @@ bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p)
     p->gp = gp;
     p->splits = s;
     p->split_keys = per * kChunk;
-    p->ws_counters = 0;
-    p->ws_ml = align_up(sizeof(unsigned) * groups, 256);
-    p->ws_part = p->ws_ml + align_up(sizeof(float) * 2 * groups * s * gp, 256);
-    p->ws_total = p->ws_part + align_up(sizeof(float) * (size_t)kD * groups * s * gp, 256);
+    const size_t rows = (size_t)B * Hq;
+    p->ws_ml = 0;
+    p->ws_part = align_up(sizeof(float) * 2 * rows * s, 256);
+    p->ws_total = s == 1 ? 256 : p->ws_part + align_up(sizeof(float) * kD * rows * s, 256);
     return true;
 }
 
@@ -268,7 +240,6 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
                              int kv_cap, float scale, void *ws, hipStream_t st)
 {
     char *w = (char *)ws;
-    unsigned *counters = (unsigned *)(w + p.ws_counters);
     float *ws_ml = (float *)(w + p.ws_ml);
     float *ws_part = (float *)(w + p.ws_part);
     const dim3 grid(p.splits, Hkv, B), block(256);
@@ -278,8 +249,8 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
     case GPV:                                                                            \
         decode_gqa_kernel<GPV><<<grid, block, 0, st>>>(                                 \
             (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, \
-            lse, Hq, Hkv, G, kv_len, kv_cap, sl2, p.splits, p.split_keys, counters, ws_ml, \
-            ws_part);                                                                    \
+            lse, Hq, Hkv, G, kv_len, kv_cap, sl2, p.splits, p.split_keys, ws_ml, ws_part); \
+                                                                                      \
         break;
     switch (p.gp) {
         ATTN_GQA_CASE(1)
@@ -290,7 +261,9 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
         default: return hipErrorInvalidValue;
     }
 #undef ATTN_GQA_CASE
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, kD, st);
 }
 
 }  // namespace attn

@@ -4,23 +4,28 @@
 // every query head attends to one shared latent cache whose rows are
 // [latent 512 | rope 64]. The key is the whole 576-wide row and the value is
 // its latent part, so one HBM read of a row serves both products. Storage is
-// bf16 but every product accumulates in fp32 and the output is rounded once
+// bf16; every product accumulates in fp32 and the output is rounded once
 // (§二.2, §五).
 //
 // Decomposition. Workgroup (split, head group, b) has 8 waves and covers 128
-// query heads, so each latent tile is loaded from HBM once and shared through
+// query heads, so each latent tile is read from HBM once and shared through
 // LDS by all heads. Each wave owns 16 heads as the columns of
 // v_mfma_f32_16x16x32_bf16:
-//   Sᵀ = C·Qᵀ      keys as MFMA rows, 576-deep contraction, Q fragments held
-//                  in registers for the whole pass;
-//   online softmax in base 2 (running max and sum, rescale by 2^(m_old−m_new));
+//   Sᵀ = C·Qᵀ      keys as MFMA rows, 576-deep contraction; the wave's Q
+//                  fragments stay in registers for the whole pass;
+//   online softmax in base 2 (running max and sum; the output is rescaled by
+//                  2^(m_old − m_new) only when some lane's max moved);
 //   Oᵀ += Vᵀ·Pᵀ    P stays in registers (the Sᵀ accumulator layout is the
-//                  B-operand layout), Vᵀ from a transposed LDS copy of the
-//                  tile's first 512 channels written at staging time.
-// Latent tiles of 32 rows are double-buffered in LDS. Splits of the cache
-// write (O, m, ℓ) partials in fp32; a second small kernel merges them through
-// their log-sum-exp ("AI Infra 入门…", §3, split-K with LSE). Rows at or past
-// kv_len are never read.
+//                  B-operand layout); the Vᵀ operand is fetched straight from
+//                  the row-major latent tile with ds_read_b64_tr_b16, which
+//                  hands each lane one column of a 4-row × 16-column block.
+// Latent tiles (32 rows × 1152 B) move HBM → LDS with global_load_lds_dwordx4
+// (no register staging), double-buffered so the next tile streams in while
+// the current one is consumed. 16-byte chunks are XOR-swizzled per row so the
+// score reads and the transposed value reads hit distinct LDS banks.
+// Splits of the cache write fp32 (m, ℓ, Õ) partials; the shared merge kernel
+// combines them through their log-sum-exp. Rows at or past kv_len are never
+// read.
 #include "common.h"
 #include "launch.h"
 
@@ -28,15 +33,23 @@ namespace attn {
 namespace {
 
 constexpr int MD = 576, MV = 512, MBC = 32, MW = 8, MH = 16 * MW;
-constexpr int MKS = MD / 32;     // 18 k-steps of the score product
-constexpr int MDB = MV / 16;     // 32 row blocks of Oᵀ
-constexpr int MKSTR = MD + 8;    // latent tile row stride (elements)
-constexpr int MVSTR = MBC + 8;   // Vᵀ tile row stride (elements)
-constexpr int MCH = MD / 8;      // 72 sixteen-byte chunks per row
-constexpr int MUNITS = (MBC / 4) * MCH;  // staging units of 4 rows × 16 B
+constexpr int MKS = MD / 32;                 // 18 k-steps of the score product
+constexpr int MDB = MV / 16;                 // 32 row blocks of Oᵀ
+constexpr int MROWB = MD * 2;                // bytes per latent row (1152)
+constexpr int MCH = MD / 8;                  // 72 sixteen-byte chunks per row
+constexpr int MTILEB = MBC * MROWB;          // 36,864 bytes per tile
+constexpr int MLOADS = MTILEB / 1024;        // 36 wave-wide 1 KiB loads per tile
 constexpr int MTHREADS = 64 * MW;
-constexpr int MUPT = (MUNITS + MTHREADS - 1) / MTHREADS;
 constexpr int kTargetGroups = 256;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Physical 16-byte chunk holding logical chunk c of tile row r.
+__device__ __forceinline__ int swz(int r, int c) {
+    return (c & ~7) | ((c & 7) ^ ((r & 7) ^ ((r >> 3) & 1)));
+}
 
 __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ ckv,
@@ -44,8 +57,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     float scale_log2, int splits, int split_keys, float *__restrict__ ws_ml,
     float *__restrict__ ws_part)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][MBC * MKSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][MV * MVSTR];
+    __shared__ __attribute__((aligned(1024))) char tile[2][MTILEB];
 
     const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -64,42 +76,16 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         for (int ks = 0; ks < MKS; ++ks) qf[ks] = as<bf16x8>(*(const u32x4 *)(qr + 32 * ks));
     }
 
-    u32x4 sreg[MUPT][4];
-    auto load_tile = [&](int t0) {
-#pragma unroll
-        for (int u = 0; u < MUPT; ++u) {
-            const int unit = tid + u * MTHREADS;
-            if (unit < MUNITS) {
-                const int kg = unit / MCH, dc = unit % MCH;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = min(t0 + 4 * kg + r, key_end - 1);
-                    sreg[u][r] = *(const u32x4 *)(cb + (size_t)key * MD + 8 * dc);
-                }
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < MUPT; ++u) {
-            const int unit = tid + u * MTHREADS;
-            if (unit < MUNITS) {
-                const int kg = unit / MCH, dc = unit % MCH;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    *(u32x4 *)&k_lds[buf][(4 * kg + r) * MKSTR + 8 * dc] = sreg[u][r];
-                if (dc < MV / 8) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const u32x2 a = {__byte_perm(sreg[u][0][j], sreg[u][1][j], 0x5410),
-                                         __byte_perm(sreg[u][2][j], sreg[u][3][j], 0x5410)};
-                        const u32x2 c = {__byte_perm(sreg[u][0][j], sreg[u][1][j], 0x7632),
-                                         __byte_perm(sreg[u][2][j], sreg[u][3][j], 0x7632)};
-                        *(u32x2 *)&vt_lds[buf][(8 * dc + 2 * j) * MVSTR + 4 * kg] = a;
-                        *(u32x2 *)&vt_lds[buf][(8 * dc + 2 * j + 1) * MVSTR + 4 * kg] = c;
-                    }
-                }
-            }
+    // HBM → LDS: wave-wide load i fills tile bytes [1024 i, 1024 i + 1024);
+    // lane l's 16 bytes land at chunk position 64 i + l = (row, physical chunk).
+    auto load_tile = [&](int t0, int buf) {
+        for (int i = wave; i < MLOADS; i += MW) {
+            const int pos = 64 * i + lane;
+            const int r = pos / MCH, pc = pos % MCH;
+            const int c = swz(r, pc);  // the swizzle is its own inverse
+            const int key = min(t0 + r, key_end - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(cb + (size_t)key * MD + 8 * c),
+                                             (lds_void *)&tile[buf][1024 * i], 16, 0, 0);
         }
     };
 
@@ -108,23 +94,32 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     for (int db = 0; db < MDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
+    // transposed value reads: lane 16·g + 4·e + c addresses row 4·g + e (and
+    // 16 + 4·g + e), columns 4·c .. 4·c + 3 of a 16-column block
+    const int vg = quad, ve = (lane >> 2) & 3, vc = lane & 3;
+    const int vr1 = 4 * vg + ve, vr2 = 16 + 4 * vg + ve;
+
     const int n_t = (key_end - key_begin + MBC - 1) / MBC;
-    load_tile(key_begin);
-    store_tile(0);
+    load_tile(key_begin, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int t = 0; t < n_t; ++t) {
         const int cur = t & 1;
         const int t0 = key_begin + t * MBC;
-        if (t + 1 < n_t) load_tile(t0 + MBC);
+        if (t + 1 < n_t) load_tile(t0 + MBC, cur ^ 1);
         if (wave_active) {
+            const char *tb = tile[cur];
             float sc[8];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
+                const int r = 16 * kb + hcol;
+                const char *rowp = tb + r * MROWB;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const uint16_t *kr = &k_lds[cur][(16 * kb + hcol) * MKSTR + 8 * quad];
 #pragma unroll
-                for (int ks = 0; ks < MKS; ++ks)
-                    acc = mfma16x16x32(as<bf16x8>(*(const u32x4 *)(kr + 32 * ks)), qf[ks], acc);
+                for (int ks = 0; ks < MKS; ++ks) {
+                    const u32x4 a = *(const u32x4 *)(rowp + 16 * swz(r, 4 * ks + quad));
+                    acc = mfma16x16x32(as<bf16x8>(a), qf[ks], acc);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = t0 + 16 * kb + 4 * quad + i;
@@ -146,20 +141,29 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
             }
             l_run = l_run * alpha + ps;
             m_run = m_new;
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // exact: α = 1 changes nothing
+#pragma unroll
+                for (int db = 0; db < MDB; ++db) oacc[db] *= alpha;
+            }
             const u32x4 pw = {pack_bf16x2(sc[0], sc[1]), pack_bf16x2(sc[2], sc[3]),
                               pack_bf16x2(sc[4], sc[5]), pack_bf16x2(sc[6], sc[7])};
             const bf16x8 pf = as<bf16x8>(pw);
-            // A slot s ↔ key 4·quad + s (s < 4) or 16 + 4·quad + (s − 4)
-            const uint16_t *vr = &vt_lds[cur][hcol * MVSTR + 4 * quad];
+            // Vᵀ operand: slots 0..3 ↔ keys 4·quad + e, slots 4..7 ↔ keys 16 + 4·quad + e
+            const char *row1 = tb + vr1 * MROWB + 8 * (vc & 1);
+            const char *row2 = tb + vr2 * MROWB + 8 * (vc & 1);
 #pragma unroll
             for (int db = 0; db < MDB; ++db) {
-                const u32x2 lo = *(const u32x2 *)(vr + 16 * db * MVSTR);
-                const u32x2 hi = *(const u32x2 *)(vr + 16 * db * MVSTR + 16);
-                const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                oacc[db] = mfma16x16x32(as<bf16x8>(a), pf, oacc[db] * alpha);
+                const int c = 2 * db + (vc >> 1);
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(row1 + 16 * swz(vr1, c)));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(row2 + 16 * swz(vr2, c)));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
+                oacc[db] = mfma16x16x32(as<bf16x8>(a), pf, oacc[db]);
             }
         }
-        if (t + 1 < n_t) store_tile(cur ^ 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
@@ -190,32 +194,6 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     }
 }
 
-// Merge the split partials of every (b, head) through their log-sum-exp.
-// Thread = (row, 4 consecutive channels); summation over splits in order.
-__global__ __launch_bounds__(256) void merge_mla_kernel(
-    const float *__restrict__ ws_ml, const float *__restrict__ ws_part,
-    uint16_t *__restrict__ o, float *__restrict__ lse, int rows, int splits)
-{
-    const int gid = blockIdx.x * 256 + threadIdx.x;
-    const int row = gid / (MV / 4), c4 = gid % (MV / 4);
-    if (row >= rows) return;
-    const float *ml = ws_ml + (size_t)row * splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        const float f = exp2_fast(ml[2 * s] - M);
-        const f32x4 p = *(const f32x4 *)(ws_part + ((size_t)row * splits + s) * MV + 4 * c4);
-        acc += f * p;
-        l = fmaf(f, ml[2 * s + 1], l);
-    }
-    const float inv = 1.f / l;
-    const u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-    *(u32x2 *)(o + (size_t)row * MV + 4 * c4) = w;
-    if (c4 == 0) lse[row] = (M + log2_fast(l)) * kLn2;
-}
-
 }  // namespace
 
 bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p)
@@ -230,12 +208,10 @@ bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p)
     s = (tiles + per - 1) / per;
     p->splits = s;
     p->split_keys = per * MBC;
-    p->ws_counters = 0;
-    p->ws_ml = 0;
     const size_t rows = (size_t)B * Hq;
+    p->ws_ml = 0;
     p->ws_part = align_up(sizeof(float) * 2 * rows * s, 256);
-    p->ws_total = p->ws_part + align_up(sizeof(float) * MV * rows * s, 256);
-    if (s == 1) p->ws_total = 256;  // unused, but keep a non-zero minimum
+    p->ws_total = s == 1 ? 256 : p->ws_part + align_up(sizeof(float) * MV * rows * s, 256);
     return true;
 }
 
@@ -252,11 +228,7 @@ hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, v
         scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    const int rows = B * Hq;
-    const int threads = rows * (MV / 4);
-    merge_mla_kernel<<<dim3((threads + 255) / 256), dim3(256), 0, st>>>(
-        ws_ml, ws_part, (uint16_t *)o, lse, rows, p.splits);
-    return hipGetLastError();
+    return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, MV, st);
 }
 
 }  // namespace attn

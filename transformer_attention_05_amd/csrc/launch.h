@@ -12,7 +12,7 @@ struct GqaPlan {
     int gp;          // padded group size (power of two, >= Hq/Hkv, <= 16)
     int splits;      // workgroups per (batch, K/V head)
     int split_keys;  // keys per split (multiple of the 256-key chunk)
-    size_t ws_counters, ws_ml, ws_part, ws_total;  // workspace byte offsets / size
+    size_t ws_ml, ws_part, ws_total;  // workspace byte offsets / size
 };
 bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p);
 hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, const void *v,
@@ -30,12 +30,17 @@ hipError_t launch_prefill_f32(const float *q, const float *k, const float *v, fl
 // ---- absorbed MLA decode -------------------------------------------------
 struct MlaPlan {
     int splits, split_keys;
-    size_t ws_counters, ws_ml, ws_part, ws_total;
+    size_t ws_ml, ws_part, ws_total;
 };
 bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p);
 hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, void *o,
                              float *lse, int B, int Hq, int kv_len, int kv_cap,
                              float scale, void *ws, hipStream_t s);
+
+// ---- split-K merge through the log-sum-exp (shared by both decodes) -------
+// ml [rows][splits][2] = (m, l) in base 2; part [rows][splits][dv] fp32.
+hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse, int rows,
+                        int splits, int dv, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
