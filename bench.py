@@ -6,10 +6,13 @@ Headline (the JSON line's `value`): single-query GQA decode of the
 Llama-3-8B-shaped workload (B=8, 32 query heads over 8 K/V heads, 4096 cached
 tokens, d=128, bf16 cache, fp32 accumulation), in K/V-cache GB/s: the
 algorithmic bytes of one call (K and V rows read once, q read, O and LSE
-written) divided by the time per call. Inputs are resident in HBM before the
-timed region; consecutive steps rotate over several copies of the cache whose
-total size exceeds twice the 256 MB Infinity Cache, so each step streams from
-HBM rather than from the last-level cache.
+written) divided by the GPU time per call. A call is the library entry point
+(split kernel + LSE merge kernel). Inputs are resident in HBM before the timed
+region; consecutive steps rotate over several copies of the cache whose total
+size exceeds twice the 256 MB Infinity Cache, so each step streams from HBM
+rather than from the last-level cache. Steps are launched by replaying a HIP
+graph of 20 consecutive calls, so host-side launch cost (Python and ctypes)
+is not what is measured; the eager per-call time is reported beside it.
 
 The same line also carries:
   * "roofline": the decode kernel's achieved bandwidth per launch (HIP events
@@ -41,7 +44,8 @@ MALL_BYTES = 256 << 20
 METRIC = "prefill TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% of HBM peak)"
 HEADLINE = "decode_gqa_llama3_8b_4k"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gqa_llama3_8b_4k_counters.json")
-DECODE_SRC = os.path.join(ROOT, "transformer_attention_05_amd", "csrc", "decode_gqa.hip")
+DECODE_SRCS = [os.path.join(ROOT, "transformer_attention_05_amd", "csrc", f)
+               for f in ("decode_gqa.hip", "merge.hip", "common.h")]
 
 
 def _args():
@@ -54,6 +58,8 @@ def _args():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--counters", action="store_true",
                     help="few headline launches + a calibration copy, for rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write the counter summary of two --counters runs under profiles/")
     return ap.parse_args()
 
 
@@ -62,25 +68,46 @@ def _rotation(nbytes_per_set: int) -> int:
     return max(2, -(-2 * MALL_BYTES // max(1, nbytes_per_set)) + 1)
 
 
-def _time_calls(torch, calls, steps, warmup):
-    """Warm up, then time `steps` calls bracketed by synchronisation; each
-    call also gets its own event pair on the current (launch) stream.
-    Returns (total seconds, mean per-launch seconds)."""
+def _time_calls(torch, calls, steps, warmup, per_graph):
+    """Time `steps` calls.
+
+    After an eager warm-up, `per_graph` consecutive calls are captured into
+    one HIP graph, which is replayed steps / per_graph times; the timed
+    region is bracketed by synchronisation, and the GPU time comes from an
+    event pair on the replay stream. The graph removes host launch overhead
+    (Python + ctypes per call) from the measurement; every kernel of every
+    call still runs. Also returns an eager per-call time for reference.
+    Returns (wall seconds, GPU seconds, eager seconds per call).
+    """
     n = len(calls)
     for i in range(warmup):
         calls[i % n]()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record()
+    ne = min(steps, 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(ne):
         calls[i % n]()
-        ev[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
-    total = time.perf_counter() - t0
-    per = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
-    return total, per
+    eager = e0.elapsed_time(e1) / 1e3 / ne
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            calls[i % n]()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = steps // per_graph
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) / 1e3, eager
 
 
 def _upload_bf16(torch, bits, dev):
@@ -104,20 +131,24 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
         sets = [(q, k, v)] + [(q, k.clone(), v.clone()) for _ in range(_rotation(2 * k.numel() * 2) - 1)]
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
-        calls = [lambda s=s: attn.attn_decode_gqa(s[0], s[1], s[2], w.kv_len, w.scale, out=o, lse=lse)
-                 for s in sets]
+        ws = torch.empty(attn.attn_decode_gqa_workspace_bytes(w.B, w.Hq, w.Hkv, w.kv_len, w.D),
+                         dtype=torch.uint8, device=dev)
+        calls = [lambda s=s: attn.attn_decode_gqa(s[0], s[1], s[2], w.kv_len, w.scale, out=o,
+                                                  lse=lse, ws=ws) for s in sets]
         work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
-        kernel = "decode_gqa_kernel"
+        kernel = "decode_gqa_kernel + merge_kernel"
     elif kind == "decode_mla":
         q, c = _upload_bf16(torch, w.q, dev), _upload_bf16(torch, w.ckv, dev)
         nbytes = workloads.decode_mla_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv)
         sets = [(q, c)] + [(q, c.clone()) for _ in range(_rotation(c.numel() * 2) - 1)]
         o = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(attn.attn_decode_mla_workspace_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv),
+                         dtype=torch.uint8, device=dev)
         calls = [lambda s=s: attn.attn_decode_mla_absorbed(s[0], s[1], w.kv_len, w.Dv, w.scale,
-                                                           out=o, lse=lse) for s in sets]
+                                                           out=o, lse=lse, ws=ws) for s in sets]
         work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
-        kernel = "decode_mla_kernel (+ merge_mla_kernel)"
+        kernel = "decode_mla_kernel + merge_kernel"
     else:
         up = _upload_bf16 if w.dtype == "bf16" else _upload_f32
         q, k, v = (up(torch, x, dev) for x in (w.q, w.k, w.v))
@@ -133,28 +164,74 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
             peak, bound, kernel = FP32_VALU_PEAK_TFLOPS, "alu", "prefill_f32_kernel"
         nsteps = max(5, min(steps, int(2e12 // max(flops, 1)) + 5))
         steps, warmup = nsteps, min(warmup, 5)
-    total, per = _time_calls(torch, calls, steps, warmup)
-    rate = work / (total / steps)
-    achieved = work / per
-    return dict(kernel=kernel, steps=steps, ms_per_call=1e3 * total / steps,
-                ms_per_launch=1e3 * per, value=rate, unit=unit, bound=bound,
-                achieved=achieved, peak=peak, frac=achieved / peak,
+    per_graph = 20 if steps % 20 == 0 else 1
+    wall, gpu, eager = _time_calls(torch, calls, steps, warmup, per_graph)
+    per = gpu / steps
+    return dict(kernel=kernel, steps=steps, calls_per_graph=per_graph,
+                ms_per_call=1e3 * per, wall_ms_per_call=1e3 * wall / steps,
+                eager_ms_per_call=1e3 * eager, value=work / per, unit=unit, bound=bound,
+                achieved=work / per, peak=peak, frac=work / per / peak,
                 work_per_call=(nbytes if unit == "GB/s" else flops))
 
 
-def _traffic(per_launch_s):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current decode kernel source (else None)."""
+def _decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in DECODE_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def _traffic():
+    """HBM bytes per call from the committed counter summary, if it was taken
+    on the current decode kernel sources (else None)."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     try:
         rec = json.load(open(COUNTERS_FILE))
-        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != src:
+        if rec.get("source_sha256") != _decode_source_hash():
             return None
-        return rec.get("hbm_bytes_per_launch")
+        return rec.get("hbm_bytes_per_call")
     except (OSError, ValueError):
         return None
+
+
+def summarize_counters(fetch_db: str, write_db: str) -> dict:
+    """Turn the two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of
+    `bench.py --counters` into HBM bytes per decode call.
+
+    Each counter (KiB per dispatch) is scaled by the factor that makes it read
+    CALIB_BYTES for the calibration copy (the last copy dispatch of the run).
+    The decode call's kernels are the split kernel and the merge kernel."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        rows = sqlite3.connect(db).execute(
+            "select kernel_name, value from counters_collection where counter_name = ? "
+            "order by dispatch_id", (counter,)).fetchall()
+        copies = [v for n, v in rows if "copyBuffer" in n]
+        scale = CALIB_BYTES / (copies[-1] * 1024.0)
+        out = {}
+        for n, v in rows:
+            for key in ("decode_gqa_kernel", "merge_kernel"):
+                if key in n:
+                    out.setdefault(key, []).append(v * 1024.0 * scale)
+        return scale, {k: sum(v) / len(v) for k, v in out.items()}, {k: len(v) for k, v in out.items()}
+
+    fs, fetch, nf = per_kernel(fetch_db, "FETCH_SIZE")
+    ws, write, nw = per_kernel(write_db, "WRITE_SIZE")
+    total = sum(fetch.values()) + sum(write.values())
+    return {
+        "workload": HEADLINE, "source_sha256": _decode_source_hash(),
+        "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+        "fetch_bytes": {k: round(v) for k, v in fetch.items()},
+        "write_bytes": {k: round(v) for k, v in write.items()},
+        "dispatches": {"fetch": nf, "write": nw},
+        "hbm_bytes_per_call": round(total),
+        "algorithmic_bytes_per_call": 134349824,
+        "commands": ["rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch -- python bench.py --counters",
+                     "rocprofv3 --pmc WRITE_SIZE -d <dir> -o write -- python bench.py --counters",
+                     "python bench.py --summarize-counters <fetch_results.db> <write_results.db>"],
+    }
 
 
 def cpu_baseline(workloads, seconds):
@@ -205,6 +282,12 @@ def counters_run(torch, attn, workloads, dev):
 
 def main():
     a = _args()
+    if a.summarize_counters:
+        rec = summarize_counters(*a.summarize_counters)
+        with open(COUNTERS_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % a.gpus, file=sys.stderr)
@@ -220,8 +303,9 @@ def main():
         return
 
     head = bench_workload(torch, attn, workloads, HEADLINE, a.steps, a.warmup, dev)
-    print("headline %s: %.1f GB/s per call, %.1f GB/s per launch (%.3f ms)" % (
-        HEADLINE, head["value"], head["achieved"], head["ms_per_launch"]), file=sys.stderr, flush=True)
+    print("headline %s: %.1f GB/s, %.4f ms per call (eager launches: %.4f ms)" % (
+        HEADLINE, head["value"], head["ms_per_call"], head["eager_ms_per_call"]),
+        file=sys.stderr, flush=True)
     results = {HEADLINE: head}
     if not a.quick:
         for name in workloads.WORKLOADS:
@@ -246,7 +330,7 @@ def main():
                    "accumulate": "fp32", "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": head["kernel"],
                      "achieved": round(head["achieved"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(head["frac"], 4), "traffic": _traffic(head["ms_per_launch"]),
+                     "frac": round(head["frac"], 4), "traffic": _traffic(),
                      "bytes_per_launch": head["work_per_call"]},
         "cpu_baseline": None if cpu is None else {k: (round(v, 4) if isinstance(v, float) else v)
                                                   for k, v in cpu.items()},

@@ -94,16 +94,15 @@ attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
  *   o        [B, Hq, D]               bf16 (output)
  *   lse      [B, Hq]                  fp32 (output, natural log)
  *   workspace: device memory of at least attn_decode_gqa_workspace_bytes()
- *              bytes, zero-filled by the caller before its FIRST use. Each
- *              call leaves its counters at zero again, so later calls need
- *              no clearing. Calls that may run concurrently must not share a
- *              workspace.
+ *              bytes (16-byte aligned). Its contents on entry do not matter:
+ *              it carries the per-split partial results from the split pass
+ *              to the merge pass of the same call. Calls that may run
+ *              concurrently must not share a workspace.
  *
  * The cache is split into chunks processed by separate workgroups, each
- * producing a partial (O, running max, running sum); the partials are merged
- * through their log-sum-exp by the last workgroup of each (b, K/V head) to
- * finish. The split depends only on the shape, so results are bitwise
- * reproducible.
+ * producing a partial (O, running max, running sum); a second kernel on the
+ * same stream merges the partials through their log-sum-exp. The split
+ * depends only on the shape, so results are bitwise reproducible.
  * D must be 128 and Hq/Hkv at most 16.
  * Errors: NULL pointer → ATTN_ERR_NULL_POINTER; B, Hq, Hkv < 1, Hq % Hkv,
  * kv_len < 1 or kv_len > kv_cap → ATTN_ERR_BAD_SHAPE; other D or group size

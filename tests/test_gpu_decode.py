@@ -21,7 +21,8 @@ def _gqa(gpu, w, ws=None):
 @pytest.mark.parametrize("B,Hq,Hkv,kv_len,kv_cap", [
     (1, 4, 1, 1, 8), (2, 8, 2, 5, 64), (2, 32, 8, 255, 300), (1, 8, 8, 256, 256),
     (3, 16, 4, 257, 512), (2, 32, 8, 1000, 1024), (1, 16, 1, 4095, 4100),
-    (1, 32, 2, 3000, 3000), (4, 24, 8, 777, 800), (1, 2, 1, 70000, 70001)])
+    (1, 32, 2, 3000, 3000), (4, 24, 8, 777, 800), (1, 2, 1, 70000, 70001), (8, 32, 8, 2, 8),
+    (4, 32, 8, 3, 3)])
 def test_decode_gqa_matches_oracle(gpu, B, Hq, Hkv, kv_len, kv_cap):
     """Ragged lengths, every group size 1..16 (3 is padded to 4), one and many
     splits; slots past kv_len hold NaN and must never be read."""
@@ -68,8 +69,8 @@ def _mla(gpu, w):
 
 
 @pytest.mark.parametrize("B,Hq,kv_len,kv_cap", [
-    (1, 16, 1, 32), (2, 16, 31, 64), (1, 128, 33, 40), (2, 32, 1000, 1024), (1, 128, 5000, 5000),
-    (1, 144, 70, 100)])
+    (1, 16, 1, 32), (4, 128, 2, 8), (2, 64, 3, 3), (2, 16, 31, 64), (1, 128, 33, 40),
+    (2, 32, 1000, 1024), (1, 128, 5000, 5000), (1, 144, 70, 100)])
 def test_decode_mla_matches_oracle(gpu, B, Hq, kv_len, kv_cap):
     w = workloads.gen_decode_mla(B, Hq, kv_len, kv_cap=kv_cap, seed=kv_len + Hq)
     o, lse = _mla(gpu, w)

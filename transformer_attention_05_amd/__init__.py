@@ -89,17 +89,18 @@ def _need(t, name, dtype, ndim):
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-initialised workspace of at least nbytes for (device, stream).
+    """A workspace of at least nbytes for (device, current stream).
 
-    The kernels leave their counters at zero after every call, so one
-    buffer serves every later call on the same stream; calls on different
-    streams get different buffers.
+    It carries split partials between the two kernels of one decode call, so
+    calls on one stream may share it and calls on different streams get
+    different buffers. Allocate it outside any graph capture (a first call
+    on the stream does that).
     """
     dev = torch.device(device)
     key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 

@@ -2,43 +2,85 @@
 //
 // Decode is memory-bound: about 4 flops per byte of K/V read ("05 · Tích vô
 // hướng, Softmax và toán của Attention", §4), so the design goal is to stream
-// every cached K/V byte from HBM exactly once with enough loads in flight.
+// every cached K/V byte from HBM exactly once and keep the memory pipe full.
 //
 // Decomposition. Workgroup (split, hkv, b) owns keys
 // [split·split_keys, min(kv_len, (split+1)·split_keys)) of one K/V head and
 // all G = Hq/Hkv query heads that share it, so each K/V byte is loaded once
-// and used G times. Its four waves take 64 keys each per 256-key step.
+// and used G times. The split count aims at two resident workgroups per CU
+// (one round, no tail). Its four waves take 32-key chunks in turn and
+// software-pipeline them: the K and V loads of a wave's next chunk are in
+// flight while the current chunk is computed.
 //
-// Per 64-key wave chunk:
-//   * S = K·qᵀ on v_mfma_f32_16x16x32_bf16 with keys as MFMA rows and the
-//     (zero-padded) heads as MFMA columns: lane l feeds K[key = l%16][8 d]
-//     straight from global memory (16 B per lane), fp32 accumulation.
+// Per 32-key wave chunk:
+//   * Sᵀ = K·qᵀ on v_mfma_f32_16x16x32_bf16, keys as MFMA rows, the
+//     (zero-padded) heads as columns; lane l feeds K[key = l%16][8 d] straight
+//     from global memory (16 B per lane), fp32 accumulation.
 //   * online softmax in base 2 (scores pre-multiplied by scale·log2 e):
 //     running max m, running sum ℓ, old sum and output rescaled by
-//     2^(m_old − m_new) ("AI Infra 入门…", §3, online softmax).
-//   * O += P·V on the VALU in fp32: lane l holds V[key][8 d] of one key
-//     (4 keys × 256 B = 1 KiB contiguous per wave load) and gets that key's
-//     weights for every head from a per-wave LDS table.
-// The waves' (m, ℓ, O) are merged in LDS; with one split the workgroup
+//     2^(m_old − m_new) ("AI Infra 入门…", §3, online softmax); the rescale
+//     is skipped when no lane's max moved (α = 1 exactly).
+//   * Oᵀ += Vᵀ·Pᵀ on the same MFMA: P stays in registers (the Sᵀ accumulator
+//     layout is the B-operand layout) as a bf16 pair hi + lo, so the weights
+//     keep about 16 significant bits (one bf16 P would put up to 2^-9
+//     relative error on every weight, which a short cache cannot average
+//     away); V rows, loaded 1 KiB-contiguous
+//     per wave load, pass through a per-wave LDS buffer from which
+//     ds_read_b64_tr_b16 hands each lane one column of a 4-row × 16-column
+//     block — the transposed A operand.
+// The waves' (m, ℓ, Oᵀ) are merged in LDS; with one split the workgroup
 // writes O/ℓ and LSE directly, otherwise it writes its partial (m, ℓ, Õ) to
 // the workspace and a second kernel merges the partials through their
 // log-sum-exp (split-K merge, "AI Infra 入门…", §3). No workgroup waits for
-// another and no cross-workgroup fence is needed: the kernel boundary orders
-// the partial writes before the merge. Slots at or past kv_len are never read.
+// another; the kernel boundary orders the partial writes before the merge.
+// Slots at or past kv_len are never read.
 #include "common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
+#ifndef ATTN_GQA_TARGET_GROUPS
+#define ATTN_GQA_TARGET_GROUPS 512  // workgroups per launch the split aims at
+#endif
+
 constexpr int kD = 128;
 constexpr int kWaves = 4;
-constexpr int kWaveKeys = 64;
-constexpr int kChunk = kWaves * kWaveKeys;  // 256 keys per workgroup step
-constexpr int kTargetGroups = 1024;         // workgroups per launch the split aims at
+constexpr int kWaveKeys = 32;
+constexpr int kChunk = kWaves * kWaveKeys;  // keys per workgroup step
+constexpr int kTargetGroups = ATTN_GQA_TARGET_GROUPS;
+constexpr int kDB = kD / 16;                // 16-row blocks of Oᵀ
 
-template <int GP>
-__global__ __launch_bounds__(256, GP >= 16 ? 1 : 2) void decode_gqa_kernel(
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Physical 16-byte chunk of logical chunk c in row r of a wave's V buffer
+// (rows of 256 B): spreads the 4-row transposed reads over all banks.
+__device__ __forceinline__ int vswz(int r, int c) { return c ^ (2 * (r & 7)); }
+
+struct Chunk {
+    u32x4 k[2][4];  // [16-key block][32-d step], MFMA A layout
+    u32x4 v[8];     // row 4·i + quad, 16-byte chunk hcol
+};
+
+__device__ __forceinline__ void load_chunk(Chunk &c, const uint16_t *kb, const uint16_t *vb,
+                                           int w0, int key_end, int hcol, int quad)
+{
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int key = min(w0 + 16 * blk + hcol, key_end - 1);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            c.k[blk][s] = *(const u32x4 *)(kb + (size_t)key * kD + 32 * s + 8 * quad);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int key = min(w0 + 4 * i + quad, key_end - 1);
+        c.v[i] = *(const u32x4 *)(vb + (size_t)key * kD + 8 * hcol);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, uint16_t *__restrict__ o, float *__restrict__ lse,
     int Hq, int Hkv, int G, int kv_len, int kv_cap, float scale_log2, int splits,
@@ -46,18 +88,18 @@ __global__ __launch_bounds__(256, GP >= 16 ? 1 : 2) void decode_gqa_kernel(
 {
     const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hcol = lane & 15, quad = lane >> 4;
     const int bh = b * Hkv + hkv;
     const int key_begin = split * split_keys;
     const int key_end = min(kv_len, key_begin + split_keys);
     const uint16_t *kbase = kc + (size_t)bh * kv_cap * kD;
     const uint16_t *vbase = vc + (size_t)bh * kv_cap * kD;
 
-    __shared__ float p_lds[kWaves][kWaveKeys * GP + GP];
-    __shared__ float red_o[kWaves][GP][kD];
-    __shared__ float red_m[kWaves][GP], red_l[kWaves][GP];
+    __shared__ __attribute__((aligned(16))) char vbuf[kWaves][kWaveKeys * kD * 2];
+    __shared__ float red_o[kWaves][16][kD + 4];
+    __shared__ float red_m[kWaves][16], red_l[kWaves][16];
 
     // qᵀ as the MFMA B operand: column = head (lane % 16), 8 d per lane.
-    const int hcol = lane & 15, quad = lane >> 4;
     bf16x8 qf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -67,122 +109,112 @@ __global__ __launch_bounds__(256, GP >= 16 ? 1 : 2) void decode_gqa_kernel(
         qf[s] = as<bf16x8>(w);
     }
 
-    float m_run = -INFINITY, l_run = 0.f;  // for head hcol (S layout)
-    float oacc[GP][8];                     // O[h][8·(lane%16) + e] for this lane's key slot
+    float m_run = -INFINITY, l_run = 0.f;  // head hcol
+    f32x4 oacc[kDB];                       // Oᵀ[d = 16·db + 4·quad + i][head hcol]
 #pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) oacc[h][e] = 0.f;
+    for (int db = 0; db < kDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float *pw = p_lds[wave];
-    for (int c0 = key_begin; c0 < key_end; c0 += kChunk) {
-        const int w0 = c0 + wave * kWaveKeys;  // this wave's first key
-        if (w0 >= key_end) break;              // wave-uniform
-        // ---- issue all loads of the chunk (K in MFMA-A layout, V row-major)
-        u32x4 kr[4][4], vr[16];
+    char *vb = vbuf[wave];
+    // transposed reads: lane 16·g + 4·e + c addresses rows 4·g + e and
+    // 16 + 4·g + e, columns 4·c .. 4·c + 3 of a 16-column block
+    const int ve = (lane >> 2) & 3, vcol = lane & 3;
+    const int vr1 = 4 * quad + ve, vr2 = 16 + 4 * quad + ve;
+
+    auto compute = [&](const Chunk &c, int w0) {
+        // ---- Sᵀ = K qᵀ (two 16-key blocks)
+        float sc[8];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const int key = min(w0 + blk * 16 + hcol, key_end - 1);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                kr[blk][s] = *(const u32x4 *)(kbase + (size_t)key * kD + 32 * s + 8 * quad);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = min(w0 + 4 * i + quad, key_end - 1);
-            vr[i] = *(const u32x4 *)(vbase + (size_t)key * kD + 8 * hcol);
-        }
-        // ---- S = K qᵀ: row = key (4·quad + i within a 16-key block), col = head
-        float sc[16];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
+        for (int blk = 0; blk < 2; ++blk) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as<bf16x8>(kr[blk][s]), qf[s], acc);
+            for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as<bf16x8>(c.k[blk][s]), qf[s], acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = w0 + blk * 16 + 4 * quad + i;
-                sc[blk * 4 + i] = key < key_end ? acc[i] * scale_log2 : -INFINITY;
+                const int key = w0 + 16 * blk + 4 * quad + i;
+                sc[4 * blk + i] = key < key_end ? acc[i] * scale_log2 : -INFINITY;
             }
         }
-        // ---- online softmax for head hcol (its 64 keys live in 4 lanes)
+        // ---- V rows → this wave's LDS buffer (row 4·i + quad, chunk hcol)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + quad;
+            *(u32x4 *)(vb + r * (kD * 2) + 16 * vswz(r, hcol)) = c.v[i];
+        }
+        // ---- online softmax for head hcol (its 32 keys live in 4 lanes)
         float mx = sc[0];
 #pragma unroll
-        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sc[j]);
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2_fast(m_run - m_new);  // m_run = -inf → 0
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;  // chunk wholly past key_end
+        const float alpha = exp2_fast(m_run - m_use);
         float ps = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            sc[j] = exp2_fast(sc[j] - m_new);
+        for (int j = 0; j < 8; ++j) {
+            sc[j] = exp2_fast(sc[j] - m_use);
             ps += sc[j];
         }
         l_run = l_run * alpha + ps;
         m_run = m_new;
-        // ---- publish p[key][head] and alpha[head] to this wave's LDS table
-        if (hcol < GP) {
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pw[(blk * 16 + 4 * quad + i) * GP + hcol] = sc[blk * 4 + i];
-            if (quad == 0) pw[kWaveKeys * GP + hcol] = alpha;
+            for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
         }
+        // P as a bf16 pair hi + lo (lo = bf16 of the exact fp32 residual), so the
+        // weights enter the product with about 16 significant bits, not 8
+        u32x4 phi, plo;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t h = pack_bf16x2(sc[2 * t], sc[2 * t + 1]);
+            phi[t] = h;
+            plo[t] = pack_bf16x2(sc[2 * t] - bf16lo(h), sc[2 * t + 1] - bf16hi(h));
+        }
+        const bf16x8 pf_hi = as<bf16x8>(phi), pf_lo = as<bf16x8>(plo);
         wave_lds_sync();
-        // ---- O = alpha·O + Σ_key p·V  (lane: key slot quad, d = 8·hcol..+7)
+        // ---- Oᵀ += Vᵀ Pᵀ; A slot s ↔ key 4·quad + s (s < 4) or 16 + 4·quad + s − 4
 #pragma unroll
-        for (int h = 0; h < GP; ++h) {
-            const float a = pw[kWaveKeys * GP + h];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) oacc[h][e] *= a;
+        for (int db = 0; db < kDB; ++db) {
+            const int ch = 2 * db + (vcol >> 1);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(vb + vr1 * (kD * 2) + 16 * vswz(vr1, ch) + 8 * (vcol & 1)));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(vb + vr2 * (kD * 2) + 16 * vswz(vr2, ch) + 8 * (vcol & 1)));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
+            oacc[db] = mfma16x16x32(as<bf16x8>(a), pf_hi, oacc[db]);
+            oacc[db] = mfma16x16x32(as<bf16x8>(a), pf_lo, oacc[db]);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float *prow = pw + (4 * i + quad) * GP;
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[2 * j] = bf16lo(vr[i][j]);
-                v[2 * j + 1] = bf16hi(vr[i][j]);
-            }
-#pragma unroll
-            for (int h = 0; h < GP; ++h) {
-                const float p = prow[h];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) oacc[h][e] = fmaf(p, v[e], oacc[h][e]);
-            }
-        }
-        wave_lds_sync();
+        wave_lds_sync();  // the buffer is rewritten by the next chunk
+    };
+
+    // ---- software-pipelined chunk loop (ping-pong register buffers)
+    const int first = key_begin + wave * kWaveKeys;
+    Chunk ca, cb;
+    if (first < key_end) load_chunk(ca, kbase, vbase, first, key_end, hcol, quad);
+    for (int w0 = first; w0 < key_end; w0 += 2 * kChunk) {
+        const int w1 = w0 + kChunk;
+        if (w1 < key_end) load_chunk(cb, kbase, vbase, w1, key_end, hcol, quad);
+        compute(ca, w0);
+        if (w1 >= key_end) break;
+        const int w2 = w1 + kChunk;
+        if (w2 < key_end) load_chunk(ca, kbase, vbase, w2, key_end, hcol, quad);
+        compute(cb, w1);
     }
 
-    // ---- merge the four key slots of the wave (lanes l, l^16, l^32, l^48)
-#pragma unroll
-    for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = oacc[h][e];
-            x += shfl_xor(x, 16);
-            x += shfl_xor(x, 32);
-            oacc[h][e] = x;
-        }
+    // ---- merge the four waves through LDS
     l_run += shfl_xor(l_run, 16);
     l_run += shfl_xor(l_run, 32);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red_o[wave][hcol][16 * db + 4 * quad + i] = oacc[db][i];
     if (quad == 0) {
-#pragma unroll
-        for (int h = 0; h < GP; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red_o[wave][h][8 * hcol + e] = oacc[h][e];
-    }
-    if (lane < GP) {
-        red_m[wave][lane] = m_run;
-        red_l[wave][lane] = l_run;
+        red_m[wave][hcol] = m_run;
+        red_l[wave][hcol] = l_run;
     }
     __syncthreads();
-
-    // ---- merge the four waves; write the result or this split's partial
-    for (int idx = tid; idx < GP * kD; idx += 256) {
+    for (int idx = tid; idx < G * kD; idx += 256) {
         const int h = idx / kD, d = idx % kD;
         float M = red_m[0][h];
 #pragma unroll
@@ -190,11 +222,10 @@ __global__ __launch_bounds__(256, GP >= 16 ? 1 : 2) void decode_gqa_kernel(
         float acc = 0.f, l = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float f = exp2_fast(red_m[w][h] - M);  // empty wave: 2^-inf = 0
+            const float f = exp2_fast(red_m[w][h] - M);  // idle wave: 2^-inf = 0
             acc = fmaf(f, red_o[w][h][d], acc);
             l = fmaf(f, red_l[w][h], l);
         }
-        if (h >= G) continue;
         const size_t row = (size_t)b * Hq + hkv * G + h;
         if (splits == 1) {
             o[row * kD + d] = (uint16_t)(pack_bf16x2(acc / l, 0.f) & 0xffffu);
@@ -217,15 +248,13 @@ bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p)
     if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || kv_len < 1) return false;
     const int G = Hq / Hkv;
     if (G > 16) return false;
-    int gp = 1;
-    while (gp < G) gp *= 2;
     const long groups = (long)B * Hkv;
     const int chunks = (kv_len + kChunk - 1) / kChunk;
     int want = (int)((kTargetGroups + groups - 1) / groups);
     int s = want < 1 ? 1 : (want < chunks ? want : chunks);
+    if (s > kMaxSplits) s = kMaxSplits;
     const int per = (chunks + s - 1) / s;
     s = (chunks + per - 1) / per;
-    p->gp = gp;
     p->splits = s;
     p->split_keys = per * kChunk;
     const size_t rows = (size_t)B * Hq;
@@ -243,24 +272,9 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
     float *ws_ml = (float *)(w + p.ws_ml);
     float *ws_part = (float *)(w + p.ws_part);
     const dim3 grid(p.splits, Hkv, B), block(256);
-    const float sl2 = scale * kLog2e;
-    const int G = Hq / Hkv;
-#define ATTN_GQA_CASE(GPV)                                                              \
-    case GPV:                                                                            \
-        decode_gqa_kernel<GPV><<<grid, block, 0, st>>>(                                 \
-            (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, \
-            lse, Hq, Hkv, G, kv_len, kv_cap, sl2, p.splits, p.split_keys, ws_ml, ws_part); \
-                                                                                      \
-        break;
-    switch (p.gp) {
-        ATTN_GQA_CASE(1)
-        ATTN_GQA_CASE(2)
-        ATTN_GQA_CASE(4)
-        ATTN_GQA_CASE(8)
-        ATTN_GQA_CASE(16)
-        default: return hipErrorInvalidValue;
-    }
-#undef ATTN_GQA_CASE
+    decode_gqa_kernel<<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, Hq,
+        Hkv, Hq / Hkv, kv_len, kv_cap, scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, kD, st);

@@ -16,7 +16,8 @@
 //   online softmax in base 2 (running max and sum; the output is rescaled by
 //                  2^(m_old − m_new) only when some lane's max moved);
 //   Oᵀ += Vᵀ·Pᵀ    P stays in registers (the Sᵀ accumulator layout is the
-//                  B-operand layout); the Vᵀ operand is fetched straight from
+//                  B-operand layout) as a bf16 pair hi + lo, so the weights
+//                  keep about 16 significant bits; the Vᵀ operand is fetched straight from
 //                  the row-major latent tile with ds_read_b64_tr_b16, which
 //                  hands each lane one column of a 4-row × 16-column block.
 // Latent tiles (32 rows × 1152 B) move HBM → LDS with global_load_lds_dwordx4
@@ -145,9 +146,16 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
 #pragma unroll
                 for (int db = 0; db < MDB; ++db) oacc[db] *= alpha;
             }
-            const u32x4 pw = {pack_bf16x2(sc[0], sc[1]), pack_bf16x2(sc[2], sc[3]),
-                              pack_bf16x2(sc[4], sc[5]), pack_bf16x2(sc[6], sc[7])};
-            const bf16x8 pf = as<bf16x8>(pw);
+            // P as a bf16 pair hi + lo (lo = bf16 of the exact fp32 residual):
+            // the weights keep about 16 significant bits in the product
+            u32x4 phi, plo;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t h = pack_bf16x2(sc[2 * u], sc[2 * u + 1]);
+                phi[u] = h;
+                plo[u] = pack_bf16x2(sc[2 * u] - bf16lo(h), sc[2 * u + 1] - bf16hi(h));
+            }
+            const bf16x8 pf_hi = as<bf16x8>(phi), pf_lo = as<bf16x8>(plo);
             // Vᵀ operand: slots 0..3 ↔ keys 4·quad + e, slots 4..7 ↔ keys 16 + 4·quad + e
             const char *row1 = tb + vr1 * MROWB + 8 * (vc & 1);
             const char *row2 = tb + vr2 * MROWB + 8 * (vc & 1);
@@ -160,7 +168,8 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
                     (lds_i16x4 *)(row2 + 16 * swz(vr2, c)));
                 const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
                 const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-                oacc[db] = mfma16x16x32(as<bf16x8>(a), pf, oacc[db]);
+                oacc[db] = mfma16x16x32(as<bf16x8>(a), pf_hi, oacc[db]);
+                oacc[db] = mfma16x16x32(as<bf16x8>(a), pf_lo, oacc[db]);
             }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -204,6 +213,7 @@ bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p)
     const long groups = (long)B * hgs;
     int want = (int)((kTargetGroups + groups - 1) / groups);
     int s = want < 1 ? 1 : (want < tiles ? want : tiles);
+    if (s > kMaxSplits) s = kMaxSplits;
     const int per = (tiles + s - 1) / s;
     s = (tiles + per - 1) / per;
     p->splits = s;

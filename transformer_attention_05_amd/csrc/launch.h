@@ -9,7 +9,6 @@ namespace attn {
 
 // ---- GQA decode ----------------------------------------------------------
 struct GqaPlan {
-    int gp;          // padded group size (power of two, >= Hq/Hkv, <= 16)
     int splits;      // workgroups per (batch, K/V head)
     int split_keys;  // keys per split (multiple of the 256-key chunk)
     size_t ws_ml, ws_part, ws_total;  // workspace byte offsets / size
@@ -38,6 +37,7 @@ hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, v
                              float scale, void *ws, hipStream_t s);
 
 // ---- split-K merge through the log-sum-exp (shared by both decodes) -------
+constexpr int kMaxSplits = 128;  // upper bound the planners respect
 // ml [rows][splits][2] = (m, l) in base 2; part [rows][splits][dv] fp32.
 hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse, int rows,
                         int splits, int dv, hipStream_t s);

@@ -4,41 +4,72 @@
 // Each of `splits` partial results for a row holds, in base 2,
 //   m_s  = the split's running max,  ℓ_s = Σ 2^(s_j − m_s),
 //   Õ_s  = Σ 2^(s_j − m_s) · v_j   (not normalised),
-// and the merge computes M = max_s m_s, ℓ = Σ_s 2^(m_s − M) ℓ_s,
-// O = Σ_s 2^(m_s − M) Õ_s / ℓ (rounded once to bf16), LSE = ln2 · (M + log2 ℓ).
+// and the merge computes M = max_s m_s, w_s = 2^(m_s − M), ℓ = Σ_s w_s ℓ_s,
+// O = Σ_s w_s Õ_s / ℓ (rounded once to bf16), LSE = ln2 · (M + log2 ℓ).
 // Splits are summed in index order, so the result is deterministic.
 //
-// Layout: ml[row][split][2] = (m, ℓ), part[row][split][dv]; one thread per
-// (row, 4 consecutive channels).
+// Layout: ml[row][split][2] = (m, ℓ), part[row][split][dv]. One 128-thread
+// block per row; each thread reduces dv/128 channels over the splits, with
+// the loads of up to 16 splits in flight at once.
 #include "common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
-__global__ __launch_bounds__(256) void merge_kernel(
+template <int CPT, int SPT>  // channels per thread (dv / 128), split slots per pass
+__global__ __launch_bounds__(128) void merge_kernel(
     const float *__restrict__ ml, const float *__restrict__ part, uint16_t *__restrict__ o,
-    float *__restrict__ lse, int rows, int splits, int dv)
+    float *__restrict__ lse, int splits)
 {
-    const int per_row = dv / 4;
-    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-    const int row = (int)(gid / per_row), c4 = (int)(gid % per_row);
-    if (row >= rows) return;
-    const float *mr = ml + (size_t)row * splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, mr[2 * s]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        const float f = exp2_fast(mr[2 * s] - M);
-        const f32x4 p = *(const f32x4 *)(part + ((size_t)row * splits + s) * dv + 4 * c4);
-        acc += f * p;
-        l = fmaf(f, mr[2 * s + 1], l);
+    constexpr int DV = 128 * CPT;
+    const int row = blockIdx.x, t = threadIdx.x;
+    const float2 *mr = (const float2 *)(ml + (size_t)row * splits * 2);
+    const float *pr = part + (size_t)row * splits * DV + CPT * t;
+    // splits are taken SPT at a time with every load of a pass in flight at
+    // once (one memory round trip when splits <= SPT); across passes the
+    // running max grows and earlier sums are rescaled, like the online
+    // softmax itself
+    float M = -INFINITY, l = 0.f, acc[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += SPT) {
+        float x[SPT][CPT];
+        float2 st[SPT];
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int s = min(s0 + u, splits - 1);
+            st[u] = mr[s];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) x[u][c] = pr[(size_t)s * DV + c];
+        }
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < SPT; ++u)
+            if (s0 + u < splits) Mn = fmaxf(Mn, st[u].x);
+        const float a = exp2_fast(M - Mn);  // first pass: 2^-inf = 0
+        l *= a;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[c] *= a;
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            // splits past the end were loaded from a clamped index: weight 0
+            const float w = s0 + u < splits ? exp2_fast(st[u].x - Mn) : 0.f;
+            l = fmaf(w, st[u].y, l);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) acc[c] = fmaf(w, x[u][c], acc[c]);
+        }
+        M = Mn;
     }
     const float inv = 1.f / l;
-    const u32x2 w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-    *(u32x2 *)(o + (size_t)row * dv + 4 * c4) = w;
-    if (c4 == 0) lse[row] = (M + log2_fast(l)) * kLn2;
+    uint16_t *orow = o + (size_t)row * DV + CPT * t;
+    if constexpr (CPT == 1) {
+        orow[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPT; c += 2) *(uint32_t *)(orow + c) = pack_bf16x2(acc[c] * inv, acc[c + 1] * inv);
+    }
+    if (t == 0) lse[row] = (M + log2_fast(l)) * kLn2;
 }
 
 }  // namespace
@@ -46,9 +77,14 @@ __global__ __launch_bounds__(256) void merge_kernel(
 hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse, int rows,
                         int splits, int dv, hipStream_t st)
 {
-    const long threads = (long)rows * (dv / 4);
-    merge_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st>>>(
-        ml, part, (uint16_t *)o, lse, rows, splits, dv);
+    if (splits > kMaxSplits) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)rows), block(128);
+    if (dv == 128)
+        merge_kernel<1, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
+    else if (dv == 512)
+        merge_kernel<4, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
