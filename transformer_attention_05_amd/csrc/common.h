@@ -36,6 +36,17 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
 }
 
+// Reductions across the two 32-lane halves of a wave (lane l with l ^ 32):
+// v_permlane32_swap(x, x) returns {x[l], x[l ^ 32]} in its two results.
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Order LDS traffic of one wave: every lane's earlier LDS writes are visible
 // to every lane's later LDS reads (and no read is hoisted above a write).
 // (A workgroup-scope fence waits for the wave's LDS operations to complete;

@@ -22,6 +22,9 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
 hipError_t launch_prefill_bf16(const void *q, const void *k, const void *v, void *o,
                                float *lse, int B, int Hq, int Hkv, int N, int D,
                                float scale, hipStream_t s);
+hipError_t launch_prefill_bf16_d128(const void *q, const void *k, const void *v, void *o,
+                                    float *lse, int B, int Hq, int Hkv, int N, float scale,
+                                    hipStream_t s);
 hipError_t launch_prefill_f32(const float *q, const float *k, const float *v, float *o,
                               float *lse, int B, int Hq, int Hkv, int N, int D,
                               float scale, hipStream_t s);

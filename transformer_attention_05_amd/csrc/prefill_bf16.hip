@@ -212,13 +212,11 @@ hipError_t launch_prefill_bf16(const void *q, const void *k, const void *v, void
                                float *lse, int B, int Hq, int Hkv, int N, int D,
                                float scale, hipStream_t st)
 {
+    if (D == 128) return launch_prefill_bf16_d128(q, k, v, o, lse, B, Hq, Hkv, N, scale, st);
     const int n_qtiles = (N + BR - 1) / BR;
     const dim3 grid((unsigned)(n_qtiles * B * Hq)), block(256);
     const float sl2 = scale * kLog2e;
-    if (D == 128)
-        prefill_bf16_kernel<128><<<grid, block, 0, st>>>((const uint16_t *)q, (const uint16_t *)k,
-            (const uint16_t *)v, (uint16_t *)o, lse, Hq, Hkv, N, n_qtiles, sl2);
-    else if (D == 64)
+    if (D == 64)
         prefill_bf16_kernel<64><<<grid, block, 0, st>>>((const uint16_t *)q, (const uint16_t *)k,
             (const uint16_t *)v, (uint16_t *)o, lse, Hq, Hkv, N, n_qtiles, sl2);
     else
