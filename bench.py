@@ -56,6 +56,8 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", metavar="WORKLOAD",
+                    help="time one named workload and print its result (for profiler runs)")
     ap.add_argument("--counters", action="store_true",
                     help="few headline launches + a calibration copy, for rocprofv3 --pmc runs")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -300,6 +302,10 @@ def main():
     torch.cuda.set_device(dev)
     if a.counters:
         counters_run(torch, attn, workloads, dev)
+        return
+    if a.only:
+        r = bench_workload(torch, attn, workloads, a.only, a.steps, a.warmup, dev)
+        print(json.dumps({a.only: r}), flush=True)
         return
 
     head = bench_workload(torch, attn, workloads, HEADLINE, a.steps, a.warmup, dev)

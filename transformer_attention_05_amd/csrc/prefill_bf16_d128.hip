@@ -1,13 +1,17 @@
 // Causal prefill for head dimension 128, bf16 in/out, fp32 accumulation, gfx950.
 //
-// One workgroup (4 waves) owns a 128-row query tile of one (batch, head);
+// One workgroup (8 waves) owns a 256-row query tile of one (batch, head);
 // each wave owns 32 query rows and keeps their Q fragments in registers for
 // the whole pass (Q outer, K/V inner: the loop order "AI Infra 入门…", §3
 // credits to FlashAttention-2). 64-key K and V tiles stream HBM → LDS with
 // global_load_lds_dwordx4 one tile ahead of use (double-buffered, no register
-// staging), both kept row-major; 16-byte chunks are XOR-swizzled per row,
-// chunk c of row r stored at c ^ (2·(r & 7) | ((r >> 3) & 1)), which keeps the
-// 32-row score reads and the 4-row transposed value reads on distinct banks.
+// staging), both row-major with padded rows: K rows take 272 B (16 B pad) so
+// 16 consecutive rows of a score read start 4 banks apart, V rows take 288 B
+// (32 B pad) so the 4 rows × 32 B of a transposed read cover 32 distinct
+// banks. With padding (rather than a swizzle) every LDS read address is a
+// per-lane base plus a compile-time offset. A wave-wide direct load fills
+// 1 KiB of LDS; the lanes that land on pad slots repeat a neighbour's
+// address.
 //
 //   Sᵀ = K·Qᵀ   v_mfma_f32_32x32x16_bf16, keys as MFMA rows, queries as
 //               columns: each lane owns one query's scores, so the row max and
@@ -17,9 +21,12 @@
 //               stops at the tile holding the tile's last row ("AI Infra
 //               入门…", §3: tile-level classification).
 //   online softmax in base 2: the max is taken on raw scores (scale > 0),
-//               p = 2^(s·scale·log2 e − m) in one FMA + v_exp_f32; the output
-//               rescale α = 2^(m_old − m_new) is skipped when no lane's max
-//               moved (α = 1 exactly) ("05 · Tích vô hướng…", §6).
+//               p = 2^(s·scale·log2 e − m) in one FMA + v_exp_f32. Sums and
+//               output are kept relative to a reference max that moves (with
+//               the rescale by 2^(m_old − m_new), "05 · Tích vô hướng…", §6)
+//               only when the running max outgrows it by more than 8, so
+//               p ≤ 256 and most tiles need no rescale; exact in real
+//               arithmetic because ℓ and O share the reference.
 //   Oᵀ += Vᵀ·Pᵀ P rounded to bf16 in registers (the Sᵀ accumulator layout is
 //               the B-operand layout); the Vᵀ operand comes straight from the
 //               row-major V tile through ds_read_b64_tr_b16.
@@ -33,29 +40,69 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace attn {
 namespace {
 
-constexpr int D = 128, BR = 128, BC = 64, NW = 4;
-constexpr int ROWB = D * 2;               // bytes per K/V row
-constexpr int TILEB = BC * ROWB;          // 16 KiB per tile
-constexpr int NLOAD = TILEB / 1024;       // wave-wide 1 KiB loads per tile and tensor
+// Compile-time choices (the defaults are the measured best).
+#ifndef ATTN_PF_WAVES
+#define ATTN_PF_WAVES 8      // waves per workgroup (32 query rows each)
+#endif
+#ifndef ATTN_PF_NBUF
+#define ATTN_PF_NBUF 2       // K/V tile buffers in LDS (prefetch distance NBUF − 1)
+#endif
+#ifndef ATTN_PF_LAZY
+#define ATTN_PF_LAZY 0       // lazy reference max (1) or exact running max (0)
+#endif
+#ifndef ATTN_PF_SPLITMASK
+#define ATTN_PF_SPLITMASK 1  // separate code for diagonal tiles (1) or masks everywhere (0)
+#endif
+#ifndef ATTN_PF_VROWB
+#define ATTN_PF_VROWB 320    // V tile row stride in LDS (bytes)
+#endif
+#ifndef ATTN_PF_SCHED
+#define ATTN_PF_SCHED 0      // keep each 16-key step's transposed reads together
+#endif
+
+constexpr int NW = ATTN_PF_WAVES, NBUF = ATTN_PF_NBUF;
+constexpr int D = 128, BR = 32 * NW, BC = 64;
+constexpr int KROWB = 272, VROWB = ATTN_PF_VROWB;   // padded LDS row strides (bytes)
+constexpr int KSLOT = KROWB / 16, VSLOT = VROWB / 16;
+constexpr int KTILEB = BC * KROWB;        // 17 KiB
+constexpr int VTILEB = BC * VROWB;        // 18 KiB
+constexpr int KLOADS = KTILEB / 1024, VLOADS = VTILEB / 1024;
+constexpr int KPW = (KLOADS + NW - 1) / NW, VPW = (VLOADS + NW - 1) / NW;
+constexpr int LOADS_MIN = KLOADS / NW + VLOADS / NW;  // loads every wave issues per tile
 constexpr int KS = D / 16, DB = D / 32;
 constexpr int kXcds = 8;
+constexpr float kLazy = 8.f;  // base-2 headroom before the reference max moves
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz_x(int r) { return (2 * (r & 7)) | ((r >> 3) & 1); }
+// Global byte offset, within a K/V tile, of the 16 bytes that lane `lane` of
+// wave-wide direct load `idx` brings into LDS slot 64·idx + lane (rows of
+// `slots` 16-byte slots, the last slots of a row being padding). Rows past
+// `rows` (the end of the sequence) are clamped to the last valid row.
+__device__ __forceinline__ uint32_t tile_src(int idx, int lane, int slots, int rows) {
+    const int s = 64 * idx + lane;
+    const int r = min(s / slots, rows - 1);
+    const int c = min(s % slots, 15);       // pad slots repeat chunk 15
+    return (uint32_t)(r * (D * 2) + 16 * c);
+}
 
-__global__ __launch_bounds__(256, 2) void prefill_d128_kernel(
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+__global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
     int Hq, int Hkv, int N, int n_qtiles, float scale_log2)
 {
-    __shared__ __attribute__((aligned(1024))) char kt[2][TILEB];
-    __shared__ __attribute__((aligned(1024))) char vt[2][TILEB];
+    __shared__ __attribute__((aligned(1024))) char kt[NBUF][KTILEB];
+    __shared__ __attribute__((aligned(1024))) char vt[NBUF][VTILEB];
 
     // ---- work item: contiguous runs of the (group, heavy-first) list per XCD
     const int G = Hq / Hkv;
@@ -72,10 +119,11 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(
     const int q0 = qt * BR;
 
     const uint16_t *Qp = q + (size_t)bhq * N * D;
-    const uint16_t *Kp = k + (size_t)grp * N * D;
-    const uint16_t *Vp = v + (size_t)grp * N * D;
+    const char *Kp = (const char *)(k + (size_t)grp * N * D);
+    const char *Vp = (const char *)(v + (size_t)grp * N * D);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int col = lane & 31, half = lane >> 5;
     const int qrow = q0 + wave * 32 + col;
     const int wrow0 = q0 + wave * 32, wrow1 = wrow0 + 31;
@@ -88,17 +136,37 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(
         for (int ks = 0; ks < KS; ++ks) qf[ks] = as<bf16x8>(*(const u32x4 *)(qr + 16 * ks));
     }
 
-    // HBM → LDS: wave-wide load idx fills tile bytes [1024·idx, +1024): rows
-    // 4·idx + lane/16, physical chunk lane % 16
-    auto load_tile = [&](int j, int buf) {
+    // this lane's source offsets for its wave's direct loads of a full tile
+    uint32_t ksrc[KPW], vsrc[VPW];
 #pragma unroll
-        for (int t = 0; t < NLOAD / NW; ++t) {
-            const int idx = wave + NW * t;
-            const int r = 4 * idx + (lane >> 4);
-            const int c = (lane & 15) ^ swz_x(r);
-            const size_t off = (size_t)min(j * BC + r, N - 1) * D + 8 * c;
-            __builtin_amdgcn_global_load_lds((const void *)(Kp + off), (lds_void *)&kt[buf][1024 * idx], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(Vp + off), (lds_void *)&vt[buf][1024 * idx], 16, 0, 0);
+    for (int t = 0; t < KPW; ++t) ksrc[t] = tile_src(min(wave + NW * t, KLOADS - 1), lane, KSLOT, BC);
+#pragma unroll
+    for (int t = 0; t < VPW; ++t) vsrc[t] = tile_src(min(wave + NW * t, VLOADS - 1), lane, VSLOT, BC);
+
+    // Loads 0 .. NW·⌊LOADS/NW⌋ − 1 are spread evenly over the waves; the
+    // remaining LOADS % NW go to the first waves.
+    auto issue = [&](const char *src, char *dst) {
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
+    };
+    auto load_tile = [&](int j, int buf) {
+        const char *kb = Kp + (size_t)j * BC * D * 2, *vb = Vp + (size_t)j * BC * D * 2;
+        const int rows = N - j * BC;  // valid rows of this tile
+        if (rows >= BC) {
+#pragma unroll
+            for (int t = 0; t < KLOADS / NW; ++t) issue(kb + ksrc[t], &kt[buf][1024 * (wave + NW * t)]);
+#pragma unroll
+            for (int t = 0; t < VLOADS / NW; ++t) issue(vb + vsrc[t], &vt[buf][1024 * (wave + NW * t)]);
+            if (wave < KLOADS % NW)
+                issue(kb + ksrc[KPW - 1], &kt[buf][1024 * (wave + NW * (KPW - 1))]);
+            if (wave < VLOADS % NW)
+                issue(vb + vsrc[VPW - 1], &vt[buf][1024 * (wave + NW * (VPW - 1))]);
+        } else {  // last, partial tile: rows past the sequence repeat its last row
+            for (int t = 0; t < KPW; ++t)
+                if (wave + NW * t < KLOADS)
+                    issue(kb + tile_src(wave + NW * t, lane, KSLOT, rows), &kt[buf][1024 * (wave + NW * t)]);
+            for (int t = 0; t < VPW; ++t)
+                if (wave + NW * t < VLOADS)
+                    issue(vb + tile_src(wave + NW * t, lane, VSLOT, rows), &vt[buf][1024 * (wave + NW * t)]);
         }
     };
 
@@ -107,108 +175,141 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    // m_ref: the reference max the sums and the output are kept relative to;
+    // it trails the true running max by less than kLazy (base 2).
+    float m_ref = -INFINITY, l_run = 0.f, lq_run = 0.f;
 
-    // per-lane LDS offsets (bytes within a tile)
-    const int ks_x = swz_x(col);                        // rows 32·kb + col share it
+    // per-lane LDS read offsets (bytes within a tile); the loops add constants
+    const int k_lane = col * KROWB + 16 * half;
     const int g = lane >> 4, e = (lane >> 2) & 3, cq = lane & 3;
-    const int vr1 = 4 * half + e;                       // + 16·mm; read 2 adds 8 rows
-    const int vchunk0 = 2 * (g & 1) + (cq >> 1);        // + 4·db
-    const int vbyte = 8 * (cq & 1);
+    const int v_lane = (4 * half + e) * VROWB + 32 * (g & 1) + 8 * cq;
 
     const int n_kt = min(N - 1, q0 + BR - 1) / BC + 1;
-    load_tile(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+        if (t < n_kt) load_tile(t, t);
+    // tile 0 resident: only the loads of tiles 1 .. NBUF-2 may be outstanding
+    if (NBUF == 3 && n_kt > 1) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
     __syncthreads();
 
-    for (int j = 0; j < n_kt; ++j) {
-        const int cur = j & 1;
-        if (j + 1 < n_kt) load_tile(j + 1, cur ^ 1);
-        const int kt0 = j * BC;
-        if (kt0 <= wrow1 && wrow0 < N) {
-            const char *kb_ = kt[cur];
-            const char *vb_ = vt[cur];
-            // ---- Sᵀ = K Qᵀ, the two 32-key blocks interleaved
-            f32x16 sacc[2];
+    // One key tile for this wave: Sᵀ, online softmax, Oᵀ update. MASK is set
+    // only for tiles that cross the wave's diagonal.
+    auto tile_step = [&](const char *kb_, const char *vb_, int kt0, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        // ---- Sᵀ = K Qᵀ, the two 32-key blocks interleaved
+        f32x16 sacc[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+            for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const u32x4 a = *(const u32x4 *)(kb_ + (32 * kb + col) * ROWB + 16 * ((2 * ks + half) ^ ks_x));
-                    sacc[kb] = mfma32x32x16(as<bf16x8>(a), qf[ks], sacc[kb]);
-                }
-            // ---- diagonal mask; lane's keys: kt0 + 32kb + 8(i/4) + 4half + i%4
-            float mx = -INFINITY;
-            if (kt0 + BC - 1 > wrow0) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kt0 + kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                        if (key > qrow) sacc[kb][i] = -INFINITY;
-                    }
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 a = *(const u32x4 *)(kb_ + k_lane + kb * 32 * KROWB + 32 * ks);
+                sacc[kb] = mfma32x32x16(as<bf16x8>(a), qf[ks], sacc[kb]);
             }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-            mx = half_max(mx);
-            const float m_new = fmaxf(m_run, mx * scale_log2);  // finite: key 0 is in tile 0
-            const float alpha = exp2_fast(m_run - m_new);
-            float ps = 0.f;
+        // ---- mask (key > query → −inf); lane's keys: kt0 + 32kb + 8(i/4) + 4half + i%4
+        if constexpr (MASK) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = exp2_fast(fmaf(sacc[kb][i], scale_log2, -m_new));
-                    sacc[kb][i] = p;
-                    ps += p;
+                    const int key = kt0 + kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+                    if (key > qrow) sacc[kb][i] = -INFINITY;
                 }
-            l_run = l_run * alpha + ps;
-            m_run = m_new;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        }
+        float mx = -INFINITY;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        const float m_tile = half_max(mx) * scale_log2;
+#if ATTN_PF_LAZY
+        // lazy rescale: move the reference only when the max outgrew it by
+        // more than kLazy, so 2^(s − m_ref) ≤ 2^kLazy (exact in real arithmetic:
+        // sums and output share the reference)
+        const bool move = m_tile > m_ref + kLazy;  // m_ref = −inf: first visible tile
+#else
+        const bool move = m_tile > m_ref;          // exact running max
+#endif
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float m_new = move ? m_tile : m_ref;
+            const float alpha = exp2_fast(m_ref - m_new);  // 1 where not moved, 0 at first
+            l_run *= alpha;
+            lq_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            m_ref = m_new;
+        }
+        float ps = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = exp2_fast(fmaf(sacc[kb][i], scale_log2, -m_ref));
+                sacc[kb][i] = p;
+                ps += p;
             }
-            // ---- Pᵀ fragments: 16-key step mm uses S registers 8(mm%2)..+7 of block mm/2
-            bf16x8 pf[4];
+        l_run += ps;
+        // ---- Pᵀ fragments: 16-key step mm uses S registers 8(mm%2)..+7 of block
+        // mm/2. With the lazy reference the largest weight is not 1, so lq sums
+        // the same bf16-rounded weights the product uses and O is normalised by
+        // it: O is then an exact weighted average of the weights it was built
+        // from (a one-hot row stays exact); the LSE uses the fp32 sum.
+        bf16x8 pf[4];
+        float pq = 0.f;
 #pragma unroll
-            for (int mm = 0; mm < 4; ++mm) {
-                u32x4 wv;
+        for (int mm = 0; mm < 4; ++mm) {
+            u32x4 wv;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    wv[t] = pack_bf16x2(sacc[mm / 2][8 * (mm % 2) + 2 * t], sacc[mm / 2][8 * (mm % 2) + 2 * t + 1]);
-                pf[mm] = as<bf16x8>(wv);
+            for (int t = 0; t < 4; ++t) {
+                wv[t] = pack_bf16x2(sacc[mm / 2][8 * (mm % 2) + 2 * t], sacc[mm / 2][8 * (mm % 2) + 2 * t + 1]);
+                if (ATTN_PF_LAZY) pq = sum_bf16x2(wv[t], pq);
             }
-            // ---- Oᵀ += Vᵀ Pᵀ; A slot t ↔ key 16mm + 8(t/4) + 4half + t%4
+            pf[mm] = as<bf16x8>(wv);
+        }
+        if (ATTN_PF_LAZY) lq_run += pq;
+        // ---- Oᵀ += Vᵀ Pᵀ; A slot t ↔ key 16mm + 8(t/4) + 4half + t%4.
+        // Lane 16g + 4e + c addresses V rows 16mm + 4half + e (and + 8),
+        // columns 32db + 16(g&1) + 4c .. + 3.
 #pragma unroll
-            for (int mm = 0; mm < 4; ++mm) {
-                const int r1 = 16 * mm + vr1, r2 = r1 + 8;
+        for (int mm = 0; mm < 4; ++mm) {
+            if (ATTN_PF_SCHED && mm) __builtin_amdgcn_sched_barrier(0);  // keep each step's reads together
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int ch = 4 * db + vchunk0;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(vb_ + r1 * ROWB + 16 * (ch ^ swz_x(r1)) + vbyte));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(vb_ + r2 * ROWB + 16 * (ch ^ swz_x(r2)) + vbyte));
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                    const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-                    oacc[db] = mfma32x32x16(as<bf16x8>(a), pf[mm], oacc[db]);
-                }
+            for (int db = 0; db < DB; ++db) {
+                const char *p1 = vb_ + v_lane + 16 * mm * VROWB + 64 * db;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p1);
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p1 + 8 * VROWB));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
+                oacc[db] = mfma32x32x16(as<bf16x8>(a), pf[mm], oacc[db]);
             }
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
+    for (int j = 0; j < n_kt; ++j) {
+        const int cur = j % NBUF;
+        const int jn = j + NBUF - 1;  // tile to prefetch
+        if (jn < n_kt) load_tile(jn, jn % NBUF);
+        const int kt0 = j * BC;
+#if ATTN_PF_SPLITMASK
+        if (wrow0 < N && kt0 + BC - 1 <= wrow0)          // wholly visible to the wave
+            tile_step(kt[cur], vt[cur], kt0, std::false_type{});
+        else if (wrow0 < N && kt0 <= wrow1)              // crosses the wave's diagonal
+            tile_step(kt[cur], vt[cur], kt0, std::true_type{});
+#else
+        if (wrow0 < N && kt0 <= wrow1) tile_step(kt[cur], vt[cur], kt0, std::true_type{});
+#endif
+        // tile j+1 resident before the barrier; newer prefetches may stay in flight
+        if (NBUF == 3 && jn < n_kt) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
         __syncthreads();
     }
 
-    // ---- epilogue: O = Oᵀ/ℓ, one rounding; LSE in natural log
-    const float l_tot = half_sum(l_run);
+    // ---- epilogue: O = Oᵀ/ℓq, one rounding; LSE (natural log) from the fp32 sum
+    const float l_tot = half_sum(l_run), lq_tot = half_sum(lq_run);
     if (qrow < N) {
-        const float inv = 1.f / l_tot;
+        const float inv = 1.f / (ATTN_PF_LAZY ? lq_tot : l_tot);
         uint16_t *orow = o + ((size_t)bhq * N + qrow) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -218,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void prefill_d128_kernel(
                                   pack_bf16x2(oacc[db][4 * gg + 2] * inv, oacc[db][4 * gg + 3] * inv)};
                 *(u32x2 *)(orow + db * 32 + 8 * gg + 4 * half) = wv;
             }
-        if (half == 0) lse[(size_t)bhq * N + qrow] = (m_run + log2_fast(l_tot)) * kLn2;
+        if (half == 0) lse[(size_t)bhq * N + qrow] = (m_ref + log2_fast(l_tot)) * kLn2;
     }
 }
 
@@ -229,7 +330,7 @@ hipError_t launch_prefill_bf16_d128(const void *q, const void *k, const void *v,
                                     hipStream_t st)
 {
     const int n_qtiles = (N + BR - 1) / BR;
-    const dim3 grid((unsigned)(n_qtiles * B * Hq)), block(256);
+    const dim3 grid((unsigned)(n_qtiles * B * Hq)), block(64 * NW);
     prefill_d128_kernel<<<grid, block, 0, st>>>((const uint16_t *)q, (const uint16_t *)k,
                                                 (const uint16_t *)v, (uint16_t *)o, lse, Hq, Hkv, N,
                                                 n_qtiles, scale * kLog2e);
