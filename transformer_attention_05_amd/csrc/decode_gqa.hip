@@ -233,10 +233,7 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
         } else {
             const size_t slot = row * splits + split;
             ws_part[slot * kD + d] = acc;
-            if (d == 0) {
-                ws_ml[2 * slot] = M;
-                ws_ml[2 * slot + 1] = l;
-            }
+            if (d == 0) *(float4 *)(ws_ml + 4 * slot) = make_float4(M, l, l, 0.f);
         }
     }
 }
@@ -259,7 +256,7 @@ bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p)
     p->split_keys = per * kChunk;
     const size_t rows = (size_t)B * Hq;
     p->ws_ml = 0;
-    p->ws_part = align_up(sizeof(float) * 2 * rows * s, 256);
+    p->ws_part = align_up(sizeof(float) * 4 * rows * s, 256);
     p->ws_total = s == 1 ? 256 : p->ws_part + align_up(sizeof(float) * kD * rows * s, 256);
     return true;
 }

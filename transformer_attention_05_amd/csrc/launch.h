@@ -41,7 +41,8 @@ hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, v
 
 // ---- split-K merge through the log-sum-exp (shared by both decodes) -------
 constexpr int kMaxSplits = 128;  // upper bound the planners respect
-// ml [rows][splits][2] = (m, l) in base 2; part [rows][splits][dv] fp32.
+// ml [rows][splits] = float4 (m, ℓ, λ, unused) in base 2 (ℓ feeds the LSE,
+// λ normalises O); part [rows][splits][dv] fp32.
 hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse, int rows,
                         int splits, int dv, hipStream_t s);
 

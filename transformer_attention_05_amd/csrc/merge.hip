@@ -2,15 +2,21 @@
 // the local reductions of Flash-Decoding mergeable).
 //
 // Each of `splits` partial results for a row holds, in base 2,
-//   m_s  = the split's running max,  ℓ_s = Σ 2^(s_j − m_s),
+//   m_s  = the split's reference max (any value ≥ its scores minus a few),
+//   ℓ_s  = Σ 2^(s_j − m_s) in fp32, the sum the log-sum-exp is made of,
+//   λ_s  = Σ of the weights 2^(s_j − m_s) as they entered the product with V
+//          (equal to ℓ_s where those weights are exact; the sum of their
+//          rounded values otherwise, so that O is a convex combination of the
+//          values with exactly the weights used),
 //   Õ_s  = Σ 2^(s_j − m_s) · v_j   (not normalised),
-// and the merge computes M = max_s m_s, w_s = 2^(m_s − M), ℓ = Σ_s w_s ℓ_s,
-// O = Σ_s w_s Õ_s / ℓ (rounded once to bf16), LSE = ln2 · (M + log2 ℓ).
-// Splits are summed in index order, so the result is deterministic.
+// and the merge computes M = max_s m_s, w_s = 2^(m_s − M),
+// O = Σ_s w_s Õ_s / Σ_s w_s λ_s (rounded once to bf16) and
+// LSE = ln2 · (M + log2 Σ_s w_s ℓ_s). Splits are summed in index order, so
+// the result is deterministic.
 //
-// Layout: ml[row][split][2] = (m, ℓ), part[row][split][dv]. One 128-thread
-// block per row; each thread reduces dv/128 channels over the splits, with
-// the loads of up to 16 splits in flight at once.
+// Layout: ml[row][split] = (m, ℓ, λ, unused) as float4, part[row][split][dv].
+// One 128-thread block per row; each thread reduces dv/128 channels over the
+// splits, with the loads of up to 16 splits in flight at once.
 #include "common.h"
 #include "launch.h"
 
@@ -24,18 +30,18 @@ __global__ __launch_bounds__(128) void merge_kernel(
 {
     constexpr int DV = 128 * CPT;
     const int row = blockIdx.x, t = threadIdx.x;
-    const float2 *mr = (const float2 *)(ml + (size_t)row * splits * 2);
+    const float4 *mr = (const float4 *)(ml + (size_t)row * splits * 4);
     const float *pr = part + (size_t)row * splits * DV + CPT * t;
     // splits are taken SPT at a time with every load of a pass in flight at
     // once (one memory round trip when splits <= SPT); across passes the
     // running max grows and earlier sums are rescaled, like the online
     // softmax itself
-    float M = -INFINITY, l = 0.f, acc[CPT];
+    float M = -INFINITY, l = 0.f, lam = 0.f, acc[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
     for (int s0 = 0; s0 < splits; s0 += SPT) {
         float x[SPT][CPT];
-        float2 st[SPT];
+        float4 st[SPT];
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
             const int s = min(s0 + u, splits - 1);
@@ -49,6 +55,7 @@ __global__ __launch_bounds__(128) void merge_kernel(
             if (s0 + u < splits) Mn = fmaxf(Mn, st[u].x);
         const float a = exp2_fast(M - Mn);  // first pass: 2^-inf = 0
         l *= a;
+        lam *= a;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) acc[c] *= a;
 #pragma unroll
@@ -56,12 +63,13 @@ __global__ __launch_bounds__(128) void merge_kernel(
             // splits past the end were loaded from a clamped index: weight 0
             const float w = s0 + u < splits ? exp2_fast(st[u].x - Mn) : 0.f;
             l = fmaf(w, st[u].y, l);
+            lam = fmaf(w, st[u].z, lam);
 #pragma unroll
             for (int c = 0; c < CPT; ++c) acc[c] = fmaf(w, x[u][c], acc[c]);
         }
         M = Mn;
     }
-    const float inv = 1.f / l;
+    const float inv = 1.f / lam;
     uint16_t *orow = o + (size_t)row * DV + CPT * t;
     if constexpr (CPT == 1) {
         orow[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);

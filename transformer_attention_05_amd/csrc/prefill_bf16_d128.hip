@@ -93,8 +93,6 @@ __device__ __forceinline__ uint32_t tile_src(int idx, int lane, int slots, int r
     return (uint32_t)(r * (D * 2) + 16 * c);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
