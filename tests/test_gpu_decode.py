@@ -87,3 +87,34 @@ def test_decode_mla_32k_workload_sampled_batches(gpu):
     bs = [0, w.B - 1]
     o_ref, lse_ref = oracle.decode_mla_absorbed(w.q[bs], w.ckv[bs], w.kv_len, w.Dv, w.scale)
     check_bf16(host(o[bs]), o_ref, host(lse[bs]), lse_ref, "decode_mla_absorbed_32k")
+
+
+@pytest.mark.parametrize("kv_len", [512, 513])
+def test_decode_mla_weight_residual_cutoff(gpu, kv_len):
+    """Caches of up to 512 keys add the product with the bf16 residual of the
+    weights; longer caches use bf16 weights alone. Both sides of the cut meet
+    the bar."""
+    w = workloads.gen_decode_mla(2, 64, kv_len, kv_cap=kv_len + 7, seed=kv_len)
+    o, lse = _mla(gpu, w)
+    o_ref, lse_ref = oracle.decode_mla_absorbed(w.q, w.ckv, w.kv_len, w.Dv, w.scale)
+    check_bf16(host(o), o_ref, host(lse), lse_ref, "mla cutoff kv_len=%d" % kv_len)
+
+
+@pytest.mark.parametrize("kv_len", [300, 1500])
+def test_decode_mla_rising_scores(gpu, kv_len):
+    """The rope channels of the latent rows (part of each key, not of its
+    value) are scaled up with the row's position, ×1 → ×48: the scores of
+    later tiles exceed the running maximum by far more than the kernel's
+    reference-max slack again and again, so every rescale path runs, and the
+    softmax ends up dominated by a few late keys while the values stay O(1).
+    Slots past kv_len stay NaN."""
+    w = workloads.gen_decode_mla(1, 32, kv_len, kv_cap=kv_len + 5, seed=9)
+    x = oracle.widen(w.ckv[:, :kv_len])
+    x[..., w.Dv:] *= np.linspace(1.0, 48.0, kv_len)[None, :, None]
+    w.ckv[:, :kv_len] = workloads.round_to_bf16_bits(x)
+    o, lse = _mla(gpu, w)
+    o_ref, lse_ref = oracle.decode_mla_absorbed(w.q, w.ckv, w.kv_len, w.Dv, w.scale)
+    # the scores really do climb by several reference-max slacks (2^8 each)
+    s = oracle.widen(w.q[0]) @ oracle.widen(w.ckv[0, :kv_len]).T * w.scale / np.log(2.0)
+    assert (s[:, -32:].max(axis=1) - s[:, :32].max(axis=1)).min() > 3 * 8
+    check_bf16(host(o), o_ref, host(lse), lse_ref, "mla rising scores kv_len=%d" % kv_len)

@@ -6,9 +6,9 @@
 // credits to FlashAttention-2). 64-key K and V tiles stream HBM → LDS with
 // global_load_lds_dwordx4 one tile ahead of use (double-buffered, no register
 // staging), both row-major with padded rows: K rows take 272 B (16 B pad) so
-// 16 consecutive rows of a score read start 4 banks apart, V rows take 288 B
-// (32 B pad) so the 4 rows × 32 B of a transposed read cover 32 distinct
-// banks. With padding (rather than a swizzle) every LDS read address is a
+// the rows of a score read start 4 banks apart, V rows take 320 B (64 B pad)
+// so the 8 rows × 32 B that one 32-lane phase of a transposed read touches
+// fall on distinct banks (both measured conflict-free). With padding (rather than a swizzle) every LDS read address is a
 // per-lane base plus a compile-time offset. A wave-wide direct load fills
 // 1 KiB of LDS; the lanes that land on pad slots repeat a neighbour's
 // address.
@@ -21,12 +21,13 @@
 //               stops at the tile holding the tile's last row ("AI Infra
 //               入门…", §3: tile-level classification).
 //   online softmax in base 2: the max is taken on raw scores (scale > 0),
-//               p = 2^(s·scale·log2 e − m) in one FMA + v_exp_f32. Sums and
-//               output are kept relative to a reference max that moves (with
-//               the rescale by 2^(m_old − m_new), "05 · Tích vô hướng…", §6)
-//               only when the running max outgrows it by more than 8, so
-//               p ≤ 256 and most tiles need no rescale; exact in real
-//               arithmetic because ℓ and O share the reference.
+//               p = 2^(s·scale·log2 e − m) in one FMA + v_exp_f32, with the
+//               running max m and the rescale of ℓ and O by 2^(m_old − m_new)
+//               ("05 · Tích vô hướng…", §6), skipped when no lane's max moved.
+//               (ATTN_PF_LAZY=1 builds a variant whose reference max moves
+//               only when the running max outgrows it by more than 8, with O
+//               normalised by the sum of the bf16 weights it was built from;
+//               it measured no faster here.)
 //   Oᵀ += Vᵀ·Pᵀ P rounded to bf16 in registers (the Sᵀ accumulator layout is
 //               the B-operand layout); the Vᵀ operand comes straight from the
 //               row-major V tile through ds_read_b64_tr_b16.
