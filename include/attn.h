@@ -73,8 +73,11 @@ typedef enum attn_dtype {
  * Query head hq uses K/V head hq / (Hq/Hkv) (contiguous GQA groups).
  * dtype ATTN_BF16: D in {64, 128}; MFMA bf16 products, fp32 accumulation.
  * dtype ATTN_FP32: D in {64, 128}; fp32 throughout.
+ * scale multiplies every score (1/√D for plain attention); it must be finite
+ * and > 0.
  * Errors: NULL pointer → ATTN_ERR_NULL_POINTER; B, Hq, Hkv, N < 1 or
- * Hq % Hkv != 0 or a tensor above 2^31 elements → ATTN_ERR_BAD_SHAPE;
+ * Hq % Hkv != 0, a tensor above 2^31 elements, or a scale that is not finite
+ * and positive → ATTN_ERR_BAD_SHAPE;
  * other D or dtype → ATTN_ERR_UNSUPPORTED; launch failure → ATTN_ERR_HIP.
  */
 attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
@@ -105,7 +108,8 @@ attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
  * depends only on the shape, so results are bitwise reproducible.
  * D must be 128 and Hq/Hkv at most 16.
  * Errors: NULL pointer → ATTN_ERR_NULL_POINTER; B, Hq, Hkv < 1, Hq % Hkv,
- * kv_len < 1 or kv_len > kv_cap → ATTN_ERR_BAD_SHAPE; other D or group size
+ * kv_len < 1 or kv_len > kv_cap, or a scale that is not finite and positive
+ * → ATTN_ERR_BAD_SHAPE; other D or group size
  * → ATTN_ERR_UNSUPPORTED; workspace NULL or too small → ATTN_ERR_WORKSPACE;
  * launch failure → ATTN_ERR_HIP.
  */

@@ -40,8 +40,11 @@ def test_status_strings(lib):
         assert attn.status_string(code) == name
 
 
-def _prefill(lib, dtype=0, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=64, D=64):
-    return lib.attn_prefill_causal(dtype, q, k, v, o, lse, B, Hq, Hkv, N, D, 0.125, None)
+def _prefill(lib, dtype=0, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, N=64, D=64, scale=0.125):
+    return lib.attn_prefill_causal(dtype, q, k, v, o, lse, B, Hq, Hkv, N, D, scale, None)
+
+
+BAD_SCALES = (0.0, -0.125, float("inf"), float("nan"))
 
 
 def test_prefill_validation(lib):
@@ -55,11 +58,14 @@ def test_prefill_validation(lib):
     assert _prefill(lib, dtype=7) == UNSUP
     assert _prefill(lib, q=P + 2) == UNSUP              # misaligned
     assert _prefill(lib, B=1 << 12, Hq=64, Hkv=8, N=1 << 16, D=128) == SHAPE  # > 2^31 elements
+    for s in BAD_SCALES:  # the kernels need a finite, positive scale
+        assert _prefill(lib, scale=s) == SHAPE
+        assert "scale" in attn.last_error()
 
 
 def _gqa(lib, q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, kv_len=100, kv_cap=128, D=128,
-         ws=P, ws_bytes=1 << 30):
-    return lib.attn_decode_gqa(q, k, v, o, lse, B, Hq, Hkv, kv_len, kv_cap, D, 0.1, ws,
+         ws=P, ws_bytes=1 << 30, scale=0.1):
+    return lib.attn_decode_gqa(q, k, v, o, lse, B, Hq, Hkv, kv_len, kv_cap, D, scale, ws,
                                ws_bytes, None)
 
 
@@ -70,6 +76,8 @@ def test_decode_gqa_validation(lib):
     assert _gqa(lib, Hq=6, Hkv=4) == SHAPE
     assert _gqa(lib, D=64) == UNSUP
     assert _gqa(lib, Hq=64, Hkv=2) == UNSUP             # group of 32 > 16
+    for s in BAD_SCALES:
+        assert _gqa(lib, scale=s) == SHAPE
     need = attn.attn_decode_gqa_workspace_bytes(2, 8, 2, 100, 128)
     assert need > 0
     assert _gqa(lib, ws=None) == WS
@@ -85,8 +93,8 @@ def test_decode_gqa_workspace_query():
 
 
 def _mla(lib, q=P, c=P, o=P, lse=P, B=2, Hq=128, kv_len=1000, kv_cap=1024, Dqk=576, Dv=512,
-         ws=P, ws_bytes=1 << 30):
-    return lib.attn_decode_mla_absorbed(q, c, o, lse, B, Hq, kv_len, kv_cap, Dqk, Dv, 0.07,
+         ws=P, ws_bytes=1 << 30, scale=0.07):
+    return lib.attn_decode_mla_absorbed(q, c, o, lse, B, Hq, kv_len, kv_cap, Dqk, Dv, scale,
                                         ws, ws_bytes, None)
 
 
@@ -97,6 +105,8 @@ def test_decode_mla_validation(lib):
     assert _mla(lib, Dqk=512, Dv=576) == SHAPE
     assert _mla(lib, Dqk=192, Dv=128) == UNSUP
     assert _mla(lib, Hq=20) == UNSUP
+    for s in BAD_SCALES:
+        assert _mla(lib, scale=s) == SHAPE
     need = attn.attn_decode_mla_workspace_bytes(2, 128, 1000)
     assert need > 0
     assert _mla(lib, ws_bytes=need - 1) == WS

@@ -27,6 +27,9 @@ attn_status ok()
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+// The kernels take row maxima of unscaled scores, which is only the max of
+// the scaled ones for a positive scale.
+bool good_scale(float s) { return s > 0.f && s <= 3.4e38f; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 constexpr long long kMaxElems = (1ll << 31) - 1;
@@ -66,6 +69,8 @@ attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
         return fail(ATTN_ERR_BAD_SHAPE, "attn_prefill_causal: B, Hq, Hkv, N, D must be >= 1");
     if (Hq % Hkv)
         return fail(ATTN_ERR_BAD_SHAPE, "attn_prefill_causal: Hq (%d) not a multiple of Hkv (%d)", Hq, Hkv);
+    if (!good_scale(scale))
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_prefill_causal: scale must be finite and > 0");
     if ((long long)B * Hq * N * D > kMaxElems)
         return fail(ATTN_ERR_BAD_SHAPE, "attn_prefill_causal: tensor exceeds 2^31 elements");
     if (dtype != ATTN_BF16 && dtype != ATTN_FP32)
@@ -100,6 +105,8 @@ attn_status attn_decode_gqa(const void *q, const void *k_cache, const void *v_ca
         return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: B, Hq, Hkv, D must be >= 1");
     if (Hq % Hkv)
         return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: Hq (%d) not a multiple of Hkv (%d)", Hq, Hkv);
+    if (!good_scale(scale))
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: scale must be finite and > 0");
     if (kv_len < 1 || kv_len > kv_cap)
         return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: need 1 <= kv_len (%d) <= kv_cap (%d)", kv_len, kv_cap);
     if ((long long)B * Hkv * kv_cap * D > kMaxElems)
@@ -136,6 +143,8 @@ attn_status attn_decode_mla_absorbed(const void *q, const void *ckv, void *o, fl
         return fail(ATTN_ERR_NULL_POINTER, "attn_decode_mla_absorbed: NULL tensor pointer");
     if (B < 1 || Hq < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk)
         return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: bad B, Hq, Dqk or Dv");
+    if (!good_scale(scale))
+        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: scale must be finite and > 0");
     if (kv_len < 1 || kv_len > kv_cap)
         return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: need 1 <= kv_len (%d) <= kv_cap (%d)",
                     kv_len, kv_cap);

@@ -9,28 +9,32 @@
 //
 // Decomposition. Workgroup (split, head group, b) has 8 waves and covers 128
 // query heads, so each latent tile is read from HBM once and shared through
-// LDS by all heads. Each wave owns 16 heads as the columns of
-// v_mfma_f32_16x16x32_bf16:
-//   Sᵀ = C·Qᵀ      keys as MFMA rows, 576-deep contraction; the wave's Q
-//                  fragments stay in registers for the whole pass;
-//   online softmax in base 2 against a reference max m that moves only when
-//                  a score exceeds it by more than kLazy (so the weights
-//                  2^(s − m) stay ≤ 2^kLazy and the output is rescaled
-//                  rarely); the log-sum-exp comes out exact either way;
-//   Oᵀ += Vᵀ·Pᵀ    P stays in registers (the Sᵀ accumulator layout is the
-//                  B-operand layout) rounded to bf16; the Vᵀ operand is
-//                  fetched straight from the row-major latent tile with
-//                  ds_read_b64_tr_b16, which hands each lane one column of a
-//                  4-row × 16-column block.
+// LDS by all heads. Per 32-key tile the work is split two ways:
+//   scores    wave w owns heads 16w .. 16w + 15 as the columns of
+//             v_mfma_f32_16x16x32_bf16: Sᵀ = C·Qᵀ with keys as MFMA rows over
+//             the 576-deep row, Q fragments in registers for the whole pass;
+//             then the online softmax of those heads;
+//   values    wave w owns latent channels 64w .. 64w + 63 for all 128 heads:
+//             Oᵀ[its 64 channels][128 heads] += Vᵀ·Pᵀ.
+// The weights cross between the two through LDS: the Sᵀ accumulator of a
+// wave already has the lane layout of the Pᵀ B operand (its slots are the
+// same keys), so each wave writes its 16 heads' bf16 weights as 1 KiB, one
+// 16-byte run per lane, and every wave reads the 8 head blocks back with
+// ds_read_b128. The Vᵀ operand comes straight from the row-major latent tile
+// through ds_read_b64_tr_b16 (one column of a 4-row × 16-column block per
+// lane), but each wave now reads only its 64 channels: transposed reads run
+// at half the rate of ds_read_b128 and were the busiest LDS traffic when
+// every wave read all 512 channels for its own heads.
+// Softmax. Base 2, against a reference max m that moves only when a score
+// exceeds it by more than kLazy (so the weights 2^(s − m) stay ≤ 2^kLazy and
+// the output is rescaled rarely); the rescale factor of each head goes to
+// LDS with its weights. The log-sum-exp comes out exact either way.
 // Weight precision. A bf16 weight carries a relative error of up to 2^-8.
 // The output is normalised by the sum of the weights exactly as multiplied,
 // so it is a convex combination of the values and a single dominant key
 // comes out exact. For short caches (kv_len ≤ kLoMaxKeys) the few weights do
 // not average their rounding errors out, so a second product adds
 // Vᵀ·bf16(P − bf16(P)) and the weights enter with about 16 significant bits.
-// Overlap. For long caches half the waves run their P·V product one tile
-// behind their scores, so on each SIMD one wave's softmax (VALU, lane
-// exchanges) runs while the other wave keeps the matrix unit busy.
 // Latent tiles (32 rows × 1152 B) move HBM → LDS with global_load_lds_dwordx4
 // (no register staging, copy_to_lds16) into a ring of MNBUF buffers. The low
 // three bits of each row's 16-byte chunk index are XORed with
@@ -39,8 +43,7 @@
 // (8 rows × 32 B per 32-lane phase) over all 64 LDS banks. (The row / 16
 // term changes no bank; without it the compiler shares address registers
 // between the two 16-row halves and runs out of registers.)
-// Splits of the cache write fp32 (m, ℓ, λ, Õ) partials, transposed through
-// LDS so that every store is a contiguous 1 KiB, with streaming
+// Splits of the cache write fp32 (m, ℓ, λ, Õ) partials with streaming
 // (non-temporal) stores that do not stay dirty in L2; the shared merge kernel
 // combines them through their log-sum-exp. Rows at or past kv_len are never
 // read.
@@ -49,17 +52,15 @@
 
 #include <type_traits>
 
-#ifndef ATTN_MLA_NBUF
-#define ATTN_MLA_NBUF 4  // LDS tile ring depth (3 or 4)
-#endif
-
 namespace attn {
 namespace {
 
 constexpr int MD = 576, MV = 512, MBC = 32, MW = 8, MH = 16 * MW;
-constexpr int MNBUF = ATTN_MLA_NBUF;
+constexpr int MNBUF = 3;                     // LDS tile ring depth
 constexpr int MKS = MD / 32;                 // 18 k-steps of the score product
-constexpr int MDB = MV / 16;                 // 32 row blocks of Oᵀ
+constexpr int MHB = MH / 16;                 // 8 head blocks of 16
+constexpr int MDW = MV / MW;                 // 64 latent channels per wave in P·V
+constexpr int MDBW = MDW / 16;               // 4 row blocks of Oᵀ per wave
 constexpr int MROWB = MD * 2;                // bytes per latent row (1152)
 constexpr int MCH = MD / 8;                  // 72 sixteen-byte chunks per row
 constexpr int MTILEB = MBC * MROWB;          // 36,864 bytes per tile
@@ -70,13 +71,18 @@ constexpr int MTHREADS = 64 * MW;
 constexpr int kTargetGroups = 256;
 constexpr float kLazy = 8.f;      // reference-max slack, log2 units
 constexpr int kLoMaxKeys = 512;   // caches this short get the second P product
-constexpr int kOutStride = 260;   // floats per head row of the output transpose
-static_assert(MNBUF >= 3 && MNBUF <= 4, "tile ring depth");
-static_assert(MNBUF * MTILEB <= 160 * 1024, "LDS");
-static_assert(MW * 16 * kOutStride * 4 <= MNBUF * MTILEB, "output transpose fits the ring");
+static_assert(MNBUF * MTILEB + 2 * MHB * 1024 + MH * 8 <= 160 * 1024, "LDS");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// HBM → LDS like copy_to_lds16, addressed as a wave-uniform base plus a
+// per-lane 32-bit byte offset (the scalar-base form of the instruction), so
+// a full tile's copies need no per-lane address arithmetic.
+__device__ __forceinline__ void copy_to_lds16_sv(const void *base, uint32_t off, const void *lds_block) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_char *)lds_block;
+    asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
 
 // Physical 16-byte chunk holding logical chunk c of tile row r (an involution).
 __device__ __forceinline__ int swz(int r, int c) {
@@ -93,7 +99,7 @@ __device__ __forceinline__ void wait_tile(int ahead, bool hi_wave) {
     }
 }
 
-template <bool LO>
+template <bool LO, bool FULL>  // FULL: every workgroup has all 8 head blocks
 __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ ckv,
     uint16_t *__restrict__ o, float *__restrict__ lse, int Hq, int kv_len, int kv_cap,
@@ -101,18 +107,18 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     float *__restrict__ ws_part)
 {
     __shared__ __attribute__((aligned(1024))) char tile[MNBUF][MTILEB];
+    __shared__ __attribute__((aligned(16))) u32x4 p_hi[MHB][64];  // weights, B-operand order
+    __shared__ __attribute__((aligned(16))) u32x4 p_lo[LO ? MHB : 1][64];
+    __shared__ __attribute__((aligned(16))) float hinfo[16][MHB];  // per head: α, then λ
 
     const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hcol = lane & 15, quad = lane >> 4;
-    const int head0 = hg * MH + wave * 16;
-    const bool wave_active = head0 < Hq;
+    const int nhb = FULL ? MHB : min(MHB, (Hq - hg * MH) / 16);  // head blocks here (Hq % 16 == 0)
+    const bool own = wave < nhb;                     // this wave scores heads 16·wave ..
+    const int head = hg * MH + wave * 16 + hcol;     // its score head
     const bool hi_wave = wave < MLOADS % MW;
-    // half the waves run P·V one tile behind their scores (long caches only:
-    // the second weight product of short caches leaves no registers for it)
-    const bool lag = !LO && wave >= MW / 2;
-    const int head = head0 + hcol;
     const int key_begin = split * split_keys;
     const int key_end = min(kv_len, key_begin + split_keys);
     const uint16_t *cb = ckv + (size_t)b * kv_cap * MD;
@@ -128,35 +134,56 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         for (int ks = 0; ks < MKS; ++ks) asm volatile("" :: "v"(qf[ks]));
     }
 
-    // HBM → LDS: wave-wide copy i fills tile bytes [1024 i, 1024 i + 1024);
-    // lane l's 16 bytes land at chunk position 64 i + l = (row, physical chunk).
+    // HBM → LDS: wave-wide copy i = wave + MW·j fills tile bytes
+    // [1024 i, 1024 i + 1024); lane l's 16 bytes land at chunk position
+    // 64 i + l = (row r, physical chunk pc), and come from row r, logical
+    // chunk swz(r, pc). The byte offsets within a full tile are fixed.
+    uint32_t voff[MLOADS_HI];
+#pragma unroll
+    for (int j = 0; j < MLOADS_HI; ++j) {
+        const int pos = 64 * (wave + MW * j) + lane;
+        const int r = min(pos / MCH, MBC - 1), pc = pos % MCH;
+        voff[j] = (uint32_t)(r * MROWB + 16 * swz(r, pc));
+    }
     // Rows past the split's end repeat its last row (their scores are masked).
-    auto load_tile = [&](int t0, int buf) {
-        for (int i = wave; i < MLOADS; i += MW) {
-            const int pos = 64 * i + lane;
-            const int r = pos / MCH, pc = pos % MCH;
-            const int key = min(t0 + r, key_end - 1);
-            copy_to_lds16(cb + (size_t)key * MD + 8 * swz(r, pc), &tile[buf][1024 * i]);
+    auto load_tile = [&](int t0, int buf) __attribute__((always_inline)) {
+        if (t0 + MBC <= key_end) {
+            const uint16_t *base = cb + (size_t)t0 * MD;
+#pragma unroll
+            for (int j = 0; j < MLOADS_HI; ++j)
+                if (j < MLOADS_LO || hi_wave)
+                    copy_to_lds16_sv(base, voff[j], &tile[buf][1024 * (wave + MW * j)]);
+        } else {
+            for (int i = wave; i < MLOADS; i += MW) {
+                const int pos = 64 * i + lane;
+                const int r = pos / MCH, pc = pos % MCH;
+                const int key = min(t0 + r, key_end - 1);
+                copy_to_lds16(cb + (size_t)key * MD + 8 * swz(r, pc), &tile[buf][1024 * i]);
+            }
         }
     };
 
-    f32x4 oacc[MDB];
+    // Oᵀ[d = 64·wave + 16·db + 4·quad + i][head = 16·hb + hcol of the group]
+    f32x4 oacc[MDBW][MHB];
 #pragma unroll
-    for (int db = 0; db < MDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // per head (the 4 lanes of a head agree): reference max, fp32 weight sum
-    // (for the LSE) and sum of the weights as multiplied (for O); the sums
-    // are per lane here and added across the head's lanes at the end
+    for (int db = 0; db < MDBW; ++db)
+#pragma unroll
+        for (int hb = 0; hb < MHB; ++hb) oacc[db][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // per score head (the 4 lanes of a head agree): reference max, fp32
+    // weight sum (for the LSE) and sum of the weights as multiplied (for O);
+    // the sums are per lane and added across the head's lanes at the end
     float m_ref = -INFINITY, l_e = 0.f, l_o = 0.f;
-    bf16x8 pf_hi, pf_lo;  // weights of the tile whose P·V is pending
 
     // transposed value reads: lane 16·g + 4·e + c addresses row 4·g + e (and
     // 16 + 4·g + e), columns 4·c .. 4·c + 3 of a 16-column block
     const int ve = (lane >> 2) & 3, vc = lane & 3;
     const int vr1 = 4 * quad + ve, vr2 = 16 + 4 * quad + ve;
 
-    // ---- scores of one tile, online softmax, weights into pf_hi / pf_lo
-    auto scores = [&](const char *tb, int t0) __attribute__((always_inline)) {
-        float sc[8];
+    // ---- scores of this wave's 16 heads, online softmax, weights to LDS.
+    // PARTIAL: the tile runs past the split's end (its last keys are masked).
+    auto scores = [&](const char *tb, int t0, auto partial_tag) __attribute__((always_inline)) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
+        float sc[8];  // raw scores q·c (the scale is applied in the exponent)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int r = 16 * kb + hcol;
@@ -169,8 +196,8 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int key = t0 + 16 * kb + 4 * quad + i;
-                sc[4 * kb + i] = key < key_end ? acc[i] * scale_log2 : -INFINITY;
+                sc[4 * kb + i] = acc[i];
+                if (PARTIAL && t0 + 16 * kb + 4 * quad + i >= key_end) sc[4 * kb + i] = -INFINITY;
             }
         }
         float mx = sc[0];
@@ -178,19 +205,20 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));  // finite: each tile has a key < key_end
+        mx *= scale_log2;                  // scale > 0: the max commutes with it
+        float alpha = 1.f;
         if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) {
             const float m_new = mx > m_ref + kLazy ? mx : m_ref;
-            const float alpha = exp2_fast(m_ref - m_new);  // first tile: 2^-inf = 0
+            alpha = exp2_fast(m_ref - m_new);  // first tile: 2^-inf = 0
             l_e *= alpha;
             l_o *= alpha;
-#pragma unroll
-            for (int db = 0; db < MDB; ++db) oacc[db] *= alpha;
             m_ref = m_new;
         }
         u32x4 phi, plo;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float p0 = exp2_fast(sc[2 * u] - m_ref), p1 = exp2_fast(sc[2 * u + 1] - m_ref);
+            const float p0 = exp2_fast(fmaf(sc[2 * u], scale_log2, -m_ref));
+            const float p1 = exp2_fast(fmaf(sc[2 * u + 1], scale_log2, -m_ref));
             l_e += p0 + p1;
             const uint32_t h = pack_bf16x2(p0, p1);
             phi[u] = h;
@@ -202,110 +230,115 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
                 l_o = sum_bf16x2(w, l_o);
             }
         }
-        pf_hi = as<bf16x8>(phi);
-        if constexpr (LO) pf_lo = as<bf16x8>(plo);
+        // B operand of head block `wave`: slots 0..3 ↔ keys 4·quad + e,
+        // slots 4..7 ↔ keys 16 + 4·quad + e (the Sᵀ rows this lane holds)
+        p_hi[wave][lane] = phi;
+        if constexpr (LO) p_lo[wave][lane] = plo;
+        if (quad == 0) hinfo[hcol][wave] = alpha;
     };
 
-    // ---- Oᵀ += Vᵀ Pᵀ for the tile in tb; A slots 0..3 ↔ keys 4·quad + e,
-    // slots 4..7 ↔ keys 16 + 4·quad + e
-    auto pv = [&](const char *tb) __attribute__((always_inline)) {
+    // ---- Oᵀ += Vᵀ Pᵀ over this wave's 64 channels and every head block
+    auto values = [&](const char *tb) __attribute__((always_inline)) {
+        // rescale first: the new weights are relative to the moved references
+        {
+            const f32x4 a0 = *(const f32x4 *)&hinfo[hcol][0], a1 = *(const f32x4 *)&hinfo[hcol][4];
+            const float al[MHB] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            bool moved = false;
+#pragma unroll
+            for (int hb = 0; hb < MHB; ++hb) moved |= hb < nhb && al[hb] != 1.f;
+            if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+                for (int hb = 0; hb < MHB; ++hb)
+#pragma unroll
+                    for (int db = 0; db < MDBW; ++db) oacc[db][hb] *= al[hb];
+            }
+        }
+        u32x4 va[MDBW];
         const char *row1 = tb + vr1 * MROWB + 8 * (vc & 1);
         const char *row2 = tb + vr2 * MROWB + 8 * (vc & 1);
 #pragma unroll
-        for (int db = 0; db < MDB; ++db) {
-            const int c = 2 * db + (vc >> 1);
+        for (int db = 0; db < MDBW; ++db) {
+            const int c = 2 * (MDBW * wave + db) + (vc >> 1);
             const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_i16x4 *)(row1 + 16 * swz(vr1, c)));
             const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_i16x4 *)(row2 + 16 * swz(vr2, c)));
             const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
-            const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-            oacc[db] = mfma16x16x32(as<bf16x8>(a), pf_hi, oacc[db]);
-            if constexpr (LO) oacc[db] = mfma16x16x32(as<bf16x8>(a), pf_lo, oacc[db]);
+            va[db] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        }
+#pragma unroll
+        for (int hb = 0; hb < MHB; ++hb) {
+            if (hb >= nhb) break;
+            const bf16x8 bh = as<bf16x8>(p_hi[hb][lane]);
+#pragma unroll
+            for (int db = 0; db < MDBW; ++db) oacc[db][hb] = mfma16x16x32(as<bf16x8>(va[db]), bh, oacc[db][hb]);
+            if constexpr (LO) {
+                const bf16x8 bl = as<bf16x8>(p_lo[hb][lane]);
+#pragma unroll
+                for (int db = 0; db < MDBW; ++db) oacc[db][hb] = mfma16x16x32(as<bf16x8>(va[db]), bl, oacc[db][hb]);
+            }
         }
     };
 
     // Ring: tile t lives in buffer t % MNBUF. Step t waits for tile t, then
-    // refills the buffer of tile t − 2 (read last by the lagging waves at step
-    // t − 1) with tile t + MNBUF − 2.
+    // refills the buffer of tile t − 1 with tile t + MNBUF − 1. The second
+    // barrier of a step publishes the weights; the first barrier of the next
+    // step keeps them until every wave has used them.
     const int n_t = (key_end - key_begin + MBC - 1) / MBC;
 #pragma unroll
-    for (int p = 0; p < MNBUF - 2; ++p)
+    for (int p = 0; p < MNBUF - 1; ++p)
         if (p < n_t) load_tile(key_begin + p * MBC, p);
-
-    // The two halves of the workgroup run separate copies of the loop (same
-    // waits and barriers), so the weights a lagging wave carries from one
-    // step to the next occupy no registers in the other half.
-    auto run = [&](auto lag_tag) __attribute__((always_inline)) {
-        constexpr bool LAG = decltype(lag_tag)::value;
-        for (int t = 0; t < n_t; ++t) {
-            const int t0 = key_begin + t * MBC;
-            wait_tile(min(MNBUF - 3, n_t - 1 - t), hi_wave);
-            __syncthreads();  // tile t visible; tile t − 2 no longer read
-            if (t + MNBUF - 2 < n_t) load_tile(t0 + (MNBUF - 2) * MBC, (t + MNBUF - 2) % MNBUF);
-            if (!wave_active) continue;
-            const char *tb = tile[t % MNBUF];
-            if constexpr (LAG) {
-                if (t > 0) pv(tile[(t + MNBUF - 1) % MNBUF]);
-                scores(tb, t0);
-            } else {
-                scores(tb, t0);
-                pv(tb);
-            }
+    for (int t = 0; t < n_t; ++t) {
+        const int t0 = key_begin + t * MBC;
+        wait_tile(min(MNBUF - 2, n_t - 1 - t), hi_wave);
+        __syncthreads();  // tile t visible; tile t − 1 and the last weights no longer read
+        if (t + MNBUF - 1 < n_t) load_tile(t0 + (MNBUF - 1) * MBC, (t + MNBUF - 1) % MNBUF);
+        const char *tb = tile[t % MNBUF];
+        if (own) {
+            if (t0 + MBC > key_end) scores(tb, t0, std::true_type{});
+            else scores(tb, t0, std::false_type{});
         }
-        if constexpr (LAG) {
-            if (wave_active && n_t > 0) pv(tile[(n_t - 1) % MNBUF]);
-        }
-    };
-    if constexpr (LO) run(std::false_type{});
-    else if (lag) run(std::true_type{});
-    else run(std::false_type{});
+        __syncthreads();  // weights and rescale factors of every head visible
+        values(tb);
+    }
 
     // ---- epilogue: per-head sums over the head's four lanes
     l_e += shfl_xor(l_e, 16);
     l_e += shfl_xor(l_e, 32);
     l_o += shfl_xor(l_o, 16);
     l_o += shfl_xor(l_o, 32);
-    // lane holds Oᵀ[d = 16·db + 4·quad + i][head]
     if (splits == 1) {
-        if (!wave_active || head >= Hq) return;
-        const float inv = 1.f / l_o;
-        uint16_t *orow = o + ((size_t)b * Hq + head) * MV;
-#pragma unroll
-        for (int db = 0; db < MDB; ++db) {
-            const u32x2 w = {pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv),
-                             pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv)};
-            *(u32x2 *)(orow + 16 * db + 4 * quad) = w;
+        // every wave needs λ of every head: pass it through LDS
+        __syncthreads();
+        if (own && quad == 0) {
+            hinfo[hcol][wave] = l_o;
+            lse[(size_t)b * Hq + head] = (m_ref + log2_fast(l_e)) * kLn2;
         }
-        if (quad == 0) lse[(size_t)b * Hq + head] = (m_ref + log2_fast(l_e)) * kLn2;
-        return;
-    }
-    // Partials: each wave transposes its 16 heads × 512 values through LDS
-    // (half the values at a time) so that every global store writes 1 KiB of
-    // one head's row.
-    __syncthreads();  // every wave is done with the ring
-    if (!wave_active) return;
-    if (quad == 0 && head < Hq)
-        *(float4 *)(ws_ml + 4 * (((size_t)b * Hq + head) * splits + split)) =
-            make_float4(m_ref, l_e, l_o, 0.f);
-    float *st = (float *)&tile[0][0] + wave * 16 * kOutStride;
+        __syncthreads();
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+        for (int hb = 0; hb < MHB; ++hb) {
+            if (hb >= nhb) break;
+            const float inv = 1.f / hinfo[hcol][hb];
+            uint16_t *orow = o + ((size_t)b * Hq + hg * MH + 16 * hb + hcol) * MV + MDW * wave + 4 * quad;
 #pragma unroll
-        for (int j = 0; j < MDB / 2; ++j) {
-            const int db = (MDB / 2) * half + j;
-            *(f32x4 *)(st + hcol * kOutStride + 16 * j + 4 * quad) = oacc[db];
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const f32x4 v = *(const f32x4 *)(st + r * kOutStride + 4 * lane);
-            if (head0 + r < Hq) {
-                const size_t slot = ((size_t)b * Hq + head0 + r) * splits + split;
-                __builtin_nontemporal_store(v, (f32x4 *)(ws_part + slot * MV + (MV / 2) * half + 4 * lane));
+            for (int db = 0; db < MDBW; ++db) {
+                const u32x2 w = {pack_bf16x2(oacc[db][hb][0] * inv, oacc[db][hb][1] * inv),
+                                 pack_bf16x2(oacc[db][hb][2] * inv, oacc[db][hb][3] * inv)};
+                *(u32x2 *)(orow + 16 * db) = w;
             }
         }
-        wave_lds_sync();
+        return;
+    }
+    if (own && quad == 0)
+        *(float4 *)(ws_ml + 4 * (((size_t)b * Hq + head) * splits + split)) =
+            make_float4(m_ref, l_e, l_o, 0.f);
+#pragma unroll
+    for (int hb = 0; hb < MHB; ++hb) {
+        if (hb >= nhb) break;
+        const size_t slot = ((size_t)b * Hq + hg * MH + 16 * hb + hcol) * splits + split;
+        float *prow = ws_part + slot * MV + MDW * wave + 4 * quad;
+#pragma unroll
+        for (int db = 0; db < MDBW; ++db) __builtin_nontemporal_store(oacc[db][hb], (f32x4 *)(prow + 16 * db));
     }
 }
 
@@ -339,7 +372,9 @@ hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, v
     float *ws_ml = (float *)(w + p.ws_ml);
     float *ws_part = (float *)(w + p.ws_part);
     const dim3 grid(p.splits, (Hq + MH - 1) / MH, B);
-    auto kern = kv_len <= kLoMaxKeys ? decode_mla_kernel<true> : decode_mla_kernel<false>;
+    const bool full = Hq % MH == 0;
+    auto kern = kv_len <= kLoMaxKeys ? (full ? decode_mla_kernel<true, true> : decode_mla_kernel<true, false>)
+                                     : (full ? decode_mla_kernel<false, true> : decode_mla_kernel<false, false>);
     kern<<<grid, dim3(MTHREADS), 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)ckv, (uint16_t *)o, lse, Hq, kv_len, kv_cap,
         scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part);
