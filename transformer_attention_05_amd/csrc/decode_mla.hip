@@ -12,8 +12,12 @@
 // LDS by all heads. Per 32-key tile the work is split two ways:
 //   scores    wave w owns heads 16w .. 16w + 15 as the columns of
 //             v_mfma_f32_16x16x32_bf16: Sᵀ = C·Qᵀ with keys as MFMA rows over
-//             the 576-deep row, Q fragments in registers for the whole pass;
-//             then the online softmax of those heads;
+//             the 576-deep row (the two 16-key halves as independent chains,
+//             each step's tile operands requested one step ahead); the Q
+//             fragments stay resident for the whole pass, 14 of the 18
+//             k-steps in registers and the last 4 in LDS (the registers are
+//             taken by Q and by the output); then the online softmax of those
+//             heads;
 //   values    wave w owns latent channels 64w .. 64w + 63 for all 128 heads:
 //             Oᵀ[its 64 channels][128 heads] += Vᵀ·Pᵀ.
 // The weights cross between the two through LDS: the Sᵀ accumulator of a
@@ -58,6 +62,8 @@ namespace {
 constexpr int MD = 576, MV = 512, MBC = 32, MW = 8, MH = 16 * MW;
 constexpr int MNBUF = 3;                     // LDS tile ring depth
 constexpr int MKS = MD / 32;                 // 18 k-steps of the score product
+constexpr int MKQ = 4;                       // k-steps whose Q fragments live in LDS
+constexpr int MKR = MKS - MKQ;               // k-steps whose Q fragments live in registers
 constexpr int MHB = MH / 16;                 // 8 head blocks of 16
 constexpr int MDW = MV / MW;                 // 64 latent channels per wave in P·V
 constexpr int MDBW = MDW / 16;               // 4 row blocks of Oᵀ per wave
@@ -71,7 +77,8 @@ constexpr int MTHREADS = 64 * MW;
 constexpr int kTargetGroups = 256;
 constexpr float kLazy = 8.f;      // reference-max slack, log2 units
 constexpr int kLoMaxKeys = 512;   // caches this short get the second P product
-static_assert(MNBUF * MTILEB + 2 * MHB * 1024 + MH * 8 <= 160 * 1024, "LDS");
+// LDS: tile ring, weights (hi and lo), per-head factors, LDS-held Q fragments
+static_assert(MNBUF * MTILEB + 2 * MHB * 1024 + MH * 4 + MKQ * MW * 1024 <= 160 * 1024, "LDS");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -107,9 +114,14 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     float *__restrict__ ws_part)
 {
     __shared__ __attribute__((aligned(1024))) char tile[MNBUF][MTILEB];
-    __shared__ __attribute__((aligned(16))) u32x4 p_hi[MHB][64];  // weights, B-operand order
+    // weights in B-operand order and per-head α (then λ)
+    constexpr int NPB = 1;
+    __shared__ __attribute__((aligned(16))) u32x4 p_hi[NPB][MHB][64];
     __shared__ __attribute__((aligned(16))) u32x4 p_lo[LO ? MHB : 1][64];
-    __shared__ __attribute__((aligned(16))) float hinfo[16][MHB];  // per head: α, then λ
+    __shared__ __attribute__((aligned(16))) float hinfo[NPB][16][MHB];
+    // Q fragments of the last MKQ k-steps, each wave's own (registers are
+    // all taken by the other Q fragments and the output)
+    __shared__ __attribute__((aligned(16))) u32x4 q_lds[MKQ][MW][64];
 
     const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -123,28 +135,34 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const int key_end = min(kv_len, key_begin + split_keys);
     const uint16_t *cb = ckv + (size_t)b * kv_cap * MD;
 
-    bf16x8 qf[MKS];
+    bf16x8 qf[MKR];
     {
         const uint16_t *qr = q + ((size_t)b * Hq + min(head, Hq - 1)) * MD + 8 * quad;
 #pragma unroll
-        for (int ks = 0; ks < MKS; ++ks) qf[ks] = as<bf16x8>(*(const u32x4 *)(qr + 32 * ks));
+        for (int ks = 0; ks < MKR; ++ks) qf[ks] = as<bf16x8>(*(const u32x4 *)(qr + 32 * ks));
+#pragma unroll
+        for (int j = 0; j < MKQ; ++j) q_lds[j][wave][lane] = *(const u32x4 *)(qr + 32 * (MKR + j));
         // Make the compiler wait for these loads here, before any tile copy is
         // in flight: waited for inside the loop, they would drain the ring.
 #pragma unroll
-        for (int ks = 0; ks < MKS; ++ks) asm volatile("" :: "v"(qf[ks]));
+        for (int ks = 0; ks < MKR; ++ks) asm volatile("" :: "v"(qf[ks]));
+        wave_lds_sync();
     }
 
     // HBM → LDS: wave-wide copy i = wave + MW·j fills tile bytes
     // [1024 i, 1024 i + 1024); lane l's 16 bytes land at chunk position
     // 64 i + l = (row r, physical chunk pc), and come from row r, logical
     // chunk swz(r, pc). The byte offsets within a full tile are fixed.
-    uint32_t voff[MLOADS_HI];
+    // (each offset is below 2^16: two per register)
+    uint32_t voffp[(MLOADS_HI + 1) / 2] = {};
 #pragma unroll
     for (int j = 0; j < MLOADS_HI; ++j) {
         const int pos = 64 * (wave + MW * j) + lane;
         const int r = min(pos / MCH, MBC - 1), pc = pos % MCH;
-        voff[j] = (uint32_t)(r * MROWB + 16 * swz(r, pc));
+        voffp[j / 2] |= (uint32_t)(r * MROWB + 16 * swz(r, pc)) << (16 * (j & 1));
     }
+    static_assert(MTILEB <= 65536, "tile offsets fit 16 bits");
+    auto voff = [&](int j) __attribute__((always_inline)) { return (voffp[j / 2] >> (16 * (j & 1))) & 0xffffu; };
     // Rows past the split's end repeat its last row (their scores are masked).
     auto load_tile = [&](int t0, int buf) __attribute__((always_inline)) {
         if (t0 + MBC <= key_end) {
@@ -152,7 +170,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
 #pragma unroll
             for (int j = 0; j < MLOADS_HI; ++j)
                 if (j < MLOADS_LO || hi_wave)
-                    copy_to_lds16_sv(base, voff[j], &tile[buf][1024 * (wave + MW * j)]);
+                    copy_to_lds16_sv(base, voff(j), &tile[buf][1024 * (wave + MW * j)]);
         } else {
             for (int i = wave; i < MLOADS; i += MW) {
                 const int pos = 64 * i + lane;
@@ -181,23 +199,40 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
 
     // ---- scores of this wave's 16 heads, online softmax, weights to LDS.
     // PARTIAL: the tile runs past the split's end (its last keys are masked).
-    auto scores = [&](const char *tb, int t0, auto partial_tag) __attribute__((always_inline)) {
+    auto scores = [&](const char *tb, int t0, int pb, auto partial_tag) __attribute__((always_inline)) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
         float sc[8];  // raw scores q·c (the scale is applied in the exponent)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int r = 16 * kb + hcol;
-            const char *rowp = tb + r * MROWB;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        {
+            // the two 16-key halves of the tile as two independent MFMA chains,
+            // the operands of step ks + 1 requested before the MFMAs of step ks
+            const char *row0 = tb + hcol * MROWB, *row1 = row0 + 16 * MROWB;
+            auto ld = [&](const char *rowp, int r, int ks) __attribute__((always_inline)) {
+                return *(const u32x4 *)(rowp + 16 * swz(r, 4 * ks + quad));
+            };
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+            u32x4 a0 = ld(row0, hcol, 0), a1 = ld(row1, 16 + hcol, 0);
 #pragma unroll
             for (int ks = 0; ks < MKS; ++ks) {
-                const u32x4 a = *(const u32x4 *)(rowp + 16 * swz(r, 4 * ks + quad));
-                acc = mfma16x16x32(as<bf16x8>(a), qf[ks], acc);
+                u32x4 n0 = a0, n1 = a1, qn;
+                if (ks + 1 < MKS) {
+                    n0 = ld(row0, hcol, ks + 1);
+                    n1 = ld(row1, 16 + hcol, ks + 1);
+                }
+                if (ks >= MKR) qn = q_lds[ks - MKR][wave][lane];
+                const bf16x8 qk = ks < MKR ? qf[ks < MKR ? ks : 0] : as<bf16x8>(qn);
+                acc0 = mfma16x16x32(as<bf16x8>(a0), qk, acc0);
+                acc1 = mfma16x16x32(as<bf16x8>(a1), qk, acc1);
+                a0 = n0;
+                a1 = n1;
+                // keep the compiler from hoisting later reads (hoisting spills)
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sc[4 * kb + i] = acc[i];
-                if (PARTIAL && t0 + 16 * kb + 4 * quad + i >= key_end) sc[4 * kb + i] = -INFINITY;
+                sc[i] = acc0[i];
+                sc[4 + i] = acc1[i];
+                if (PARTIAL && t0 + 4 * quad + i >= key_end) sc[i] = -INFINITY;
+                if (PARTIAL && t0 + 16 + 4 * quad + i >= key_end) sc[4 + i] = -INFINITY;
             }
         }
         float mx = sc[0];
@@ -232,16 +267,16 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         }
         // B operand of head block `wave`: slots 0..3 ↔ keys 4·quad + e,
         // slots 4..7 ↔ keys 16 + 4·quad + e (the Sᵀ rows this lane holds)
-        p_hi[wave][lane] = phi;
+        p_hi[pb][wave][lane] = phi;
         if constexpr (LO) p_lo[wave][lane] = plo;
-        if (quad == 0) hinfo[hcol][wave] = alpha;
+        if (quad == 0) hinfo[pb][hcol][wave] = alpha;
     };
 
     // ---- Oᵀ += Vᵀ Pᵀ over this wave's 64 channels and every head block
-    auto values = [&](const char *tb) __attribute__((always_inline)) {
+    auto values = [&](const char *tb, int pb) __attribute__((always_inline)) {
         // rescale first: the new weights are relative to the moved references
         {
-            const f32x4 a0 = *(const f32x4 *)&hinfo[hcol][0], a1 = *(const f32x4 *)&hinfo[hcol][4];
+            const f32x4 a0 = *(const f32x4 *)&hinfo[pb][hcol][0], a1 = *(const f32x4 *)&hinfo[pb][hcol][4];
             const float al[MHB] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             bool moved = false;
 #pragma unroll
@@ -268,23 +303,32 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         }
 #pragma unroll
         for (int hb = 0; hb < MHB; ++hb) {
-            if (hb >= nhb) break;
-            const bf16x8 bh = as<bf16x8>(p_hi[hb][lane]);
+            if (hb < nhb) {
+                const bf16x8 bh = as<bf16x8>(p_hi[pb][hb][lane]);
 #pragma unroll
-            for (int db = 0; db < MDBW; ++db) oacc[db][hb] = mfma16x16x32(as<bf16x8>(va[db]), bh, oacc[db][hb]);
-            if constexpr (LO) {
-                const bf16x8 bl = as<bf16x8>(p_lo[hb][lane]);
+                for (int db = 0; db < MDBW; ++db) oacc[db][hb] = mfma16x16x32(as<bf16x8>(va[db]), bh, oacc[db][hb]);
+                if constexpr (LO) {
+                    const bf16x8 bl = as<bf16x8>(p_lo[hb][lane]);
 #pragma unroll
-                for (int db = 0; db < MDBW; ++db) oacc[db][hb] = mfma16x16x32(as<bf16x8>(va[db]), bl, oacc[db][hb]);
+                    for (int db = 0; db < MDBW; ++db) oacc[db][hb] = mfma16x16x32(as<bf16x8>(va[db]), bl, oacc[db][hb]);
+                }
             }
         }
     };
 
-    // Ring: tile t lives in buffer t % MNBUF. Step t waits for tile t, then
-    // refills the buffer of tile t − 1 with tile t + MNBUF − 1. The second
-    // barrier of a step publishes the weights; the first barrier of the next
-    // step keeps them until every wave has used them.
     const int n_t = (key_end - key_begin + MBC - 1) / MBC;
+    auto do_scores = [&](const char *tb, int t0, int pb) __attribute__((always_inline)) {
+        if (own) {
+            if (t0 + MBC > key_end) scores(tb, t0, pb, std::true_type{});
+            else scores(tb, t0, pb, std::false_type{});
+        }
+    };
+    // Tile t lives in buffer t % MNBUF. Step t waits for tile t, then refills
+    // the buffer of tile t − 1 with tile t + MNBUF − 1. The second barrier of
+    // a step publishes the weights; the first barrier of the next step keeps
+    // them until every wave has used them. (A one-barrier variant with
+    // double-buffered weights measured slower: a wave's scores then compete
+    // for LDS with the other waves' P·V.)
 #pragma unroll
     for (int p = 0; p < MNBUF - 1; ++p)
         if (p < n_t) load_tile(key_begin + p * MBC, p);
@@ -294,12 +338,9 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         __syncthreads();  // tile t visible; tile t − 1 and the last weights no longer read
         if (t + MNBUF - 1 < n_t) load_tile(t0 + (MNBUF - 1) * MBC, (t + MNBUF - 1) % MNBUF);
         const char *tb = tile[t % MNBUF];
-        if (own) {
-            if (t0 + MBC > key_end) scores(tb, t0, std::true_type{});
-            else scores(tb, t0, std::false_type{});
-        }
+        do_scores(tb, t0, 0);
         __syncthreads();  // weights and rescale factors of every head visible
-        values(tb);
+        values(tb, 0);
     }
 
     // ---- epilogue: per-head sums over the head's four lanes
@@ -311,14 +352,14 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         // every wave needs λ of every head: pass it through LDS
         __syncthreads();
         if (own && quad == 0) {
-            hinfo[hcol][wave] = l_o;
+            hinfo[0][hcol][wave] = l_o;
             lse[(size_t)b * Hq + head] = (m_ref + log2_fast(l_e)) * kLn2;
         }
         __syncthreads();
 #pragma unroll
         for (int hb = 0; hb < MHB; ++hb) {
             if (hb >= nhb) break;
-            const float inv = 1.f / hinfo[hcol][hb];
+            const float inv = 1.f / hinfo[0][hcol][hb];
             uint16_t *orow = o + ((size_t)b * Hq + hg * MH + 16 * hb + hcol) * MV + MDW * wave + 4 * quad;
 #pragma unroll
             for (int db = 0; db < MDBW; ++db) {
