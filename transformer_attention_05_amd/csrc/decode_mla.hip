@@ -199,7 +199,10 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
 
     // ---- scores of this wave's 16 heads, online softmax, weights to LDS.
     // PARTIAL: the tile runs past the split's end (its last keys are masked).
-    auto scores = [&](const char *tb, int t0, int pb, auto partial_tag) __attribute__((always_inline)) {
+    // cbase (if set): the next full tile's copies into buffer cbuf are issued
+    // between the score steps instead of in one burst
+    auto scores = [&](const char *tb, int t0, int pb, const uint16_t *cbase, int cbuf,
+                      auto partial_tag) __attribute__((always_inline)) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
         float sc[8];  // raw scores q·c (the scale is applied in the exponent)
         {
@@ -213,6 +216,12 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
             u32x4 a0 = ld(row0, hcol, 0), a1 = ld(row1, 16 + hcol, 0);
 #pragma unroll
             for (int ks = 0; ks < MKS; ++ks) {
+                constexpr int kEvery = (MKS + MLOADS_HI - 1) / MLOADS_HI;  // score steps per copy
+                if (cbase && ks % kEvery == 0) {
+                    const int j = ks / kEvery;
+                    if (j < MLOADS_LO || hi_wave)
+                        copy_to_lds16_sv(cbase, voff(j), &tile[cbuf][1024 * (wave + MW * j)]);
+                }
                 u32x4 n0 = a0, n1 = a1, qn;
                 if (ks + 1 < MKS) {
                     n0 = ld(row0, hcol, ks + 1);
@@ -317,10 +326,10 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     };
 
     const int n_t = (key_end - key_begin + MBC - 1) / MBC;
-    auto do_scores = [&](const char *tb, int t0, int pb) __attribute__((always_inline)) {
+    auto do_scores = [&](const char *tb, int t0, int pb, const uint16_t *cbase, int cbuf) __attribute__((always_inline)) {
         if (own) {
-            if (t0 + MBC > key_end) scores(tb, t0, pb, std::true_type{});
-            else scores(tb, t0, pb, std::false_type{});
+            if (t0 + MBC > key_end) scores(tb, t0, pb, cbase, cbuf, std::true_type{});
+            else scores(tb, t0, pb, cbase, cbuf, std::false_type{});
         }
     };
     // Tile t lives in buffer t % MNBUF. Step t waits for tile t, then refills
@@ -336,9 +345,14 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         const int t0 = key_begin + t * MBC;
         wait_tile(min(MNBUF - 2, n_t - 1 - t), hi_wave);
         __syncthreads();  // tile t visible; tile t − 1 and the last weights no longer read
-        if (t + MNBUF - 1 < n_t) load_tile(t0 + (MNBUF - 1) * MBC, (t + MNBUF - 1) % MNBUF);
+        // refill: a full next tile is copied from inside the score steps of
+        // the waves that score; a partial one (clamped rows), or the copies of
+        // a wave without score heads, in one go
+        const int tn = t0 + (MNBUF - 1) * MBC, bn = (t + MNBUF - 1) % MNBUF;
+        const bool refill = t + MNBUF - 1 < n_t, spread = refill && own && tn + MBC <= key_end;
+        if (refill && !spread) load_tile(tn, bn);
         const char *tb = tile[t % MNBUF];
-        do_scores(tb, t0, 0);
+        do_scores(tb, t0, 0, spread ? cb + (size_t)tn * MD : nullptr, bn);
         __syncthreads();  // weights and rescale factors of every head visible
         values(tb, 0);
     }
