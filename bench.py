@@ -161,11 +161,16 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
         work = flops / 1e12
         unit = "TFLOP/s"
         if w.dtype == "bf16":
-            peak, bound, kernel = MFMA_BF16_PEAK_TFLOPS, "mfma", "prefill_bf16_kernel"
+            peak, bound = MFMA_BF16_PEAK_TFLOPS, "mfma"
+            kernel = "prefill_d128_kernel" if w.D == 128 else "prefill_bf16_kernel"
         else:
             peak, bound, kernel = FP32_VALU_PEAK_TFLOPS, "alu", "prefill_f32_kernel"
-        nsteps = max(5, min(steps, int(2e12 // max(flops, 1)) + 5))
-        steps, warmup = nsteps, min(warmup, 5)
+        # about 0.1 s of timed work after about 20 ms of warm-up (the clocks
+        # ramp during the first milliseconds of a burst)
+        nsteps = max(5, min(steps, int(1e14 // max(flops, 1))))
+        if nsteps >= 20:
+            nsteps -= nsteps % 20
+        steps, warmup = nsteps, max(min(warmup, 5), min(200, int(2e13 // max(flops, 1))))
     per_graph = 20 if steps % 20 == 0 else 1
     wall, gpu, eager = _time_calls(torch, calls, steps, warmup, per_graph)
     per = gpu / steps

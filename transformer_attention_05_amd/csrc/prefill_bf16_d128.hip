@@ -26,14 +26,19 @@
 //               ("05 · Tích vô hướng…", §6), skipped when no lane's max moved.
 //               (ATTN_PF_LAZY=1 builds a variant whose reference max moves
 //               only when the running max outgrows it by more than 8, with O
-//               normalised by the sum of the bf16 weights it was built from;
-//               it measured no faster here.)
+//               normalised by the sum of the bf16 weights it was built from:
+//               equal at 4K keys, ≈2.5 % slower at 32K.)
 //   Oᵀ += Vᵀ·Pᵀ P rounded to bf16 in registers (the Sᵀ accumulator layout is
 //               the B-operand layout); the Vᵀ operand comes straight from the
 //               row-major V tile through ds_read_b64_tr_b16.
 //   epilogue    O = Oᵀ/ℓ rounded once to bf16; LSE = ln2·(m + log2 ℓ).
 //
 // S and P never leave registers ("05 · Tích vô hướng…", §5–§6).
+// Loop split: the key tiles before a workgroup's first row, visible to every
+// wave, run in a loop of their own with only the unmasked step; the few
+// tiles around the diagonal follow with a per-wave choice of skip, masked
+// or unmasked step. (With all three in one loop the compiler kept the output
+// in two register sets and copied 64 registers per tile.)
 // Work order: the query tiles of one (batch, K/V head) group run on one XCD
 // (workgroups are dealt to the 8 XCDs round-robin by id), heaviest first, so
 // the concurrently running tiles of a group walk the same K/V through that
@@ -65,6 +70,10 @@ namespace {
 #ifndef ATTN_PF_SCHED
 #define ATTN_PF_SCHED 0      // keep each 16-key step's transposed reads together
 #endif
+#ifndef ATTN_PF_BULK
+#define ATTN_PF_BULK 1       // separate loop for the tiles wholly visible to every wave
+#endif
+
 
 constexpr int NW = ATTN_PF_WAVES, NBUF = ATTN_PF_NBUF;
 constexpr int D = 128, BR = 32 * NW, BC = 64;
@@ -287,7 +296,22 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         }
     };
 
-    for (int j = 0; j < n_kt; ++j) {
+    // Bulk: the key tiles before the workgroup's first row are wholly visible
+    // to every wave. They get a loop of their own with a single unmasked step,
+    // so the output registers stay put (where masked, unmasked and skipped
+    // tiles meet in one loop, the compiler copies all 64 of them back and
+    // forth every tile).
+    const int n_bulk = ATTN_PF_BULK && q0 + BR <= N ? q0 / BC : 0;
+    for (int j = 0; j < n_bulk; ++j) {
+        const int cur = j % NBUF;
+        const int jn = j + NBUF - 1;  // tile to prefetch
+        if (jn < n_kt) load_tile(jn, jn % NBUF);
+        tile_step(kt[cur], vt[cur], j * BC, std::false_type{});
+        if (NBUF == 3 && jn < n_kt) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
+        __syncthreads();
+    }
+    // Tail: the tiles around the diagonal, classified per wave.
+    for (int j = n_bulk; j < n_kt; ++j) {
         const int cur = j % NBUF;
         const int jn = j + NBUF - 1;  // tile to prefetch
         if (jn < n_kt) load_tile(jn, jn % NBUF);
