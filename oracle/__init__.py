@@ -56,7 +56,13 @@ def _load():
                                                   dp, dp, dp, i]
             lib.oracle_decode_gqa.argtypes = [dp, dp, dp, i, i, i, i, i, i, d, dp, dp, dp, i]
             lib.oracle_decode_mla.argtypes = [dp, dp, i, i, i, i, i, i, d, dp, dp, i]
-            for f in (lib.oracle_prefill_causal, lib.oracle_decode_gqa, lib.oracle_decode_mla):
+            lib.oracle_prefill_chunked.argtypes = [dp, dp, dp, i, i, i, i, ip, i, i, d, ip, i,
+                                                   dp, dp, i]
+            lib.oracle_decode_gqa_ragged.argtypes = [dp, dp, dp, i, i, i, ip, i, i, d, dp, dp, i]
+            lib.oracle_decode_mla_ragged.argtypes = [dp, dp, i, i, ip, i, i, i, d, dp, dp, i]
+            for f in (lib.oracle_prefill_causal, lib.oracle_decode_gqa, lib.oracle_decode_mla,
+                      lib.oracle_prefill_chunked, lib.oracle_decode_gqa_ragged,
+                      lib.oracle_decode_mla_ragged):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -88,6 +94,17 @@ def widen(x: np.ndarray) -> np.ndarray:
 
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _iptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+
+
+def _lens(kv_lens, B) -> np.ndarray:
+    lens = np.ascontiguousarray(np.asarray(kv_lens).reshape(-1), dtype=np.int32)
+    if lens.shape[0] != B:
+        raise ValueError("kv_lens must hold one length per sequence")
+    return lens
 
 
 def prefill_causal(q, k, v, scale, rows=None, return_p=False, threads=None):
@@ -155,4 +172,70 @@ def decode_mla_absorbed(q, ckv, kv_len, dv, scale, threads=None):
         float(scale), _ptr(o), _ptr(lse), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_decode_mla rejected its arguments")
+    return o, lse
+
+
+def prefill_chunked(q, k_cache, v_cache, kv_lens, scale, rows=None, threads=None):
+    """A chunk of Nq new tokens against a cache (bottom-right causal mask).
+
+    q [B,Hq,Nq,D]; caches [B,Hkv,kv_cap,D]; kv_lens [B] with Nq <= kv_lens[b]
+    <= kv_cap: sequence b's keys are its first kv_lens[b] slots, the last Nq
+    of them the chunk's own. `rows` selects chunk rows (default: all).
+    Returns (o [B,Hq,R,D], lse [B,Hq,R]).
+    """
+    q = np.asarray(q)
+    B, Hq, Nq, D = q.shape
+    _, Hkv, kv_cap, _ = k_cache.shape
+    lens = _lens(kv_lens, B)
+    rows = np.arange(Nq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    R = rows.shape[0]
+    n = int(lens.max())   # slots past every sequence's length are never read
+    q64 = widen(q[:, :, rows, :])
+    k64, v64 = widen(k_cache[:, :, :n]), widen(v_cache[:, :, :n])
+    o = np.empty((B, Hq, R, D))
+    lse = np.empty((B, Hq, R))
+    rc = _load().oracle_prefill_chunked(
+        _ptr(q64), _ptr(k64), _ptr(v64), B, Hq, Hkv, Nq, _iptr(lens), n, D, float(scale),
+        _iptr(rows), R, _ptr(o), _ptr(lse), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_prefill_chunked rejected its arguments")
+    return o, lse
+
+
+def decode_gqa_ragged(q, k_cache, v_cache, kv_lens, scale, threads=None):
+    """Decode of a ragged batch: sequence b reads its first kv_lens[b] slots
+    (0 allowed: O = 0, LSE = −∞). Returns (o [B,Hq,D], lse [B,Hq])."""
+    q = np.asarray(q)
+    B, Hq, D = q.shape
+    _, Hkv, kv_cap, _ = k_cache.shape
+    lens = _lens(kv_lens, B)
+    n = max(1, int(lens.max()))
+    q64 = widen(q)
+    k64, v64 = widen(k_cache[:, :, :n]), widen(v_cache[:, :, :n])
+    o = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    rc = _load().oracle_decode_gqa_ragged(
+        _ptr(q64), _ptr(k64), _ptr(v64), B, Hq, Hkv, _iptr(lens), n, D, float(scale),
+        _ptr(o), _ptr(lse), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_decode_gqa_ragged rejected its arguments")
+    return o, lse
+
+
+def decode_mla_ragged(q, ckv, kv_lens, dv, scale, threads=None):
+    """Absorbed-MLA decode of a ragged batch (sequence b reads its first
+    kv_lens[b] rows). Returns (o [B,Hq,dv], lse [B,Hq])."""
+    q = np.asarray(q)
+    B, Hq, Dqk = q.shape
+    lens = _lens(kv_lens, B)
+    n = max(1, int(lens.max()))
+    q64 = widen(q)
+    c64 = widen(ckv[:, :n])
+    o = np.empty((B, Hq, dv))
+    lse = np.empty((B, Hq))
+    rc = _load().oracle_decode_mla_ragged(
+        _ptr(q64), _ptr(c64), B, Hq, _iptr(lens), n, Dqk, int(dv), float(scale),
+        _ptr(o), _ptr(lse), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_decode_mla_ragged rejected its arguments")
     return o, lse

@@ -34,6 +34,14 @@
  * Decode uses no mask (the single query sees only history, [p1] §3) and
  * reads only the first kv_len cache slots, never unfilled ones ([p4] Q3).
  *
+ * Chunked prefill: a chunk of Nq new tokens whose K/V were appended to a
+ * cache, so a sequence's keys are [history | chunk] ([p5] §3: K = past K
+ * followed by current K). The score matrix [Nq][kv_len] gets the triu(1)
+ * mask on its last Nq columns only: chunk row i sees every history key and
+ * chunk keys 0..i ([p5] §3). Ragged batches give every sequence its own
+ * kv_len; a sequence with kv_len = 0 attends to nothing, so its sums are
+ * empty: O = 0 and LSE = ln 0 = −∞.
+ *
  * GQA: query head hq reads K/V head hq / (Hq/Hkv): contiguous groups of
  * Hq/Hkv query heads share one K/V head ([p2] §4).
  * MLA absorbed: one latent head shared by every query head; the key is the
@@ -207,10 +215,75 @@ int oracle_prefill_causal(const double *q, const double *k, const double *v,
     return rc;
 }
 
+/* ------------------------------------------- chunked prefill on a cache --- */
+typedef struct {
+    const double *q, *k, *v;
+    int B, Hq, Hkv, kv_cap, D, n_rows;
+    const int *kv_lens;
+    double scale;
+    const unsigned char *mask; /* [B][n_rows][kv_cap] */
+    double *o, *lse;
+} chunk_ctx;
+
+static void chunk_unit(void *vctx, long unit, double *scratch)
+{
+    chunk_ctx *c = (chunk_ctx *)vctx;
+    long r = unit % c->n_rows;
+    long bh = unit / c->n_rows;
+    int hq = (int)(bh % c->Hq);
+    int b = (int)(bh / c->Hq);
+    int hkv = hq / (c->Hq / c->Hkv);
+    const double *k = c->k + ((long)b * c->Hkv + hkv) * (long)c->kv_cap * c->D;
+    const double *v = c->v + ((long)b * c->Hkv + hkv) * (long)c->kv_cap * c->D;
+    attend_row(c->q + ((long)bh * c->n_rows + r) * c->D, k, c->D, c->D, v, c->D, c->D,
+               c->kv_lens[b], c->mask + ((long)b * c->n_rows + r) * c->kv_cap, c->scale,
+               scratch, c->o + ((long)bh * c->n_rows + r) * c->D,
+               c->lse + (long)bh * c->n_rows + r, NULL);
+}
+
+/* Chunked prefill against a cache: sequence b holds kv_lens[b] keys, the
+ * last Nq of which belong to the chunk (Nq <= kv_lens[b] <= kv_cap).
+ * Mask (triu(1) on the last Nq columns, [p5] §3): with P = kv_lens[b] − Nq
+ * history keys, key j is masked for chunk row i iff j >= P and j − P > i.
+ * q:   [B][Hq][n_rows][D] — the evaluated chunk rows, in `rows` order
+ * k,v: [B][Hkv][kv_cap][D]
+ * rows: n_rows chunk row indices in [0, Nq)
+ * o: [B][Hq][n_rows][D], lse: [B][Hq][n_rows]. */
+int oracle_prefill_chunked(const double *q, const double *k, const double *v,
+                           int B, int Hq, int Hkv, int Nq, const int *kv_lens,
+                           int kv_cap, int D, double scale, const int *rows,
+                           int n_rows, double *o, double *lse, int threads)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || D < 1 || n_rows < 1 || Hq % Hkv || kv_cap < Nq)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (kv_lens[b] < Nq || kv_lens[b] > kv_cap)
+            return -1;
+    for (int r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= Nq)
+            return -1;
+    unsigned char *mask = (unsigned char *)malloc((size_t)B * n_rows * (size_t)kv_cap);
+    if (!mask)
+        return -1;
+    for (int b = 0; b < B; ++b) {
+        const int past = kv_lens[b] - Nq;
+        for (long r = 0; r < n_rows; ++r) {
+            unsigned char *m = mask + ((long)b * n_rows + r) * kv_cap;
+            for (int j = 0; j < kv_cap; ++j)
+                m[j] = (unsigned char)(j >= past && j - past > rows[r]);
+        }
+    }
+    chunk_ctx c = {q, k, v, B, Hq, Hkv, kv_cap, D, n_rows, kv_lens, scale, mask, o, lse};
+    int rc = run_units(chunk_unit, &c, (long)B * Hq * n_rows, kv_cap, threads);
+    free(mask);
+    return rc;
+}
+
 /* ------------------------------------------------------------ GQA decode --- */
 typedef struct {
     const double *q, *k, *v;
     int B, Hq, Hkv, kv_len, kv_cap, D;
+    const int *kv_lens; /* NULL: every sequence is filled to kv_len */
     double scale;
     double *o, *lse, *p;
 } decode_ctx;
@@ -223,7 +296,8 @@ static void decode_unit(void *vctx, long unit, double *scratch)
     int hkv = hq / (c->Hq / c->Hkv);
     const double *k = c->k + ((long)b * c->Hkv + hkv) * (long)c->kv_cap * c->D;
     const double *v = c->v + ((long)b * c->Hkv + hkv) * (long)c->kv_cap * c->D;
-    attend_row(c->q + unit * c->D, k, c->D, c->D, v, c->D, c->D, c->kv_len, NULL,
+    const int n = c->kv_lens ? c->kv_lens[b] : c->kv_len;
+    attend_row(c->q + unit * c->D, k, c->D, c->D, v, c->D, c->D, n, NULL,
                c->scale, scratch, c->o + unit * c->D, c->lse + unit,
                c->p ? c->p + unit * c->kv_len : NULL);
 }
@@ -237,14 +311,30 @@ int oracle_decode_gqa(const double *q, const double *k, const double *v,
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv || kv_len < 1 || kv_len > kv_cap)
         return -1;
-    decode_ctx c = {q, k, v, B, Hq, Hkv, kv_len, kv_cap, D, scale, o, lse, p};
+    decode_ctx c = {q, k, v, B, Hq, Hkv, kv_len, kv_cap, D, NULL, scale, o, lse, p};
     return run_units(decode_unit, &c, (long)B * Hq, kv_len, threads);
+}
+
+/* Ragged decode: sequence b is filled to kv_lens[b] (0 <= kv_lens[b] <=
+ * kv_cap); otherwise as oracle_decode_gqa. No weights are returned. */
+int oracle_decode_gqa_ragged(const double *q, const double *k, const double *v,
+                             int B, int Hq, int Hkv, const int *kv_lens, int kv_cap,
+                             int D, double scale, double *o, double *lse, int threads)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv || kv_cap < 1)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (kv_lens[b] < 0 || kv_lens[b] > kv_cap)
+            return -1;
+    decode_ctx c = {q, k, v, B, Hq, Hkv, 0, kv_cap, D, kv_lens, scale, o, lse, NULL};
+    return run_units(decode_unit, &c, (long)B * Hq, kv_cap, threads);
 }
 
 /* ----------------------------------------------------- MLA absorbed decode --- */
 typedef struct {
     const double *q, *c;
     int B, Hq, kv_len, kv_cap, Dqk, Dv;
+    const int *kv_lens; /* NULL: every sequence is filled to kv_len */
     double scale;
     double *o, *lse;
 } mla_ctx;
@@ -256,8 +346,8 @@ static void mla_unit(void *vctx, long unit, double *scratch)
     const double *lat = c->c + (long)b * c->kv_cap * c->Dqk;
     /* key = the whole row (latent | rope); value = its first Dv channels */
     attend_row(c->q + unit * c->Dqk, lat, c->Dqk, c->Dqk, lat, c->Dqk, c->Dv,
-               c->kv_len, NULL, c->scale, scratch, c->o + unit * c->Dv,
-               c->lse + unit, NULL);
+               c->kv_lens ? c->kv_lens[b] : c->kv_len, NULL, c->scale, scratch,
+               c->o + unit * c->Dv, c->lse + unit, NULL);
 }
 
 /* q: [B][Hq][Dqk]; ckv: [B][kv_cap][Dqk]; o: [B][Hq][Dv]; lse: [B][Hq]. */
@@ -267,6 +357,20 @@ int oracle_decode_mla(const double *q, const double *ckv, int B, int Hq,
 {
     if (B < 1 || Hq < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk || kv_len < 1 || kv_len > kv_cap)
         return -1;
-    mla_ctx c = {q, ckv, B, Hq, kv_len, kv_cap, Dqk, Dv, scale, o, lse};
+    mla_ctx c = {q, ckv, B, Hq, kv_len, kv_cap, Dqk, Dv, NULL, scale, o, lse};
     return run_units(mla_unit, &c, (long)B * Hq, kv_len, threads);
+}
+
+/* Ragged absorbed-MLA decode: sequence b is filled to kv_lens[b]. */
+int oracle_decode_mla_ragged(const double *q, const double *ckv, int B, int Hq,
+                             const int *kv_lens, int kv_cap, int Dqk, int Dv,
+                             double scale, double *o, double *lse, int threads)
+{
+    if (B < 1 || Hq < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk || kv_cap < 1)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (kv_lens[b] < 0 || kv_lens[b] > kv_cap)
+            return -1;
+    mla_ctx c = {q, ckv, B, Hq, 0, kv_cap, Dqk, Dv, kv_lens, scale, o, lse};
+    return run_units(mla_unit, &c, (long)B * Hq, kv_cap, threads);
 }

@@ -338,3 +338,130 @@ def test_oracle_rejects_bad_arguments():
         oracle.prefill_causal(w.q, w.k, w.v, w.scale)
     with pytest.raises(ValueError):
         oracle.prefill_causal(w.q[:, :2], w.k, w.v, w.scale, rows=[8])
+
+
+# ------------------------------------------ chunked prefill and ragged decode ---
+def test_chunked_mask_page_picture():
+    """第11节 §3: with K = [history | chunk], the triu(1) mask covers only the
+    chunk's own columns. With one-hot values (V[j] = e_j) the output row is
+    the weight row itself: every history key and chunk keys 0..i carry
+    weight > 0; chunk keys after i carry exactly 0 (the 4×4 picture)."""
+    vis4 = np.array(GOLD["causal_mask_4x4"]["visible"], dtype=bool)
+    past, Nq = 3, 4
+    L = past + Nq
+    w = workloads.gen_prefill_chunked(1, 2, 1, Nq, L, D=L, seed=31)
+    eye = workloads.round_to_bf16_bits(np.eye(L, dtype=np.float32))
+    v = eye[None, None]
+    o, _ = oracle.prefill_chunked(w.q, w.k, v, w.kv_lens, w.scale)
+    for hq in range(2):
+        p = o[0, hq]                                  # [Nq, L] weights
+        assert np.all(p[:, :past] > 0.0)
+        assert np.all(p[:, past:][~vis4] == 0.0)
+        assert np.all(p[:, past:][vis4] > 0.0)
+        np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_chunked_rows_equal_full_prefill_bitwise():
+    """Bộ 06 Q2 (cached K/V are exact) with 第11节 §3: the chunk's rows are the
+    last Nq rows of a causal prefill over history + chunk, bit for bit (the
+    same scores in the same order; masked keys add exact zeros)."""
+    Nq, L = 9, 30
+    w = workloads.gen_prefill_chunked(2, 4, 2, Nq, L, D=16, seed=32)
+    o_c, lse_c = oracle.prefill_chunked(w.q, w.k, w.v, w.kv_lens, w.scale)
+    full_q = np.zeros((2, 4, L, 16), np.uint16)
+    full_q[:, :, L - Nq:] = w.q
+    o_f, lse_f = oracle.prefill_causal(full_q, w.k[:, :, :L], w.v[:, :, :L], w.scale,
+                                       rows=np.arange(L - Nq, L))
+    np.testing.assert_array_equal(o_c, o_f)
+    np.testing.assert_array_equal(lse_c, lse_f)
+
+
+def test_chunked_matches_torch_sdpa_on_the_full_sequence():
+    """Library special case: torch's CPU float64 SDPA with is_causal over the
+    whole sequence (history + chunk), last Nq rows; ragged lengths per
+    sequence, contiguous GQA groups."""
+    Nq, lens = 7, [7, 19, 40]
+    w = workloads.gen_prefill_chunked(3, 6, 2, Nq, lens, D=32, kv_cap=44, seed=33)
+    o, lse = oracle.prefill_chunked(w.q, w.k, w.v, w.kv_lens, w.scale)
+    for b, L in enumerate(lens):
+        k = oracle.widen(w.k[b:b + 1, :, :L])
+        v = oracle.widen(w.v[b:b + 1, :, :L])
+        q = np.zeros((1, 6, L, 32))
+        q[:, :, L - Nq:] = oracle.widen(w.q[b:b + 1])
+        ref = _torch_sdpa(q, k, v, w.scale, True)[:, :, L - Nq:]
+        np.testing.assert_allclose(o[b:b + 1], ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b:b + 1], _torch_lse(q, k, w.scale, True)[:, :, L - Nq:],
+                                   rtol=0, atol=1e-12)
+
+
+def test_chunked_zero_query_uniform_weights():
+    """Q = 0: chunk row i sees P + i + 1 keys with equal weights, so
+    O[i] = mean(V[0..P+i]) and LSE[i] = ln(P + i + 1)."""
+    Nq, L = 6, 25
+    w = workloads.gen_prefill_chunked(1, 2, 1, Nq, L, D=8, seed=34)
+    q = np.zeros_like(w.q)
+    o, lse = oracle.prefill_chunked(q, w.k, w.v, w.kv_lens, w.scale)
+    v = oracle.widen(w.v[0, 0, :L])
+    P = L - Nq
+    for i in range(Nq):
+        np.testing.assert_allclose(o[0, :, i], np.broadcast_to(v[:P + i + 1].mean(0), (2, 8)),
+                                   rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[0, :, i], math.log(P + i + 1), rtol=0, atol=1e-14)
+
+
+def test_chunk_of_one_token_is_decode():
+    """A one-token chunk is a decode step: no chunk key lies after it, so it
+    sees the whole filled cache (Bộ 06 Q2) — bit for bit the decode result."""
+    w = workloads.gen_prefill_chunked(2, 4, 2, 1, [5, 33], D=16, kv_cap=40, seed=35)
+    o, lse = oracle.prefill_chunked(w.q, w.k, w.v, w.kv_lens, w.scale)
+    for b, L in enumerate(w.kv_lens):
+        o_d, lse_d = oracle.decode_gqa(w.q[b:b + 1, :, 0], w.k[b:b + 1], w.v[b:b + 1], int(L), w.scale)
+        np.testing.assert_array_equal(o[b:b + 1, :, 0], o_d)
+        np.testing.assert_array_equal(lse[b:b + 1, :, 0], lse_d)
+
+
+def test_ragged_decode_is_per_sequence_decode():
+    """A ragged batch is B independent decodes, each over its own filled
+    prefix (Bộ 06 Q3): bit for bit, for GQA and for absorbed MLA; the NaN
+    tail past each length never reaches the result."""
+    lens = [1, 17, 64, 40]
+    w = workloads.gen_decode_gqa(4, 8, 2, D=32, kv_cap=64, kv_lens=lens, seed=36)
+    o, lse = oracle.decode_gqa_ragged(w.q, w.k, w.v, w.kv_lens, w.scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    for b, L in enumerate(lens):
+        o_d, lse_d = oracle.decode_gqa(w.q[b:b + 1], w.k[b:b + 1], w.v[b:b + 1], L, w.scale)
+        np.testing.assert_array_equal(o[b:b + 1], o_d)
+        np.testing.assert_array_equal(lse[b:b + 1], lse_d)
+    m = workloads.gen_decode_mla(3, 16, Dqk=72, Dv=64, kv_cap=50, kv_lens=[50, 3, 21], seed=37)
+    o, lse = oracle.decode_mla_ragged(m.q, m.ckv, m.kv_lens, m.Dv, m.scale)
+    for b, L in enumerate(m.kv_lens):
+        o_d, lse_d = oracle.decode_mla_absorbed(m.q[b:b + 1], m.ckv[b:b + 1], int(L), m.Dv, m.scale)
+        np.testing.assert_array_equal(o[b:b + 1], o_d)
+        np.testing.assert_array_equal(lse[b:b + 1], lse_d)
+
+
+def test_ragged_decode_zero_query_and_empty_sequence():
+    """Q = 0: O = mean(V[:L]), LSE = ln L. A sequence with no filled slot has
+    empty sums: O = 0 and LSE = ln 0 = −∞ (no NaN)."""
+    lens = [0, 1, 9]
+    w = workloads.gen_decode_gqa(3, 4, 2, D=16, kv_cap=12, kv_lens=lens, seed=38)
+    o, lse = oracle.decode_gqa_ragged(np.zeros_like(w.q), w.k, w.v, w.kv_lens, w.scale)
+    assert np.all(o[0] == 0.0) and np.all(lse[0] == -np.inf)
+    for b in (1, 2):
+        v = oracle.widen(w.v[b, :, :lens[b]])            # [Hkv, L, D]
+        np.testing.assert_allclose(o[b], np.repeat(v.mean(1), 2, axis=0), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[b], math.log(lens[b]), rtol=0, atol=1e-15)
+    m = workloads.gen_decode_mla(2, 16, Dqk=24, Dv=16, kv_cap=8, kv_lens=[0, 8], seed=39)
+    o, lse = oracle.decode_mla_ragged(m.q, m.ckv, m.kv_lens, m.Dv, m.scale)
+    assert np.all(o[0] == 0.0) and np.all(lse[0] == -np.inf) and np.all(np.isfinite(o[1]))
+
+
+def test_chunked_and_ragged_reject_bad_lengths():
+    w = workloads.gen_prefill_chunked(1, 2, 1, 4, 10, D=8, seed=40)
+    with pytest.raises(ValueError):       # shorter than the chunk
+        oracle.prefill_chunked(w.q, w.k, w.v, [3], w.scale)
+    with pytest.raises(ValueError):       # one length per sequence
+        oracle.prefill_chunked(w.q, w.k, w.v, [10, 10], w.scale)
+    d = workloads.gen_decode_gqa(2, 2, 1, D=8, kv_cap=6, kv_lens=[2, 6], seed=41)
+    with pytest.raises(ValueError):
+        oracle.decode_gqa_ragged(d.q, d.k, d.v, [-1, 3], d.scale)

@@ -101,6 +101,28 @@ class DecodeGQA:
     q: np.ndarray
     k: np.ndarray
     v: np.ndarray
+    kv_lens: np.ndarray | None = None   # [B] int32 per-sequence lengths (ragged batch)
+
+
+@dataclass
+class PrefillChunked:
+    """A chunk of Nq new tokens per sequence attending to a K/V cache.
+
+    q [B,Hq,Nq,D]; k, v [B,Hkv,kv_cap,D] bf16. Sequence b has kv_lens[b]
+    filled slots; the last Nq of them are the chunk's own K/V (already
+    appended), the ones before are its history.
+    """
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    kv_cap: int
+    D: int
+    scale: float
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    kv_lens: np.ndarray                 # [B] int32, each in [Nq, kv_cap]
 
 
 @dataclass
@@ -121,6 +143,23 @@ class DecodeMLA:
     q: np.ndarray
     ckv: np.ndarray
     s: np.ndarray = field(default=None)   # channel scale, [Dv] float64
+    kv_lens: np.ndarray | None = None     # [B] int32 per-sequence lengths (ragged batch)
+
+
+def ragged_lengths(B, lo, hi, seed) -> np.ndarray:
+    """B sequence lengths drawn uniformly from the integers lo..hi (seeded)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    return rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+
+
+def _lengths(B, kv_lens, kv_len):
+    """Per-sequence fill lengths: kv_lens if given, else kv_len for all."""
+    if kv_lens is None:
+        return np.full(B, kv_len, np.int32)
+    lens = np.asarray(kv_lens, dtype=np.int32).reshape(-1)
+    if lens.shape[0] != B:
+        raise ValueError("kv_lens must hold one length per sequence")
+    return lens
 
 
 def gen_prefill(B, Hq, Hkv, N, D, dtype="bf16", seed=0, scale=None,
@@ -156,11 +195,17 @@ def gen_prefill(B, Hq, Hkv, N, D, dtype="bf16", seed=0, scale=None,
     return Prefill(B, Hq, Hkv, N, D, dtype, float(scale), q, k, v, rows)
 
 
-def gen_decode_gqa(B, Hq, Hkv, kv_len, D=128, kv_cap=None, seed=0, scale=None,
-                   poison_tail=True) -> DecodeGQA:
+def gen_decode_gqa(B, Hq, Hkv, kv_len=None, D=128, kv_cap=None, seed=0, scale=None,
+                   poison_tail=True, kv_lens=None) -> DecodeGQA:
     """One query token per sequence; K/V cache of capacity kv_cap filled to
-    kv_len. Slots past kv_len hold NaN when poison_tail is set, so a kernel
-    that reads them produces NaN."""
+    kv_len (or, for a ragged batch, sequence b filled to kv_lens[b]; kv_len
+    is then the longest). Slots past a sequence's length hold NaN when
+    poison_tail is set, so a kernel that reads them produces NaN."""
+    if kv_lens is not None:
+        lens = _lengths(B, kv_lens, None)
+        kv_len = int(lens.max())
+    else:
+        lens = _lengths(B, None, kv_len)
     if kv_cap is None:
         kv_cap = kv_len
     rq, rk, rv = _rng(seed, 3)
@@ -169,16 +214,47 @@ def gen_decode_gqa(B, Hq, Hkv, kv_len, D=128, kv_cap=None, seed=0, scale=None,
     q = _normal_bf16(rq, (B, Hq, D))
     k = np.empty((B, Hkv, kv_cap, D), np.uint16)
     v = np.empty((B, Hkv, kv_cap, D), np.uint16)
-    k[:, :, :kv_len] = _normal_bf16(rk, (B, Hkv, kv_len, D))
-    v[:, :, :kv_len] = _normal_bf16(rv, (B, Hkv, kv_len, D))
     fill = BF16_NAN_BITS if poison_tail else np.uint16(0)
-    k[:, :, kv_len:] = fill
-    v[:, :, kv_len:] = fill
-    return DecodeGQA(B, Hq, Hkv, kv_len, kv_cap, D, float(scale), q, k, v)
+    for b in range(B):
+        n = int(lens[b])
+        k[b, :, :n] = _normal_bf16(rk, (Hkv, n, D))
+        v[b, :, :n] = _normal_bf16(rv, (Hkv, n, D))
+        k[b, :, n:] = fill
+        v[b, :, n:] = fill
+    return DecodeGQA(B, Hq, Hkv, kv_len, kv_cap, D, float(scale), q, k, v,
+                     lens if kv_lens is not None else None)
 
 
-def gen_decode_mla(B, Hq, kv_len, Dqk=576, Dv=512, kv_cap=None, seed=0,
-                   scale=None, mag_lo=1e-4, mag_hi=1e2, poison_tail=True) -> DecodeMLA:
+def gen_prefill_chunked(B, Hq, Hkv, Nq, kv_lens, D=128, kv_cap=None, seed=0, scale=None,
+                        poison_tail=True) -> PrefillChunked:
+    """A chunk of Nq query tokens per sequence against a cache filled to
+    kv_lens[b] (a scalar applies to every sequence). All of Q and the filled
+    K/V are N(0,1) in bf16; slots past a sequence's length hold NaN when
+    poison_tail is set."""
+    lens = _lengths(B, None, int(kv_lens)) if np.ndim(kv_lens) == 0 else _lengths(B, kv_lens, None)
+    if lens.min() < Nq:
+        raise ValueError("every sequence must hold at least the chunk's Nq tokens")
+    if kv_cap is None:
+        kv_cap = int(lens.max())
+    rq, rk, rv = _rng(seed, 3)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    q = _normal_bf16(rq, (B, Hq, Nq, D))
+    k = np.empty((B, Hkv, kv_cap, D), np.uint16)
+    v = np.empty((B, Hkv, kv_cap, D), np.uint16)
+    fill = BF16_NAN_BITS if poison_tail else np.uint16(0)
+    for b in range(B):
+        n = int(lens[b])
+        k[b, :, :n] = _normal_bf16(rk, (Hkv, n, D))
+        v[b, :, :n] = _normal_bf16(rv, (Hkv, n, D))
+        k[b, :, n:] = fill
+        v[b, :, n:] = fill
+    return PrefillChunked(B, Hq, Hkv, Nq, kv_cap, D, float(scale), q, k, v, lens)
+
+
+def gen_decode_mla(B, Hq, kv_len=None, Dqk=576, Dv=512, kv_cap=None, seed=0,
+                   scale=None, mag_lo=1e-4, mag_hi=1e2, poison_tail=True,
+                   kv_lens=None) -> DecodeMLA:
     """Absorbed-MLA decode inputs, channel-balanced before storage.
 
     s_k = 10^U(log10 mag_lo, log10 mag_hi) per latent channel. The model-side
@@ -186,7 +262,14 @@ def gen_decode_mla(B, Hq, kv_len, Dqk=576, Dv=512, kv_cap=None, seed=0,
     stay O(1)); what is stored is bf16(q̃ ⊙ s⁻¹) and bf16(s ⊙ c). The rope
     channels (Dqk - Dv of them) are N(0,1) and not scaled. Default scale is
     1/√192 (128 no-rope + 64 rope dims of the pre-absorption head).
+    With kv_lens (a ragged batch) sequence b is filled to kv_lens[b] and
+    kv_len is the longest.
     """
+    if kv_lens is not None:
+        lens = _lengths(B, kv_lens, None)
+        kv_len = int(lens.max())
+    else:
+        lens = _lengths(B, None, kv_len)
     if kv_cap is None:
         kv_cap = kv_len
     rq, rc, rs = _rng(seed, 3)
@@ -199,15 +282,17 @@ def gen_decode_mla(B, Hq, kv_len, Dqk=576, Dv=512, kv_cap=None, seed=0,
     q = round_to_bf16_bits(qn)
     ckv = np.empty((B, kv_cap, Dqk), np.uint16)
     for b in range(B):                              # per batch to bound memory
-        cn = _normal(rc, (kv_len, Dqk)).astype(np.float64)
+        n = int(lens[b])
+        cn = _normal(rc, (n, Dqk)).astype(np.float64)
         c_raw = cn[:, :Dv] / s                      # raw latent
         cn[:, :Dv] = s * c_raw                      # S·c
-        ckv[b, :kv_len] = round_to_bf16_bits(cn)
-    ckv[:, kv_len:] = BF16_NAN_BITS if poison_tail else np.uint16(0)
-    return DecodeMLA(B, Hq, kv_len, kv_cap, Dqk, Dv, float(scale), q, ckv, s)
+        ckv[b, :n] = round_to_bf16_bits(cn)
+        ckv[b, n:] = BF16_NAN_BITS if poison_tail else np.uint16(0)
+    return DecodeMLA(B, Hq, kv_len, kv_cap, Dqk, Dv, float(scale), q, ckv, s,
+                     lens if kv_lens is not None else None)
 
 
-# ------------------------------------------------- the five named workloads ---
+# --------------------------------------------------------- named workloads ---
 WORKLOADS = {
     "prefill_f32_tiny": dict(
         kind="prefill", B=1, Hq=2, Hkv=2, N=64, D=64, dtype="f32", seed=1001,
@@ -224,6 +309,17 @@ WORKLOADS = {
     "decode_mla_absorbed_32k": dict(
         kind="decode_mla", B=16, Hq=128, kv_len=32768, Dqk=576, Dv=512, seed=1005,
         scale=1.0 / math.sqrt(128 + 64)),
+    # serving shapes of the same kernels: a prompt chunk appended to a cache
+    # (bottom-right causal mask) and decode batches of mixed lengths
+    "prefill_chunked_4k_on_32k": dict(
+        kind="prefill_chunked", B=1, Hq=32, Hkv=8, Nq=4096, kv_lens=32768, D=128,
+        seed=1006, scale=1.0 / math.sqrt(128)),
+    "decode_gqa_ragged_8k": dict(
+        kind="decode_gqa", B=32, Hq=32, Hkv=8, kv_lens=("ragged", 128, 8192, 1107),
+        kv_cap=8192, D=128, seed=1007, scale=1.0 / math.sqrt(128)),
+    "decode_mla_ragged_32k": dict(
+        kind="decode_mla", B=16, Hq=128, kv_lens=("ragged", 1024, 32768, 1108),
+        kv_cap=32768, Dqk=576, Dv=512, seed=1008, scale=1.0 / math.sqrt(128 + 64)),
 }
 
 
@@ -232,6 +328,11 @@ def make(name: str, **overrides):
     cfg = dict(WORKLOADS[name])
     cfg.update(overrides)
     kind = cfg.pop("kind")
+    lens = cfg.get("kv_lens")
+    if isinstance(lens, tuple) and lens and lens[0] == "ragged":
+        cfg["kv_lens"] = ragged_lengths(cfg["B"], *lens[1:])
+    if kind == "prefill_chunked":
+        return gen_prefill_chunked(**cfg)
     if kind == "prefill":
         return gen_prefill(**cfg)
     if kind == "decode_gqa":
@@ -269,3 +370,25 @@ def decode_mla_bytes(B, Hq, kv_len, Dqk, Dv, elt=2):
 
 def decode_mla_flops(B, Hq, kv_len, Dqk, Dv):
     return 2 * B * Hq * kv_len * (Dqk + Dv)
+
+
+def prefill_chunked_flops(Hq, Nq, kv_lens, D):
+    """Flops of the visible pairs of a chunk against its cache: chunk row i
+    of sequence b sees kv_lens[b] − Nq + i + 1 keys; 4·D flops per pair."""
+    lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
+    pairs = int(np.sum(Nq * (lens - Nq) + Nq * (Nq + 1) // 2))
+    return 4 * D * pairs * Hq
+
+
+def decode_gqa_ragged_bytes(Hq, Hkv, kv_lens, D, elt=2):
+    """As decode_gqa_bytes with per-sequence filled lengths."""
+    lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
+    B = lens.shape[0]
+    return int(elt * (2 * Hkv * int(lens.sum()) * D + 2 * B * Hq * D) + 4 * B * Hq)
+
+
+def decode_mla_ragged_bytes(Hq, kv_lens, Dqk, Dv, elt=2):
+    """As decode_mla_bytes with per-sequence filled lengths."""
+    lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
+    B = lens.shape[0]
+    return int(elt * (int(lens.sum()) * Dqk + B * Hq * Dqk + B * Hq * Dv) + 4 * B * Hq)
