@@ -20,6 +20,9 @@
  *  - "MLA 矩阵乘法吸收的数值稳定性治理": §一 absorption into the query,
  *    §二 channel scale S and FP32 on-chip accumulation, §五 low-precision
  *    storage with high-precision accumulation.
+ *  - "第11节：Attention 实现（Flash vs Fallback）": §3 (the keys are the
+ *    cached history followed by the current tokens; the triu(1) causal mask
+ *    covers only the current tokens' columns), §4 score shape [B,H,Q,K].
  *
  * Conventions shared by all entry points
  *  - All tensor pointers are DEVICE pointers on the current HIP device,
@@ -86,6 +89,38 @@ attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
                                 hipStream_t stream);
 
 /*
+ * Chunked prefill against a K/V cache: for each sequence, Nq new tokens whose
+ * K/V are already appended to the cache attend to the whole filled cache.
+ * Sequence b's cache holds kv_lens[b] positions; its last Nq are the chunk's
+ * own tokens, so chunk row i sits at position P + i with P = kv_lens[b] − Nq,
+ * and key j is visible to it iff j <= P + i (every history key, and chunk
+ * keys 0..i: the bottom-right-aligned causal mask). Slots at or past
+ * kv_lens[b] are never read.
+ *
+ *   q        [B, Hq, Nq, D]          bf16
+ *   k_cache  [B, Hkv, kv_cap, D]     bf16
+ *   v_cache  [B, Hkv, kv_cap, D]     bf16
+ *   o        [B, Hq, Nq, D]          bf16 (output)
+ *   lse      [B, Hq, Nq]             fp32 (output, natural log)
+ *   kv_lens  [B]                     int32, DEVICE memory, read by the kernel
+ *            at run time (so a captured graph can be replayed with new
+ *            lengths); each value must lie in [Nq, kv_cap] — values outside
+ *            are clamped into that range, they are not reported.
+ *
+ * Query head hq uses K/V head hq / (Hq/Hkv). D must be 128. Nq = 1 is a
+ * decode step; Nq = kv_lens[b] with kv_cap = Nq is attn_prefill_causal.
+ * Errors: NULL pointer → ATTN_ERR_NULL_POINTER; B, Hq, Hkv, Nq < 1,
+ * Hq % Hkv, Nq > kv_cap, a tensor above 2^31 elements, or a scale that is
+ * not finite and positive → ATTN_ERR_BAD_SHAPE; other D → ATTN_ERR_UNSUPPORTED;
+ * launch failure → ATTN_ERR_HIP.
+ */
+attn_status attn_prefill_chunked(const void *q, const void *k_cache,
+                                 const void *v_cache, void *o, float *lse,
+                                 const int *kv_lens, int B, int Hq, int Hkv,
+                                 int Nq, int kv_cap, int D, float scale,
+                                 hipStream_t stream);
+
+/*
  * Single-query GQA decode over a bf16 K/V cache (no mask: the one query sees
  * every cached position). Only the first kv_len slots are read; slots
  * kv_len..kv_cap-1 are never touched (they may hold anything). kv_len counts
@@ -124,6 +159,30 @@ size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len,
                                        int D);
 
 /*
+ * GQA decode of a ragged batch: as attn_decode_gqa, but sequence b's cache
+ * is filled to kv_lens[b] ("Bộ 06 · Bên trong model", Q3: attend to the
+ * filled part only; each sequence of a serving batch has its own length).
+ *
+ *   kv_lens  [B] int32, DEVICE memory, read at run time; each value is
+ *            clamped to [0, max_kv_len]. A sequence of length 0 attends to
+ *            nothing: its O is 0 and its LSE is −∞ (the empty sums).
+ *   max_kv_len  the longest length in the batch (or any bound of it, at
+ *            most kv_cap): it fixes the split of the cache and the
+ *            workspace size, attn_decode_gqa_workspace_bytes(B, Hq, Hkv,
+ *            max_kv_len, D). Work for splits past a sequence's length is
+ *            skipped.
+ *
+ * Errors as for attn_decode_gqa with max_kv_len in the place of kv_len;
+ * kv_lens NULL → ATTN_ERR_NULL_POINTER.
+ */
+attn_status attn_decode_gqa_ragged(const void *q, const void *k_cache,
+                                   const void *v_cache, void *o, float *lse,
+                                   const int *kv_lens, int B, int Hq, int Hkv,
+                                   int max_kv_len, int kv_cap, int D,
+                                   float scale, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Absorbed MLA decode: every query head attends to one shared latent cache.
  * Each cached row is [latent (Dv) | rope (Dqk − Dv)]; the key is the whole
  * row and the value is its latent part, so the value is read from the same
@@ -152,6 +211,22 @@ attn_status attn_decode_mla_absorbed(const void *q, const void *ckv, void *o,
 /* Bytes of workspace attn_decode_mla_absorbed needs (0 if invalid). */
 size_t attn_decode_mla_workspace_bytes(int B, int Hq, int kv_len, int Dqk,
                                        int Dv);
+
+/*
+ * Absorbed MLA decode of a ragged batch: as attn_decode_mla_absorbed, with
+ * sequence b's latent cache filled to kv_lens[b] (DEVICE int32 [B], clamped
+ * to [0, max_kv_len]; length 0 gives O = 0, LSE = −∞). max_kv_len fixes the
+ * split and the workspace, attn_decode_mla_workspace_bytes(B, Hq,
+ * max_kv_len, Dqk, Dv).
+ * Errors as for attn_decode_mla_absorbed with max_kv_len in the place of
+ * kv_len; kv_lens NULL → ATTN_ERR_NULL_POINTER.
+ */
+attn_status attn_decode_mla_ragged(const void *q, const void *ckv, void *o,
+                                   float *lse, const int *kv_lens, int B,
+                                   int Hq, int max_kv_len, int kv_cap,
+                                   int Dqk, int Dv, float scale,
+                                   void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char *attn_status_string(attn_status s);

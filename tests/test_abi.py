@@ -29,7 +29,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -110,6 +110,54 @@ def test_decode_mla_validation(lib):
     need = attn.attn_decode_mla_workspace_bytes(2, 128, 1000)
     assert need > 0
     assert _mla(lib, ws_bytes=need - 1) == WS
+
+
+def _chunked(lib, q=P, k=P, v=P, o=P, lse=P, lens=P, B=2, Hq=8, Hkv=2, Nq=100, kv_cap=512,
+             D=128, scale=0.1):
+    return lib.attn_prefill_chunked(q, k, v, o, lse, lens, B, Hq, Hkv, Nq, kv_cap, D, scale, None)
+
+
+def test_prefill_chunked_validation(lib):
+    assert _chunked(lib, lens=None) == NULLP
+    assert _chunked(lib, v=None) == NULLP
+    assert _chunked(lib, Nq=0) == SHAPE
+    assert _chunked(lib, Nq=513) == SHAPE                # the chunk does not fit the cache
+    assert _chunked(lib, Hq=6, Hkv=4) == SHAPE
+    assert _chunked(lib, B=1 << 10, Hkv=8, Hq=8, kv_cap=1 << 12, Nq=1 << 12) == SHAPE
+    assert _chunked(lib, D=64) == UNSUP
+    assert _chunked(lib, lens=P + 2) == UNSUP            # misaligned length array
+    for s in BAD_SCALES:
+        assert _chunked(lib, scale=s) == SHAPE
+
+
+def _gqa_r(lib, q=P, k=P, v=P, o=P, lse=P, lens=P, B=2, Hq=8, Hkv=2, max_len=100, kv_cap=128,
+           D=128, ws=P, ws_bytes=1 << 30, scale=0.1):
+    return lib.attn_decode_gqa_ragged(q, k, v, o, lse, lens, B, Hq, Hkv, max_len, kv_cap, D,
+                                      scale, ws, ws_bytes, None)
+
+
+def _mla_r(lib, q=P, c=P, o=P, lse=P, lens=P, B=2, Hq=128, max_len=1000, kv_cap=1024, Dqk=576,
+           Dv=512, ws=P, ws_bytes=1 << 30, scale=0.07):
+    return lib.attn_decode_mla_ragged(q, c, o, lse, lens, B, Hq, max_len, kv_cap, Dqk, Dv, scale,
+                                      ws, ws_bytes, None)
+
+
+def test_ragged_decode_validation(lib):
+    assert _gqa_r(lib, lens=None) == NULLP
+    assert _gqa_r(lib, max_len=0) == SHAPE
+    assert _gqa_r(lib, max_len=129) == SHAPE
+    assert "max_kv_len" in attn.last_error()
+    assert _gqa_r(lib, D=64) == UNSUP
+    assert _gqa_r(lib, lens=P + 1) == UNSUP
+    need = attn.attn_decode_gqa_workspace_bytes(2, 8, 2, 100, 128)
+    assert _gqa_r(lib, ws_bytes=need - 1) == WS
+    assert _mla_r(lib, lens=None) == NULLP
+    assert _mla_r(lib, max_len=1025) == SHAPE
+    assert _mla_r(lib, Hq=20) == UNSUP
+    need = attn.attn_decode_mla_workspace_bytes(2, 128, 1000)
+    assert _mla_r(lib, ws_bytes=need - 1) == WS
+    for s in BAD_SCALES:
+        assert _gqa_r(lib, scale=s) == SHAPE and _mla_r(lib, scale=s) == SHAPE
 
 
 def test_last_error_is_thread_local(lib):

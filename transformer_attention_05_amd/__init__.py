@@ -8,6 +8,10 @@ no fallback: if libattn.so is missing or fails to load, every call raises.
     o, lse = attn_prefill_causal(q, k, v, scale)                  # [B,H,N,D]
     o, lse = attn_decode_gqa(q, k_cache, v_cache, kv_len, scale)  # q [B,Hq,D]
     o, lse = attn_decode_mla_absorbed(q, ckv, kv_len, 512, scale) # q [B,Hq,576]
+    o, lse = attn_prefill_chunked(q, k_cache, v_cache, kv_lens, scale)  # q [B,Hq,Nq,D]
+    o, lse = attn_decode_gqa_ragged(q, k_cache, v_cache, kv_lens, max_kv_len, scale)
+    o, lse = attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, 512, scale)
+(kv_lens: an int32 GPU tensor of per-sequence lengths, read by the kernels.)
 """
 from __future__ import annotations
 
@@ -51,11 +55,17 @@ def load() -> ctypes.CDLL:
         lib.attn_prefill_causal.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_mla_absorbed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        lib.attn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        lib.attn_decode_gqa_ragged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz,
+                                               vp]
+        lib.attn_decode_mla_ragged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.attn_decode_mla_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.attn_decode_gqa_workspace_bytes.restype = sz
         lib.attn_decode_mla_workspace_bytes.restype = sz
-        for fn in (lib.attn_prefill_causal, lib.attn_decode_gqa, lib.attn_decode_mla_absorbed):
+        for fn in (lib.attn_prefill_causal, lib.attn_decode_gqa, lib.attn_decode_mla_absorbed,
+                   lib.attn_prefill_chunked, lib.attn_decode_gqa_ragged,
+                   lib.attn_decode_mla_ragged):
             fn.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
@@ -187,6 +197,98 @@ def attn_decode_mla_absorbed(q, ckv, kv_len, dv=512, scale=None, out=None, lse=N
     st = lib.attn_decode_mla_absorbed(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), B, Hq, int(kv_len),
                                       kv_cap, Dqk, dv, float(scale), _ptr(w),
                                       w.numel() * w.element_size(), _stream(q.device))
+    _check(st, lib)
+    return o, l
+
+
+def _need_lens(kv_lens, B):
+    _need(kv_lens, "kv_lens", torch.int32, 1)
+    if kv_lens.shape[0] != B:
+        raise ValueError("kv_lens must hold one length per sequence")
+
+
+def attn_prefill_chunked(q, k_cache, v_cache, kv_lens, scale=None, out=None, lse=None):
+    """Chunked prefill against a cache. q [B,Hq,Nq,D] bf16; caches
+    [B,Hkv,kv_cap,D] bf16 filled to kv_lens[b] (int32 GPU tensor [B], each
+    in [Nq, kv_cap]), the last Nq slots being the chunk's own tokens.
+    Returns (o [B,Hq,Nq,D] bf16, lse [B,Hq,Nq] fp32)."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, Hq, Nq, D = q.shape
+    _, Hkv, kv_cap, _ = k_cache.shape
+    if k_cache.shape != (B, Hkv, kv_cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, Hkv, kv_cap, D] matching q")
+    _need_lens(kv_lens, B)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "out", torch.bfloat16, 4)
+    _need(l, "lse", torch.float32, 3)
+    st = lib.attn_prefill_chunked(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
+                                  _ptr(kv_lens), B, Hq, Hkv, Nq, kv_cap, D, float(scale),
+                                  _stream(q.device))
+    _check(st, lib)
+    return o, l
+
+
+def attn_decode_gqa_ragged(q, k_cache, v_cache, kv_lens, max_kv_len, scale=None, out=None,
+                           lse=None, ws=None):
+    """GQA decode of a ragged batch: sequence b's caches are filled to
+    kv_lens[b] (int32 GPU tensor [B], each at most max_kv_len). Returns
+    (o [B,Hq,D] bf16, lse [B,Hq] fp32); a sequence of length 0 gets O = 0,
+    LSE = -inf."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    B, Hq, D = q.shape
+    _, Hkv, kv_cap, _ = k_cache.shape
+    if k_cache.shape != (B, Hkv, kv_cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, Hkv, kv_cap, D] matching q")
+    _need_lens(kv_lens, B)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "out", torch.bfloat16, 3)
+    _need(l, "lse", torch.float32, 2)
+    need = lib.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, int(max_kv_len), D)
+    w = workspace(need, q.device) if ws is None else ws
+    st = lib.attn_decode_gqa_ragged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
+                                    _ptr(kv_lens), B, Hq, Hkv, int(max_kv_len), kv_cap, D,
+                                    float(scale), _ptr(w), w.numel() * w.element_size(),
+                                    _stream(q.device))
+    _check(st, lib)
+    return o, l
+
+
+def attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, dv=512, scale=None, out=None, lse=None,
+                           ws=None):
+    """Absorbed MLA decode of a ragged batch: sequence b's latent cache is
+    filled to kv_lens[b] (int32 GPU tensor [B], each at most max_kv_len).
+    Returns (o [B,Hq,dv] bf16, lse [B,Hq] fp32)."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(ckv, "ckv", torch.bfloat16, 3)
+    B, Hq, Dqk = q.shape
+    kv_cap = ckv.shape[1]
+    if ckv.shape != (B, kv_cap, Dqk):
+        raise ValueError("ckv must be [B, kv_cap, Dqk] matching q")
+    _need_lens(kv_lens, B)
+    if scale is None:
+        scale = 1.0 / math.sqrt(128 + 64)
+    o = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "out", torch.bfloat16, 3)
+    _need(l, "lse", torch.float32, 2)
+    need = lib.attn_decode_mla_workspace_bytes(B, Hq, int(max_kv_len), Dqk, dv)
+    w = workspace(need, q.device) if ws is None else ws
+    st = lib.attn_decode_mla_ragged(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), _ptr(kv_lens), B, Hq,
+                                    int(max_kv_len), kv_cap, Dqk, dv, float(scale), _ptr(w),
+                                    w.numel() * w.element_size(), _stream(q.device))
     _check(st, lib)
     return o, l
 

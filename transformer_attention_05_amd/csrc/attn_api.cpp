@@ -40,6 +40,73 @@ attn_status from_hip(hipError_t e, const char *what)
     return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Shared by the uniform and the ragged GQA decode: kv_lens NULL means every
+// sequence holds kv_len keys; otherwise kv_len is the longest.
+attn_status decode_gqa_impl(const char *fn, const void *q, const void *k_cache,
+                            const void *v_cache, void *o, float *lse, const int *kv_lens,
+                            int B, int Hq, int Hkv, int kv_len, int kv_cap, int D, float scale,
+                            void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const char *len_name = kv_lens ? "max_kv_len" : "kv_len";
+    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: B, Hq, Hkv, D must be >= 1", fn);
+    if (Hq % Hkv)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: Hq (%d) not a multiple of Hkv (%d)", fn, Hq, Hkv);
+    if (!good_scale(scale))
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: scale must be finite and > 0", fn);
+    if (kv_len < 1 || kv_len > kv_cap)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: need 1 <= %s (%d) <= kv_cap (%d)", fn, len_name, kv_len,
+                    kv_cap);
+    if ((long long)B * Hkv * kv_cap * D > kMaxElems)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: cache exceeds 2^31 elements", fn);
+    if (D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d (only 128)", fn, D);
+    if (Hq / Hkv > 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: group size %d above 16", fn, Hq / Hkv);
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(o) || !aligned4(lse) ||
+        !aligned4(kv_lens))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned (o, lse, kv_lens: 4)", fn);
+    attn::GqaPlan p;
+    attn::gqa_plan(B, Hq, Hkv, kv_len, &p);
+    if (!workspace || workspace_bytes < p.ws_total || !aligned16(workspace))
+        return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, p.ws_total,
+                    workspace ? workspace_bytes : (size_t)0);
+    return from_hip(attn::launch_decode_gqa(p, q, k_cache, v_cache, o, lse, B, Hq, Hkv, kv_len,
+                                            kv_cap, scale, workspace, stream, kv_lens),
+                    fn);
+}
+
+attn_status decode_mla_impl(const char *fn, const void *q, const void *ckv, void *o, float *lse,
+                            const int *kv_lens, int B, int Hq, int kv_len, int kv_cap, int Dqk,
+                            int Dv, float scale, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream)
+{
+    const char *len_name = kv_lens ? "max_kv_len" : "kv_len";
+    if (B < 1 || Hq < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: bad B, Hq, Dqk or Dv", fn);
+    if (!good_scale(scale))
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: scale must be finite and > 0", fn);
+    if (kv_len < 1 || kv_len > kv_cap)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: need 1 <= %s (%d) <= kv_cap (%d)", fn, len_name, kv_len,
+                    kv_cap);
+    if ((long long)B * kv_cap * Dqk > kMaxElems)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: cache exceeds 2^31 elements", fn);
+    if (Dqk != 576 || Dv != 512)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: (Dqk, Dv) = (%d, %d), only (576, 512)", fn, Dqk, Dv);
+    if (Hq % 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: Hq (%d) not a multiple of 16", fn, Hq);
+    if (!aligned16(q) || !aligned16(ckv) || !aligned16(o) || !aligned4(lse) || !aligned4(kv_lens))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned (lse, kv_lens: 4)", fn);
+    attn::MlaPlan p;
+    attn::mla_plan(B, Hq, kv_len, &p);
+    if (!workspace || workspace_bytes < p.ws_total || !aligned16(workspace))
+        return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, p.ws_total,
+                    workspace ? workspace_bytes : (size_t)0);
+    return from_hip(attn::launch_decode_mla(p, q, ckv, o, lse, B, Hq, kv_len, kv_cap, scale,
+                                            workspace, stream, kv_lens),
+                    fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,6 +154,34 @@ attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
                     "attn_prefill_causal");
 }
 
+attn_status attn_prefill_chunked(const void *q, const void *k_cache, const void *v_cache,
+                                 void *o, float *lse, const int *kv_lens, int B, int Hq,
+                                 int Hkv, int Nq, int kv_cap, int D, float scale,
+                                 hipStream_t stream)
+{
+    static const char fn[] = "attn_prefill_chunked";
+    if (!q || !k_cache || !v_cache || !o || !lse || !kv_lens)
+        return fail(ATTN_ERR_NULL_POINTER, "%s: NULL tensor pointer", fn);
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || D < 1)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: B, Hq, Hkv, Nq, D must be >= 1", fn);
+    if (Hq % Hkv)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: Hq (%d) not a multiple of Hkv (%d)", fn, Hq, Hkv);
+    if (!good_scale(scale))
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: scale must be finite and > 0", fn);
+    if (Nq > kv_cap)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: need Nq (%d) <= kv_cap (%d)", fn, Nq, kv_cap);
+    if ((long long)B * Hq * Nq * D > kMaxElems || (long long)B * Hkv * kv_cap * D > kMaxElems)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: tensor exceeds 2^31 elements", fn);
+    if (D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d (only 128)", fn, D);
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        !aligned4(lse) || !aligned4(kv_lens))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned (lse, kv_lens: 4)", fn);
+    return from_hip(attn::launch_prefill_chunked_d128(q, k_cache, v_cache, o, lse, kv_lens, B, Hq,
+                                                      Hkv, Nq, kv_cap, scale, stream),
+                    fn);
+}
+
 size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len, int D)
 {
     attn::GqaPlan p;
@@ -101,30 +196,19 @@ attn_status attn_decode_gqa(const void *q, const void *k_cache, const void *v_ca
 {
     if (!q || !k_cache || !v_cache || !o || !lse)
         return fail(ATTN_ERR_NULL_POINTER, "attn_decode_gqa: NULL tensor pointer");
-    if (B < 1 || Hq < 1 || Hkv < 1 || D < 1)
-        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: B, Hq, Hkv, D must be >= 1");
-    if (Hq % Hkv)
-        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: Hq (%d) not a multiple of Hkv (%d)", Hq, Hkv);
-    if (!good_scale(scale))
-        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: scale must be finite and > 0");
-    if (kv_len < 1 || kv_len > kv_cap)
-        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: need 1 <= kv_len (%d) <= kv_cap (%d)", kv_len, kv_cap);
-    if ((long long)B * Hkv * kv_cap * D > kMaxElems)
-        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_gqa: cache exceeds 2^31 elements");
-    if (D != 128)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: head dim %d (only 128)", D);
-    if (Hq / Hkv > 16)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: group size %d above 16", Hq / Hkv);
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(o) || !aligned4(lse))
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_gqa: tensors must be 16-byte aligned (o, lse: 4)");
-    attn::GqaPlan p;
-    attn::gqa_plan(B, Hq, Hkv, kv_len, &p);
-    if (!workspace || workspace_bytes < p.ws_total || !aligned16(workspace))
-        return fail(ATTN_ERR_WORKSPACE, "attn_decode_gqa: workspace needs %zu bytes (got %zu)",
-                    p.ws_total, workspace ? workspace_bytes : (size_t)0);
-    return from_hip(attn::launch_decode_gqa(p, q, k_cache, v_cache, o, lse, B, Hq, Hkv, kv_len,
-                                            kv_cap, scale, workspace, stream),
-                    "attn_decode_gqa");
+    return decode_gqa_impl("attn_decode_gqa", q, k_cache, v_cache, o, lse, nullptr, B, Hq, Hkv,
+                           kv_len, kv_cap, D, scale, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_gqa_ragged(const void *q, const void *k_cache, const void *v_cache,
+                                   void *o, float *lse, const int *kv_lens, int B, int Hq,
+                                   int Hkv, int max_kv_len, int kv_cap, int D, float scale,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!q || !k_cache || !v_cache || !o || !lse || !kv_lens)
+        return fail(ATTN_ERR_NULL_POINTER, "attn_decode_gqa_ragged: NULL tensor pointer");
+    return decode_gqa_impl("attn_decode_gqa_ragged", q, k_cache, v_cache, o, lse, kv_lens, B, Hq,
+                           Hkv, max_kv_len, kv_cap, D, scale, workspace, workspace_bytes, stream);
 }
 
 size_t attn_decode_mla_workspace_bytes(int B, int Hq, int kv_len, int Dqk, int Dv)
@@ -141,30 +225,19 @@ attn_status attn_decode_mla_absorbed(const void *q, const void *ckv, void *o, fl
 {
     if (!q || !ckv || !o || !lse)
         return fail(ATTN_ERR_NULL_POINTER, "attn_decode_mla_absorbed: NULL tensor pointer");
-    if (B < 1 || Hq < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk)
-        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: bad B, Hq, Dqk or Dv");
-    if (!good_scale(scale))
-        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: scale must be finite and > 0");
-    if (kv_len < 1 || kv_len > kv_cap)
-        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: need 1 <= kv_len (%d) <= kv_cap (%d)",
-                    kv_len, kv_cap);
-    if ((long long)B * kv_cap * Dqk > kMaxElems)
-        return fail(ATTN_ERR_BAD_SHAPE, "attn_decode_mla_absorbed: cache exceeds 2^31 elements");
-    if (Dqk != 576 || Dv != 512)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: (Dqk, Dv) = (%d, %d), only (576, 512)",
-                    Dqk, Dv);
-    if (Hq % 16)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: Hq (%d) not a multiple of 16", Hq);
-    if (!aligned16(q) || !aligned16(ckv) || !aligned16(o) || !aligned4(lse))
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_mla_absorbed: tensors must be 16-byte aligned");
-    attn::MlaPlan p;
-    attn::mla_plan(B, Hq, kv_len, &p);
-    if (!workspace || workspace_bytes < p.ws_total || !aligned16(workspace))
-        return fail(ATTN_ERR_WORKSPACE, "attn_decode_mla_absorbed: workspace needs %zu bytes (got %zu)",
-                    p.ws_total, workspace ? workspace_bytes : (size_t)0);
-    return from_hip(attn::launch_decode_mla(p, q, ckv, o, lse, B, Hq, kv_len, kv_cap, scale,
-                                            workspace, stream),
-                    "attn_decode_mla_absorbed");
+    return decode_mla_impl("attn_decode_mla_absorbed", q, ckv, o, lse, nullptr, B, Hq, kv_len,
+                           kv_cap, Dqk, Dv, scale, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_mla_ragged(const void *q, const void *ckv, void *o, float *lse,
+                                   const int *kv_lens, int B, int Hq, int max_kv_len, int kv_cap,
+                                   int Dqk, int Dv, float scale, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream)
+{
+    if (!q || !ckv || !o || !lse || !kv_lens)
+        return fail(ATTN_ERR_NULL_POINTER, "attn_decode_mla_ragged: NULL tensor pointer");
+    return decode_mla_impl("attn_decode_mla_ragged", q, ckv, o, lse, kv_lens, B, Hq, max_kv_len,
+                           kv_cap, Dqk, Dv, scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

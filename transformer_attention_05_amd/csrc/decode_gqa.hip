@@ -34,6 +34,11 @@
 // log-sum-exp (split-K merge, "AI Infra 入门…", §3). No workgroup waits for
 // another; the kernel boundary orders the partial writes before the merge.
 // Slots at or past kv_len are never read.
+// Ragged batches: with a per-sequence length array, workgroup (split, hkv, b)
+// clips its key range to its own sequence's length; splits wholly past it do
+// no work and write an empty partial (m = −∞, ℓ = λ = 0, Õ = 0), which the
+// merge weighs by 2^−∞ = 0. A sequence with no key gets O = 0 and
+// LSE = ln 0 = −∞ (the empty sums).
 #include "common.h"
 #include "launch.h"
 
@@ -84,9 +89,12 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, uint16_t *__restrict__ o, float *__restrict__ lse,
     int Hq, int Hkv, int G, int kv_len, int kv_cap, float scale_log2, int splits,
-    int split_keys, float *__restrict__ ws_ml, float *__restrict__ ws_part)
+    int split_keys, float *__restrict__ ws_ml, float *__restrict__ ws_part,
+    const int *__restrict__ kv_lens)
 {
     const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+    // ragged batch: this sequence's own length, clamped to [0, kv_len]
+    if (kv_lens) kv_len = min(max(kv_lens[b], 0), kv_len);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hcol = lane & 15, quad = lane >> 4;
     const int bh = b * Hkv + hkv;
@@ -219,17 +227,18 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
         float M = red_m[0][h];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red_m[w][h]);
+        const float Mu = M == -INFINITY ? 0.f : M;  // no key at all: every weight 0
         float acc = 0.f, l = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float f = exp2_fast(red_m[w][h] - M);  // idle wave: 2^-inf = 0
+            const float f = exp2_fast(red_m[w][h] - Mu);  // idle wave: 2^-inf = 0
             acc = fmaf(f, red_o[w][h][d], acc);
             l = fmaf(f, red_l[w][h], l);
         }
         const size_t row = (size_t)b * Hq + hkv * G + h;
         if (splits == 1) {
-            o[row * kD + d] = (uint16_t)(pack_bf16x2(acc / l, 0.f) & 0xffffu);
-            if (d == 0) lse[row] = (M + log2_fast(l)) * kLn2;
+            o[row * kD + d] = (uint16_t)(pack_bf16x2(l > 0.f ? acc / l : 0.f, 0.f) & 0xffffu);
+            if (d == 0) lse[row] = (M + log2_fast(l)) * kLn2;  // no key: −∞
         } else {
             const size_t slot = row * splits + split;
             ws_part[slot * kD + d] = acc;
@@ -263,7 +272,8 @@ bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p)
 
 hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, const void *v,
                              void *o, float *lse, int B, int Hq, int Hkv, int kv_len,
-                             int kv_cap, float scale, void *ws, hipStream_t st)
+                             int kv_cap, float scale, void *ws, hipStream_t st,
+                             const int *kv_lens)
 {
     char *w = (char *)ws;
     float *ws_ml = (float *)(w + p.ws_ml);
@@ -271,7 +281,8 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
     const dim3 grid(p.splits, Hkv, B), block(256);
     decode_gqa_kernel<<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, Hq,
-        Hkv, Hq / Hkv, kv_len, kv_cap, scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part);
+        Hkv, Hq / Hkv, kv_len, kv_cap, scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part,
+        kv_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, kD, st);

@@ -51,6 +51,11 @@
 // (non-temporal) stores that do not stay dirty in L2; the shared merge kernel
 // combines them through their log-sum-exp. Rows at or past kv_len are never
 // read.
+// Ragged batches: with a per-sequence length array, each workgroup clips its
+// key range to its own sequence's length (an empty split writes an empty
+// partial, weighted 0 by the merge; a sequence with no key gets O = 0 and
+// LSE = −∞), and the residual product is switched on per workgroup for
+// sequences of at most kLoMaxKeys keys.
 #include "common.h"
 #include "launch.h"
 
@@ -106,24 +111,29 @@ __device__ __forceinline__ void wait_tile(int ahead, bool hi_wave) {
     }
 }
 
-template <bool LO, bool FULL>  // FULL: every workgroup has all 8 head blocks
+// LOM: the weight residual product off (0), on (1), or on for sequences of
+// at most kLoMaxKeys keys (2); FULL: every workgroup has all 8 head blocks
+template <int LOM, bool FULL>
 __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ ckv,
     uint16_t *__restrict__ o, float *__restrict__ lse, int Hq, int kv_len, int kv_cap,
     float scale_log2, int splits, int split_keys, float *__restrict__ ws_ml,
-    float *__restrict__ ws_part)
+    float *__restrict__ ws_part, const int *__restrict__ kv_lens)
 {
     __shared__ __attribute__((aligned(1024))) char tile[MNBUF][MTILEB];
     // weights in B-operand order and per-head α (then λ)
     constexpr int NPB = 1;
     __shared__ __attribute__((aligned(16))) u32x4 p_hi[NPB][MHB][64];
-    __shared__ __attribute__((aligned(16))) u32x4 p_lo[LO ? MHB : 1][64];
+    __shared__ __attribute__((aligned(16))) u32x4 p_lo[LOM ? MHB : 1][64];
     __shared__ __attribute__((aligned(16))) float hinfo[NPB][16][MHB];
     // Q fragments of the last MKQ k-steps, each wave's own (registers are
     // all taken by the other Q fragments and the output)
     __shared__ __attribute__((aligned(16))) u32x4 q_lds[MKQ][MW][64];
 
     const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+    // ragged batch: this sequence's own length, clamped to [0, kv_len]
+    if (kv_lens) kv_len = min(max(kv_lens[b], 0), kv_len);
+    const bool lo_on = LOM == 1 || (LOM == 2 && kv_len <= kLoMaxKeys);  // wave-uniform
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hcol = lane & 15, quad = lane >> 4;
@@ -267,7 +277,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
             const uint32_t h = pack_bf16x2(p0, p1);
             phi[u] = h;
             l_o = sum_bf16x2(h, l_o);
-            if constexpr (LO) {
+            if (LOM != 0 && lo_on) {
                 // the residual p − bf16(p) is exact in fp32
                 const uint32_t w = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
                 plo[u] = w;
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         // B operand of head block `wave`: slots 0..3 ↔ keys 4·quad + e,
         // slots 4..7 ↔ keys 16 + 4·quad + e (the Sᵀ rows this lane holds)
         p_hi[pb][wave][lane] = phi;
-        if constexpr (LO) p_lo[wave][lane] = plo;
+        if (LOM != 0 && lo_on) p_lo[wave][lane] = plo;
         if (quad == 0) hinfo[pb][hcol][wave] = alpha;
     };
 
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
                 const bf16x8 bh = as<bf16x8>(p_hi[pb][hb][lane]);
 #pragma unroll
                 for (int db = 0; db < MDBW; ++db) oacc[db][hb] = mfma16x16x32(as<bf16x8>(va[db]), bh, oacc[db][hb]);
-                if constexpr (LO) {
+                if (LOM != 0 && lo_on) {
                     const bf16x8 bl = as<bf16x8>(p_lo[hb][lane]);
 #pragma unroll
                     for (int db = 0; db < MDBW; ++db) oacc[db][hb] = mfma16x16x32(as<bf16x8>(va[db]), bl, oacc[db][hb]);
@@ -325,7 +335,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         }
     };
 
-    const int n_t = (key_end - key_begin + MBC - 1) / MBC;
+    const int n_t = max(0, key_end - key_begin + MBC - 1) / MBC;  // 0: split past the end
     auto do_scores = [&](const char *tb, int t0, int pb, const uint16_t *cbase, int cbuf) __attribute__((always_inline)) {
         if (own) {
             if (t0 + MBC > key_end) scores(tb, t0, pb, cbase, cbuf, std::true_type{});
@@ -373,7 +383,8 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
 #pragma unroll
         for (int hb = 0; hb < MHB; ++hb) {
             if (hb >= nhb) break;
-            const float inv = 1.f / hinfo[0][hcol][hb];
+            const float lam = hinfo[0][hcol][hb];
+            const float inv = lam > 0.f ? 1.f / lam : 0.f;  // no key: O = 0
             uint16_t *orow = o + ((size_t)b * Hq + hg * MH + 16 * hb + hcol) * MV + MDW * wave + 4 * quad;
 #pragma unroll
             for (int db = 0; db < MDBW; ++db) {
@@ -421,18 +432,21 @@ bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p)
 
 hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, void *o,
                              float *lse, int B, int Hq, int kv_len, int kv_cap,
-                             float scale, void *ws, hipStream_t st)
+                             float scale, void *ws, hipStream_t st, const int *kv_lens)
 {
     char *w = (char *)ws;
     float *ws_ml = (float *)(w + p.ws_ml);
     float *ws_part = (float *)(w + p.ws_part);
     const dim3 grid(p.splits, (Hq + MH - 1) / MH, B);
     const bool full = Hq % MH == 0;
-    auto kern = kv_len <= kLoMaxKeys ? (full ? decode_mla_kernel<true, true> : decode_mla_kernel<true, false>)
-                                     : (full ? decode_mla_kernel<false, true> : decode_mla_kernel<false, false>);
+    // kv_len is the longest sequence; in a ragged batch shorter ones may need
+    // the residual product, decided per workgroup
+    auto kern = kv_len <= kLoMaxKeys ? (full ? decode_mla_kernel<1, true> : decode_mla_kernel<1, false>)
+              : kv_lens ? (full ? decode_mla_kernel<2, true> : decode_mla_kernel<2, false>)
+                        : (full ? decode_mla_kernel<0, true> : decode_mla_kernel<0, false>);
     kern<<<grid, dim3(MTHREADS), 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)ckv, (uint16_t *)o, lse, Hq, kv_len, kv_cap,
-        scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part);
+        scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part, kv_lens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, MV, st);

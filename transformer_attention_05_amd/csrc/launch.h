@@ -14,9 +14,12 @@ struct GqaPlan {
     size_t ws_ml, ws_part, ws_total;  // workspace byte offsets / size
 };
 bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p);
+// kv_lens: NULL (every sequence holds kv_len keys) or a device array of B
+// per-sequence lengths, each clamped to [0, kv_len] by the kernel.
 hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, const void *v,
                              void *o, float *lse, int B, int Hq, int Hkv, int kv_len,
-                             int kv_cap, float scale, void *ws, hipStream_t s);
+                             int kv_cap, float scale, void *ws, hipStream_t s,
+                             const int *kv_lens);
 
 // ---- causal prefill ------------------------------------------------------
 hipError_t launch_prefill_bf16(const void *q, const void *k, const void *v, void *o,
@@ -25,6 +28,12 @@ hipError_t launch_prefill_bf16(const void *q, const void *k, const void *v, void
 hipError_t launch_prefill_bf16_d128(const void *q, const void *k, const void *v, void *o,
                                     float *lse, int B, int Hq, int Hkv, int N, float scale,
                                     hipStream_t s);
+// N queries per sequence against caches of kv_cap slots filled to kv_lens[b]
+// (a device array, clamped to [N, kv_cap]); the queries are the last N
+// positions (bottom-right causal mask).
+hipError_t launch_prefill_chunked_d128(const void *q, const void *k, const void *v, void *o,
+                                       float *lse, const int *kv_lens, int B, int Hq, int Hkv,
+                                       int N, int kv_cap, float scale, hipStream_t s);
 hipError_t launch_prefill_f32(const float *q, const float *k, const float *v, float *o,
                               float *lse, int B, int Hq, int Hkv, int N, int D,
                               float scale, hipStream_t s);
@@ -35,9 +44,10 @@ struct MlaPlan {
     size_t ws_ml, ws_part, ws_total;
 };
 bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p);
+// kv_lens as for launch_decode_gqa (kv_len = the longest sequence).
 hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, void *o,
                              float *lse, int B, int Hq, int kv_len, int kv_cap,
-                             float scale, void *ws, hipStream_t s);
+                             float scale, void *ws, hipStream_t s, const int *kv_lens);
 
 // ---- split-K merge through the log-sum-exp (shared by both decodes) -------
 constexpr int kMaxSplits = 128;  // upper bound the planners respect

@@ -12,7 +12,8 @@
 // and the merge computes M = max_s m_s, w_s = 2^(m_s − M),
 // O = Σ_s w_s Õ_s / Σ_s w_s λ_s (rounded once to bf16) and
 // LSE = ln2 · (M + log2 Σ_s w_s ℓ_s). Splits are summed in index order, so
-// the result is deterministic.
+// the result is deterministic. An empty split (no key: m = −∞, sums 0) gets
+// weight 0; a row whose splits are all empty gets O = 0 and LSE = −∞.
 //
 // Layout: ml[row][split] = (m, ℓ, λ, unused) as float4, part[row][split][dv].
 // One 128-thread block per row; each thread reduces dv/128 channels over the
@@ -53,7 +54,8 @@ __global__ __launch_bounds__(128) void merge_kernel(
 #pragma unroll
         for (int u = 0; u < SPT; ++u)
             if (s0 + u < splits) Mn = fmaxf(Mn, st[u].x);
-        const float a = exp2_fast(M - Mn);  // first pass: 2^-inf = 0
+        const float Mu = Mn == -INFINITY ? 0.f : Mn;  // only empty splits so far
+        const float a = exp2_fast(M - Mu);  // first pass: 2^-inf = 0
         l *= a;
         lam *= a;
 #pragma unroll
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(128) void merge_kernel(
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
             // splits past the end were loaded from a clamped index: weight 0
-            const float w = s0 + u < splits ? exp2_fast(st[u].x - Mn) : 0.f;
+            const float w = s0 + u < splits ? exp2_fast(st[u].x - Mu) : 0.f;
             l = fmaf(w, st[u].y, l);
             lam = fmaf(w, st[u].z, lam);
 #pragma unroll
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(128) void merge_kernel(
         }
         M = Mn;
     }
-    const float inv = 1.f / lam;
+    const float inv = lam > 0.f ? 1.f / lam : 0.f;
     uint16_t *orow = o + (size_t)row * DV + CPT * t;
     if constexpr (CPT == 1) {
         orow[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);

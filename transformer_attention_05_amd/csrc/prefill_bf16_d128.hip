@@ -104,10 +104,16 @@ __device__ __forceinline__ uint32_t tile_src(int idx, int lane, int slots, int r
 }
 
 
+// N queries per (batch, head). CHUNK = false: K/V hold the same N positions
+// (rows of N slots). CHUNK = true: K/V are caches of kv_cap slots per (batch,
+// K/V head) filled to kv_lens[b], whose last N entries are the queries' own
+// positions, so query i sits at position kv_lens[b] − N + i.
+template <bool CHUNK>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
-    int Hq, int Hkv, int N, int n_qtiles, float scale_log2)
+    int Hq, int Hkv, int N, int n_qtiles, float scale_log2, int kv_cap,
+    const int *__restrict__ kv_lens)
 {
     __shared__ __attribute__((aligned(1024))) char kt[NBUF][KTILEB];
     __shared__ __attribute__((aligned(1024))) char vt[NBUF][VTILEB];
@@ -125,15 +131,24 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     const int hq = hkv * G + within % G;
     const int bhq = b * Hq + hq;
     const int q0 = qt * BR;
+    // keys of this sequence, their row stride, and the position of query 0
+    // (lengths outside [N, kv_cap] are clamped into it)
+    int kv_len = N, kv_stride = N, q_off = 0;
+    if constexpr (CHUNK) {
+        kv_len = min(max(kv_lens[b], N), kv_cap);
+        kv_stride = kv_cap;
+        q_off = kv_len - N;
+    }
 
     const uint16_t *Qp = q + (size_t)bhq * N * D;
-    const char *Kp = (const char *)(k + (size_t)grp * N * D);
-    const char *Vp = (const char *)(v + (size_t)grp * N * D);
+    const char *Kp = (const char *)(k + (size_t)grp * kv_stride * D);
+    const char *Vp = (const char *)(v + (size_t)grp * kv_stride * D);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int col = lane & 31, half = lane >> 5;
     const int qrow = q0 + wave * 32 + col;
+    const int qpos = qrow + q_off;  // the query's key position
     const int wrow0 = q0 + wave * 32, wrow1 = wrow0 + 31;
 
     // Q fragment (B operand of Sᵀ): query qrow, d = 16·ks + 8·half + 0..7
@@ -158,7 +173,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     };
     auto load_tile = [&](int j, int buf) {
         const char *kb = Kp + (size_t)j * BC * D * 2, *vb = Vp + (size_t)j * BC * D * 2;
-        const int rows = N - j * BC;  // valid rows of this tile
+        const int rows = kv_len - j * BC;  // valid rows of this tile
         if (rows >= BC) {
 #pragma unroll
             for (int t = 0; t < KLOADS / NW; ++t) issue(kb + ksrc[t], &kt[buf][1024 * (wave + NW * t)]);
@@ -192,7 +207,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     const int g = lane >> 4, e = (lane >> 2) & 3, cq = lane & 3;
     const int v_lane = (4 * half + e) * VROWB + 32 * (g & 1) + 8 * cq;
 
-    const int n_kt = min(N - 1, q0 + BR - 1) / BC + 1;
+    const int n_kt = min(kv_len - 1, q_off + q0 + BR - 1) / BC + 1;
 #pragma unroll
     for (int t = 0; t < NBUF - 1; ++t)
         if (t < n_kt) load_tile(t, t);
@@ -224,7 +239,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = kt0 + kb * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-                    if (key > qrow) sacc[kb][i] = -INFINITY;
+                    if (key > qpos) sacc[kb][i] = -INFINITY;
                 }
         }
         float mx = -INFINITY;
@@ -301,7 +316,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     // so the output registers stay put (where masked, unmasked and skipped
     // tiles meet in one loop, the compiler copies all 64 of them back and
     // forth every tile).
-    const int n_bulk = ATTN_PF_BULK && q0 + BR <= N ? q0 / BC : 0;
+    // (in a ragged last query tile the waves past the last query run the
+    // bulk tiles too; their rows are never written)
+    const int n_bulk = ATTN_PF_BULK ? (q_off + q0 + 1) / BC : 0;
     for (int j = 0; j < n_bulk; ++j) {
         const int cur = j % NBUF;
         const int jn = j + NBUF - 1;  // tile to prefetch
@@ -317,12 +334,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         if (jn < n_kt) load_tile(jn, jn % NBUF);
         const int kt0 = j * BC;
 #if ATTN_PF_SPLITMASK
-        if (wrow0 < N && kt0 + BC - 1 <= wrow0)          // wholly visible to the wave
+        if (wrow0 < N && kt0 + BC - 1 <= wrow0 + q_off)  // wholly visible to the wave
             tile_step(kt[cur], vt[cur], kt0, std::false_type{});
-        else if (wrow0 < N && kt0 <= wrow1)              // crosses the wave's diagonal
+        else if (wrow0 < N && kt0 <= wrow1 + q_off)      // crosses the wave's diagonal
             tile_step(kt[cur], vt[cur], kt0, std::true_type{});
 #else
-        if (wrow0 < N && kt0 <= wrow1) tile_step(kt[cur], vt[cur], kt0, std::true_type{});
+        if (wrow0 < N && kt0 <= wrow1 + q_off) tile_step(kt[cur], vt[cur], kt0, std::true_type{});
 #endif
         // tile j+1 resident before the barrier; newer prefetches may stay in flight
         if (NBUF == 3 && jn < n_kt) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
@@ -354,9 +371,21 @@ hipError_t launch_prefill_bf16_d128(const void *q, const void *k, const void *v,
 {
     const int n_qtiles = (N + BR - 1) / BR;
     const dim3 grid((unsigned)(n_qtiles * B * Hq)), block(64 * NW);
-    prefill_d128_kernel<<<grid, block, 0, st>>>((const uint16_t *)q, (const uint16_t *)k,
-                                                (const uint16_t *)v, (uint16_t *)o, lse, Hq, Hkv, N,
-                                                n_qtiles, scale * kLog2e);
+    prefill_d128_kernel<false><<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, Hq,
+        Hkv, N, n_qtiles, scale * kLog2e, N, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_chunked_d128(const void *q, const void *k, const void *v, void *o,
+                                       float *lse, const int *kv_lens, int B, int Hq, int Hkv,
+                                       int Nq, int kv_cap, float scale, hipStream_t st)
+{
+    const int n_qtiles = (Nq + BR - 1) / BR;
+    const dim3 grid((unsigned)(n_qtiles * B * Hq)), block(64 * NW);
+    prefill_d128_kernel<true><<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, Hq,
+        Hkv, Nq, n_qtiles, scale * kLog2e, kv_cap, kv_lens);
     return hipGetLastError();
 }
 
