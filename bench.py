@@ -127,30 +127,62 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
     cfg = workloads.WORKLOADS[name]
     w = workloads.make(name)
     kind = cfg["kind"]
+    ragged = getattr(w, "kv_lens", None) is not None and kind != "prefill_chunked"
+    if ragged:
+        lens = torch.from_numpy(w.kv_lens).to(dev)
     if kind == "decode_gqa":
         q, k, v = (_upload_bf16(torch, x, dev) for x in (w.q, w.k, w.v))
-        nbytes = workloads.decode_gqa_bytes(w.B, w.Hq, w.Hkv, w.kv_len, w.D)
+        if ragged:
+            nbytes = workloads.decode_gqa_ragged_bytes(w.Hq, w.Hkv, w.kv_lens, w.D)
+        else:
+            nbytes = workloads.decode_gqa_bytes(w.B, w.Hq, w.Hkv, w.kv_len, w.D)
         sets = [(q, k, v)] + [(q, k.clone(), v.clone()) for _ in range(_rotation(2 * k.numel() * 2) - 1)]
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
         ws = torch.empty(attn.attn_decode_gqa_workspace_bytes(w.B, w.Hq, w.Hkv, w.kv_len, w.D),
                          dtype=torch.uint8, device=dev)
-        calls = [lambda s=s: attn.attn_decode_gqa(s[0], s[1], s[2], w.kv_len, w.scale, out=o,
-                                                  lse=lse, ws=ws) for s in sets]
+        if ragged:
+            calls = [lambda s=s: attn.attn_decode_gqa_ragged(s[0], s[1], s[2], lens, w.kv_len,
+                                                             w.scale, out=o, lse=lse, ws=ws)
+                     for s in sets]
+        else:
+            calls = [lambda s=s: attn.attn_decode_gqa(s[0], s[1], s[2], w.kv_len, w.scale, out=o,
+                                                      lse=lse, ws=ws) for s in sets]
         work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
         kernel = "decode_gqa_kernel + merge_kernel"
     elif kind == "decode_mla":
         q, c = _upload_bf16(torch, w.q, dev), _upload_bf16(torch, w.ckv, dev)
-        nbytes = workloads.decode_mla_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv)
+        if ragged:
+            nbytes = workloads.decode_mla_ragged_bytes(w.Hq, w.kv_lens, w.Dqk, w.Dv)
+        else:
+            nbytes = workloads.decode_mla_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv)
         sets = [(q, c)] + [(q, c.clone()) for _ in range(_rotation(c.numel() * 2) - 1)]
         o = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
-        ws = torch.empty(attn.attn_decode_mla_workspace_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv),
-                         dtype=torch.uint8, device=dev)
-        calls = [lambda s=s: attn.attn_decode_mla_absorbed(s[0], s[1], w.kv_len, w.Dv, w.scale,
-                                                           out=o, lse=lse, ws=ws) for s in sets]
+        ws_fn = attn.attn_decode_mla_ragged_workspace_bytes if ragged else attn.attn_decode_mla_workspace_bytes
+        ws = torch.empty(ws_fn(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv), dtype=torch.uint8, device=dev)
+        if ragged:
+            calls = [lambda s=s: attn.attn_decode_mla_ragged(s[0], s[1], lens, w.kv_len, w.Dv,
+                                                             w.scale, out=o, lse=lse, ws=ws)
+                     for s in sets]
+        else:
+            calls = [lambda s=s: attn.attn_decode_mla_absorbed(s[0], s[1], w.kv_len, w.Dv, w.scale,
+                                                               out=o, lse=lse, ws=ws) for s in sets]
         work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
         kernel = "decode_mla_kernel + merge_kernel"
+    elif kind == "prefill_chunked":
+        q, k, v = (_upload_bf16(torch, x, dev) for x in (w.q, w.k, w.v))
+        lens = torch.from_numpy(w.kv_lens).to(dev)
+        flops = workloads.prefill_chunked_flops(w.Hq, w.Nq, w.kv_lens, w.D)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+        calls = [lambda: attn.attn_prefill_chunked(q, k, v, lens, w.scale, out=o, lse=lse)]
+        work, unit, peak, bound = flops / 1e12, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS, "mfma"
+        kernel = "prefill_d128_kernel<true>"
+        nsteps = max(5, min(steps, int(1e14 // max(flops, 1))))
+        if nsteps >= 20:
+            nsteps -= nsteps % 20
+        steps, warmup = nsteps, max(min(warmup, 5), min(200, int(2e13 // max(flops, 1))))
     else:
         up = _upload_bf16 if w.dtype == "bf16" else _upload_f32
         q, k, v = (up(torch, x, dev) for x in (w.q, w.k, w.v))
@@ -162,7 +194,7 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
         unit = "TFLOP/s"
         if w.dtype == "bf16":
             peak, bound = MFMA_BF16_PEAK_TFLOPS, "mfma"
-            kernel = "prefill_d128_kernel" if w.D == 128 else "prefill_bf16_kernel"
+            kernel = "prefill_d128_kernel<false>" if w.D == 128 else "prefill_bf16_kernel"
         else:
             peak, bound, kernel = FP32_VALU_PEAK_TFLOPS, "alu", "prefill_f32_kernel"
         # about 0.1 s of timed work after about 20 ms of warm-up (the clocks

@@ -214,10 +214,14 @@ size_t attn_decode_mla_workspace_bytes(int B, int Hq, int kv_len, int Dqk,
 
 /*
  * Absorbed MLA decode of a ragged batch: as attn_decode_mla_absorbed, with
- * sequence b's latent cache filled to kv_lens[b] (DEVICE int32 [B], clamped
- * to [0, max_kv_len]; length 0 gives O = 0, LSE = −∞). max_kv_len fixes the
- * split and the workspace, attn_decode_mla_workspace_bytes(B, Hq,
- * max_kv_len, Dqk, Dv).
+ * sequence b's latent cache filled to kv_lens[b] (DEVICE int32 [B], read at
+ * run time, clamped to [0, max_kv_len]; length 0 gives O = 0, LSE = −∞).
+ * The work is split evenly over the 32-key tiles of all sequences together
+ * (one workgroup per compute unit, each taking an equal run of tiles, across
+ * sequence boundaries), so short and long sequences in one batch keep the
+ * whole GPU busy; the split is recomputed on the device from kv_lens on
+ * every call. max_kv_len (the longest length, or a bound of it, at most
+ * kv_cap) bounds the lengths. Workspace: attn_decode_mla_ragged_workspace_bytes().
  * Errors as for attn_decode_mla_absorbed with max_kv_len in the place of
  * kv_len; kv_lens NULL → ATTN_ERR_NULL_POINTER.
  */
@@ -227,6 +231,10 @@ attn_status attn_decode_mla_ragged(const void *q, const void *ckv, void *o,
                                    int Dqk, int Dv, float scale,
                                    void *workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* Bytes of workspace attn_decode_mla_ragged needs (0 if invalid). */
+size_t attn_decode_mla_ragged_workspace_bytes(int B, int Hq, int max_kv_len,
+                                              int Dqk, int Dv);
 
 /* Static, human-readable name of a status code. */
 const char *attn_status_string(attn_status s);

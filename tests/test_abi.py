@@ -29,7 +29,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -154,7 +154,8 @@ def test_ragged_decode_validation(lib):
     assert _mla_r(lib, lens=None) == NULLP
     assert _mla_r(lib, max_len=1025) == SHAPE
     assert _mla_r(lib, Hq=20) == UNSUP
-    need = attn.attn_decode_mla_workspace_bytes(2, 128, 1000)
+    need = attn.attn_decode_mla_ragged_workspace_bytes(2, 128, 1000)
+    assert need > 0 and attn.attn_decode_mla_ragged_workspace_bytes(2, 120, 1000) == 0
     assert _mla_r(lib, ws_bytes=need - 1) == WS
     for s in BAD_SCALES:
         assert _gqa_r(lib, scale=s) == SHAPE and _mla_r(lib, scale=s) == SHAPE

@@ -61,8 +61,10 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_mla_ragged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.attn_decode_mla_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.attn_decode_mla_ragged_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.attn_decode_gqa_workspace_bytes.restype = sz
         lib.attn_decode_mla_workspace_bytes.restype = sz
+        lib.attn_decode_mla_ragged_workspace_bytes.restype = sz
         for fn in (lib.attn_prefill_causal, lib.attn_decode_gqa, lib.attn_decode_mla_absorbed,
                    lib.attn_prefill_chunked, lib.attn_decode_gqa_ragged,
                    lib.attn_decode_mla_ragged):
@@ -175,6 +177,10 @@ def attn_decode_mla_workspace_bytes(B, Hq, kv_len, Dqk=576, Dv=512) -> int:
     return int(load().attn_decode_mla_workspace_bytes(B, Hq, kv_len, Dqk, Dv))
 
 
+def attn_decode_mla_ragged_workspace_bytes(B, Hq, max_kv_len, Dqk=576, Dv=512) -> int:
+    return int(load().attn_decode_mla_ragged_workspace_bytes(B, Hq, max_kv_len, Dqk, Dv))
+
+
 def attn_decode_mla_absorbed(q, ckv, kv_len, dv=512, scale=None, out=None, lse=None, ws=None):
     """Absorbed MLA decode. q [B,Hq,Dqk] bf16 (absorbed, channel-balanced
     query | rope), ckv [B,kv_cap,Dqk] bf16 (balanced latent | rope). Value =
@@ -284,7 +290,7 @@ def attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, dv=512, scale=None, out=
     l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
     _need(o, "out", torch.bfloat16, 3)
     _need(l, "lse", torch.float32, 2)
-    need = lib.attn_decode_mla_workspace_bytes(B, Hq, int(max_kv_len), Dqk, dv)
+    need = lib.attn_decode_mla_ragged_workspace_bytes(B, Hq, int(max_kv_len), Dqk, dv)
     w = workspace(need, q.device) if ws is None else ws
     st = lib.attn_decode_mla_ragged(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), _ptr(kv_lens), B, Hq,
                                     int(max_kv_len), kv_cap, Dqk, dv, float(scale), _ptr(w),

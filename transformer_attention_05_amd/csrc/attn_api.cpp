@@ -98,7 +98,10 @@ attn_status decode_mla_impl(const char *fn, const void *q, const void *ckv, void
     if (!aligned16(q) || !aligned16(ckv) || !aligned16(o) || !aligned4(lse) || !aligned4(kv_lens))
         return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned (lse, kv_lens: 4)", fn);
     attn::MlaPlan p;
-    attn::mla_plan(B, Hq, kv_len, &p);
+    if (kv_lens)
+        attn::mla_ragged_plan(B, Hq, kv_len, &p);
+    else
+        attn::mla_plan(B, Hq, kv_len, &p);
     if (!workspace || workspace_bytes < p.ws_total || !aligned16(workspace))
         return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, p.ws_total,
                     workspace ? workspace_bytes : (size_t)0);
@@ -227,6 +230,13 @@ attn_status attn_decode_mla_absorbed(const void *q, const void *ckv, void *o, fl
         return fail(ATTN_ERR_NULL_POINTER, "attn_decode_mla_absorbed: NULL tensor pointer");
     return decode_mla_impl("attn_decode_mla_absorbed", q, ckv, o, lse, nullptr, B, Hq, kv_len,
                            kv_cap, Dqk, Dv, scale, workspace, workspace_bytes, stream);
+}
+
+size_t attn_decode_mla_ragged_workspace_bytes(int B, int Hq, int max_kv_len, int Dqk, int Dv)
+{
+    attn::MlaPlan p;
+    if (Dqk != 576 || Dv != 512 || !attn::mla_ragged_plan(B, Hq, max_kv_len, &p)) return 0;
+    return p.ws_total;
 }
 
 attn_status attn_decode_mla_ragged(const void *q, const void *ckv, void *o, float *lse,

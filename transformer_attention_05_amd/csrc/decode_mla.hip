@@ -51,13 +51,16 @@
 // (non-temporal) stores that do not stay dirty in L2; the shared merge kernel
 // combines them through their log-sum-exp. Rows at or past kv_len are never
 // read.
-// Ragged batches: with a per-sequence length array, each workgroup clips its
-// key range to its own sequence's length (an empty split writes an empty
-// partial, weighted 0 by the merge; a sequence with no key gets O = 0 and
-// LSE = −∞), and the residual product is switched on per workgroup for
-// sequences of at most kLoMaxKeys keys.
+// Ragged batches (per-sequence lengths in device memory): one workgroup per
+// CU, each taking an equal run of the 32-key tiles of all sequences in batch
+// order (ragged.h), so a mix of short and long sequences keeps every CU
+// busy; a run that crosses sequence boundaries produces one partial per
+// sequence, and the merge finds a row's partials from the same arithmetic.
+// The residual product is switched on per segment for sequences of at most
+// kLoMaxKeys keys. A sequence with no key gets O = 0 and LSE = −∞.
 #include "common.h"
 #include "launch.h"
+#include "ragged.h"
 
 #include <type_traits>
 
@@ -112,13 +115,19 @@ __device__ __forceinline__ void wait_tile(int ahead, bool hi_wave) {
 }
 
 // LOM: the weight residual product off (0), on (1), or on for sequences of
-// at most kLoMaxKeys keys (2); FULL: every workgroup has all 8 head blocks
-template <int LOM, bool FULL>
+// at most kLoMaxKeys keys (2); FULL: every workgroup has all 8 head blocks.
+// SK = false: workgroup (split, hg, b) takes keys [split·split_keys, ...) of
+// sequence b, every sequence holding kv_len keys. SK = true (ragged batch,
+// grid (splits, hg, 1)): workgroup `split` is worker w of the balanced split
+// of ragged.h over the tiles of all B sequences (lengths kv_lens[b], at most
+// kv_len); it walks its run one sequence segment at a time and writes each
+// segment's partial to slot w + b.
+template <int LOM, bool FULL, bool SK>
 __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ ckv,
     uint16_t *__restrict__ o, float *__restrict__ lse, int Hq, int kv_len, int kv_cap,
     float scale_log2, int splits, int split_keys, float *__restrict__ ws_ml,
-    float *__restrict__ ws_part, const int *__restrict__ kv_lens)
+    float *__restrict__ ws_part, const int *__restrict__ kv_lens, int B)
 {
     __shared__ __attribute__((aligned(1024))) char tile[MNBUF][MTILEB];
     // weights in B-operand order and per-head α (then λ)
@@ -130,10 +139,8 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     // all taken by the other Q fragments and the output)
     __shared__ __attribute__((aligned(16))) u32x4 q_lds[MKQ][MW][64];
 
-    const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
-    // ragged batch: this sequence's own length, clamped to [0, kv_len]
-    if (kv_lens) kv_len = min(max(kv_lens[b], 0), kv_len);
-    const bool lo_on = LOM == 1 || (LOM == 2 && kv_len <= kLoMaxKeys);  // wave-uniform
+    const int split = blockIdx.x, hg = blockIdx.y;
+    int b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hcol = lane & 15, quad = lane >> 4;
@@ -141,8 +148,30 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const bool own = wave < nhb;                     // this wave scores heads 16·wave ..
     const int head = hg * MH + wave * 16 + hcol;     // its score head
     const bool hi_wave = wave < MLOADS % MW;
-    const int key_begin = split * split_keys;
-    const int key_end = min(kv_len, key_begin + split_keys);
+
+    // SK: this worker's run of tiles [run_t, run_end) and the first tile of
+    // the sequence it starts in
+    int run_t = 0, run_end = 0, seq_first = 0;
+    if constexpr (SK) {
+        const int T = ragged_total(kv_lens, B, kv_len, MBC);
+        const int P_eff = min(splits, T);
+        if (split >= P_eff) return;                  // more workers than tiles
+        run_t = ragged_run_begin(split, T, P_eff);
+        run_end = ragged_run_begin(split + 1, T, P_eff);
+        ragged_locate(kv_lens, B, kv_len, MBC, run_t, b, seq_first);
+    }
+    for (;;) {  // SK: one pass per sequence segment of the run; otherwise one pass
+    int seq_len, key_begin, key_end;
+    if constexpr (SK) {
+        seq_len = ragged_len(kv_lens, b, kv_len);
+        key_begin = (run_t - seq_first) * MBC;
+        key_end = min(seq_len, (run_end - seq_first) * MBC);
+    } else {
+        seq_len = kv_len;
+        key_begin = split * split_keys;
+        key_end = min(kv_len, key_begin + split_keys);
+    }
+    const bool lo_on = LOM == 1 || (LOM == 2 && seq_len <= kLoMaxKeys);  // wave-uniform
     const uint16_t *cb = ckv + (size_t)b * kv_cap * MD;
 
     bf16x8 qf[MKR];
@@ -372,7 +401,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     l_e += shfl_xor(l_e, 32);
     l_o += shfl_xor(l_o, 16);
     l_o += shfl_xor(l_o, 32);
-    if (splits == 1) {
+    if (!SK && splits == 1) {
         // every wave needs λ of every head: pass it through LDS
         __syncthreads();
         if (own && quad == 0) {
@@ -395,16 +424,27 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         }
         return;
     }
+    // partial records: [row][split] for the uniform split, [slot][row of
+    // the batch's heads] (slot = w + b) for the balanced one
+    auto rec = [&](int h) __attribute__((always_inline)) {
+        return SK ? (size_t)(split + b) * Hq + h : ((size_t)b * Hq + h) * splits + split;
+    };
     if (own && quad == 0)
-        *(float4 *)(ws_ml + 4 * (((size_t)b * Hq + head) * splits + split)) =
-            make_float4(m_ref, l_e, l_o, 0.f);
+        *(float4 *)(ws_ml + 4 * rec(head)) = make_float4(m_ref, l_e, l_o, 0.f);
 #pragma unroll
     for (int hb = 0; hb < MHB; ++hb) {
         if (hb >= nhb) break;
-        const size_t slot = ((size_t)b * Hq + hg * MH + 16 * hb + hcol) * splits + split;
-        float *prow = ws_part + slot * MV + MDW * wave + 4 * quad;
+        float *prow = ws_part + rec(hg * MH + 16 * hb + hcol) * MV + MDW * wave + 4 * quad;
 #pragma unroll
         for (int db = 0; db < MDBW; ++db) __builtin_nontemporal_store(oacc[db][hb], (f32x4 *)(prow + 16 * db));
+    }
+    if constexpr (!SK) break;
+    // next segment: the next sequence with keys, if the run goes on
+    run_t = min(run_end, seq_first + (seq_len + MBC - 1) / MBC);
+    if (run_t >= run_end) break;
+    seq_first = run_t;
+    do ++b; while (ragged_len(kv_lens, b, kv_len) == 0);
+    __syncthreads();  // the last tile and weights of this segment are no longer read
     }
 }
 
@@ -430,6 +470,22 @@ bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p)
     return true;
 }
 
+bool mla_ragged_plan(int B, int Hq, int max_len, MlaPlan *p)
+{
+    if (B < 1 || Hq < 16 || Hq % 16 || max_len < 1) return false;
+    const long hgs = (Hq + MH - 1) / MH;
+    const long tiles_max = (long)B * ((max_len + MBC - 1) / MBC);
+    long P = (kTargetGroups + hgs - 1) / hgs;        // workers per head group
+    if (P > tiles_max) P = tiles_max;
+    p->splits = (int)P;
+    p->split_keys = 0;
+    const size_t recs = (size_t)(P + B) * Hq;        // slots w + b, all heads
+    p->ws_ml = 0;
+    p->ws_part = align_up(sizeof(float) * 4 * recs, 256);
+    p->ws_total = p->ws_part + align_up(sizeof(float) * MV * recs, 256);
+    return true;
+}
+
 hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, void *o,
                              float *lse, int B, int Hq, int kv_len, int kv_cap,
                              float scale, void *ws, hipStream_t st, const int *kv_lens)
@@ -437,16 +493,30 @@ hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, v
     char *w = (char *)ws;
     float *ws_ml = (float *)(w + p.ws_ml);
     float *ws_part = (float *)(w + p.ws_part);
-    const dim3 grid(p.splits, (Hq + MH - 1) / MH, B);
+    const int hgs = (Hq + MH - 1) / MH;
     const bool full = Hq % MH == 0;
-    // kv_len is the longest sequence; in a ragged batch shorter ones may need
-    // the residual product, decided per workgroup
-    auto kern = kv_len <= kLoMaxKeys ? (full ? decode_mla_kernel<1, true> : decode_mla_kernel<1, false>)
-              : kv_lens ? (full ? decode_mla_kernel<2, true> : decode_mla_kernel<2, false>)
-                        : (full ? decode_mla_kernel<0, true> : decode_mla_kernel<0, false>);
+    if (kv_lens) {
+        // ragged: balanced split over the tiles of all sequences (kv_len is
+        // the longest); short sequences switch the residual product on
+        const dim3 grid(p.splits, hgs, 1);
+        auto kern = kv_len <= kLoMaxKeys
+                        ? (full ? decode_mla_kernel<1, true, true> : decode_mla_kernel<1, false, true>)
+                        : (full ? decode_mla_kernel<2, true, true> : decode_mla_kernel<2, false, true>);
+        kern<<<grid, dim3(MTHREADS), 0, st>>>(
+            (const uint16_t *)q, (const uint16_t *)ckv, (uint16_t *)o, lse, Hq, kv_len, kv_cap,
+            scale * kLog2e, p.splits, 0, ws_ml, ws_part, kv_lens, B);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_merge_ragged(ws_ml, ws_part, o, lse, kv_lens, B, Hq, kv_len, p.splits, MBC,
+                                   MV, st);
+    }
+    const dim3 grid(p.splits, hgs, B);
+    auto kern = kv_len <= kLoMaxKeys
+                    ? (full ? decode_mla_kernel<1, true, false> : decode_mla_kernel<1, false, false>)
+                    : (full ? decode_mla_kernel<0, true, false> : decode_mla_kernel<0, false, false>);
     kern<<<grid, dim3(MTHREADS), 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)ckv, (uint16_t *)o, lse, Hq, kv_len, kv_cap,
-        scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part, kv_lens);
+        scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part, nullptr, B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, MV, st);

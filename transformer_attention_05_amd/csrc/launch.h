@@ -44,7 +44,10 @@ struct MlaPlan {
     size_t ws_ml, ws_part, ws_total;
 };
 bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p);
-// kv_lens as for launch_decode_gqa (kv_len = the longest sequence).
+// ragged batch: splits = workers per head group of the balanced split
+bool mla_ragged_plan(int B, int Hq, int max_len, MlaPlan *p);
+// kv_lens: NULL, or a device array of B lengths (plan from mla_ragged_plan,
+// kv_len = the longest sequence).
 hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, void *o,
                              float *lse, int B, int Hq, int kv_len, int kv_cap,
                              float scale, void *ws, hipStream_t s, const int *kv_lens);
@@ -55,6 +58,13 @@ constexpr int kMaxSplits = 128;  // upper bound the planners respect
 // λ normalises O); part [rows][splits][dv] fp32.
 hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse, int rows,
                         int splits, int dv, hipStream_t s);
+// The merge of the balanced split of a ragged batch (ragged.h): records
+// [slot][row of the batch's Hq heads], slot = worker + sequence, `workers`
+// workers over tiles of `tile` keys of sequences of length kv_lens[b] (at
+// most max_len). A sequence with no key gets O = 0, LSE = −∞.
+hipError_t launch_merge_ragged(const float *ml, const float *part, void *o, float *lse,
+                               const int *kv_lens, int B, int Hq, int max_len, int workers,
+                               int tile, int dv, hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

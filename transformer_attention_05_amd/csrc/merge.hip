@@ -15,24 +15,27 @@
 // the result is deterministic. An empty split (no key: m = −∞, sums 0) gets
 // weight 0; a row whose splits are all empty gets O = 0 and LSE = −∞.
 //
-// Layout: ml[row][split] = (m, ℓ, λ, unused) as float4, part[row][split][dv].
+// Layout: ml[row][split] = (m, ℓ, λ, unused) as float4, part[row][split][dv];
+// for the balanced split of a ragged batch (ragged.h), ml[slot][row] and
+// part[slot][row][dv] with slot = worker + sequence.
 // One 128-thread block per row; each thread reduces dv/128 channels over the
 // splits, with the loads of up to 16 splits in flight at once.
 #include "common.h"
 #include "launch.h"
+#include "ragged.h"
 
 namespace attn {
 namespace {
 
-template <int CPT, int SPT>  // channels per thread (dv / 128), split slots per pass
-__global__ __launch_bounds__(128) void merge_kernel(
-    const float *__restrict__ ml, const float *__restrict__ part, uint16_t *__restrict__ o,
-    float *__restrict__ lse, int splits)
+// Merge `splits` partial records of one row: record s at ml4[s·mstride]
+// (float4) and pr[s·pstride + ...] (dv floats); thread t owns channels
+// CPT·t .. CPT·t + CPT − 1.
+template <int CPT, int SPT>
+__device__ __forceinline__ void merge_row(const float4 *__restrict__ mr, size_t mstride,
+                                          const float *__restrict__ pr, size_t pstride, int splits,
+                                          uint16_t *__restrict__ orow, float *__restrict__ lse_out,
+                                          int t)
 {
-    constexpr int DV = 128 * CPT;
-    const int row = blockIdx.x, t = threadIdx.x;
-    const float4 *mr = (const float4 *)(ml + (size_t)row * splits * 4);
-    const float *pr = part + (size_t)row * splits * DV + CPT * t;
     // splits are taken SPT at a time with every load of a pass in flight at
     // once (one memory round trip when splits <= SPT); across passes the
     // running max grows and earlier sums are rescaled, like the online
@@ -46,9 +49,9 @@ __global__ __launch_bounds__(128) void merge_kernel(
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
             const int s = min(s0 + u, splits - 1);
-            st[u] = mr[s];
+            st[u] = mr[(size_t)s * mstride];
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) x[u][c] = pr[(size_t)s * DV + c];
+            for (int c = 0; c < CPT; ++c) x[u][c] = pr[(size_t)s * pstride + c];
         }
         float Mn = M;
 #pragma unroll
@@ -72,14 +75,63 @@ __global__ __launch_bounds__(128) void merge_kernel(
         M = Mn;
     }
     const float inv = lam > 0.f ? 1.f / lam : 0.f;
-    uint16_t *orow = o + (size_t)row * DV + CPT * t;
     if constexpr (CPT == 1) {
         orow[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
     } else {
 #pragma unroll
         for (int c = 0; c < CPT; c += 2) *(uint32_t *)(orow + c) = pack_bf16x2(acc[c] * inv, acc[c + 1] * inv);
     }
-    if (t == 0) lse[row] = (M + log2_fast(l)) * kLn2;
+    if (t == 0) *lse_out = (M + log2_fast(l)) * kLn2;
+}
+
+template <int CPT, int SPT>  // channels per thread (dv / 128), split slots per pass
+__global__ __launch_bounds__(128) void merge_kernel(
+    const float *__restrict__ ml, const float *__restrict__ part, uint16_t *__restrict__ o,
+    float *__restrict__ lse, int splits)
+{
+    constexpr int DV = 128 * CPT;
+    const int row = blockIdx.x, t = threadIdx.x;
+    merge_row<CPT, SPT>((const float4 *)(ml + (size_t)row * splits * 4), 1,
+                        part + (size_t)row * splits * DV + CPT * t, DV, splits,
+                        o + (size_t)row * DV + CPT * t, lse + row, t);
+}
+
+// Ragged batch, balanced split: row (b, h) gathers the records of the
+// workers whose runs overlap sequence b (slots w + b, consecutive).
+template <int CPT, int SPT>
+__global__ __launch_bounds__(128) void merge_ragged_kernel(
+    const float *__restrict__ ml, const float *__restrict__ part, uint16_t *__restrict__ o,
+    float *__restrict__ lse, const int *__restrict__ kv_lens, int B, int Hq, int max_len,
+    int workers, int tile)
+{
+    constexpr int DV = 128 * CPT;
+    const int row = blockIdx.x, t = threadIdx.x;
+    const int b = row / Hq, h = row % Hq;
+    const int n = (ragged_len(kv_lens, b, max_len) + tile - 1) / tile;
+    uint16_t *orow = o + (size_t)row * DV + CPT * t;
+    if (n == 0) {  // no key: empty sums
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) orow[c] = 0;
+        if (t == 0) lse[row] = -INFINITY;
+        return;
+    }
+    const int T = ragged_total(kv_lens, B, max_len, tile);
+    // first tile of sequence b = tiles of sequences 0 .. b−1
+    int first = 0;
+    {
+        const int lane = __lane_id();
+        for (int c = 0; c < b; c += 64) {
+            int m = c + lane < b ? (ragged_len(kv_lens, c + lane, max_len) + tile - 1) / tile : 0;
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) m += __shfl_xor(m, d);
+            first += m;
+        }
+    }
+    const int P_eff = min(workers, T);
+    const int w0 = ragged_owner(first, T, P_eff), w1 = ragged_owner(first + n - 1, T, P_eff);
+    const size_t slot0 = (size_t)(w0 + b) * Hq + h;
+    merge_row<CPT, SPT>((const float4 *)ml + slot0, (size_t)Hq, part + slot0 * DV + CPT * t,
+                        (size_t)Hq * DV, w1 - w0 + 1, orow, lse + row, t);
 }
 
 }  // namespace
@@ -93,6 +145,22 @@ hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse,
         merge_kernel<1, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
     else if (dv == 512)
         merge_kernel<4, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_ragged(const float *ml, const float *part, void *o, float *lse,
+                               const int *kv_lens, int B, int Hq, int max_len, int workers,
+                               int tile, int dv, hipStream_t st)
+{
+    const dim3 grid((unsigned)(B * Hq)), block(128);
+    if (dv == 128)
+        merge_ragged_kernel<1, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, kv_lens, B,
+                                                           Hq, max_len, workers, tile);
+    else if (dv == 512)
+        merge_ragged_kernel<4, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, kv_lens, B,
+                                                           Hq, max_len, workers, tile);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
