@@ -135,7 +135,8 @@ def test_decode_gqa_ragged_8k_workload(gpu):
     (16, [0, 1, 100, 512, 513, 2000], 2000, 2000),   # short rows take the residual product
     (128, [3, 40, 600], 600, 640),
     (32, [0, 200, 512], 512, 520),                   # every row short
-    (144, [70, 1], 100, 100)])
+    (144, [70, 1], 100, 100),
+    (16, [int(x) for x in workloads.ragged_lengths(70, 0, 700, 7)], 700, 700)])  # > 64 sequences
 def test_decode_mla_ragged_matches_oracle(gpu, Hq, lens, max_len, kv_cap):
     B = len(lens)
     w = workloads.gen_decode_mla(B, Hq, kv_cap=kv_cap, kv_lens=lens, seed=B + Hq)

@@ -118,10 +118,10 @@ __device__ __forceinline__ void wait_tile(int ahead, bool hi_wave) {
 // at most kLoMaxKeys keys (2); FULL: every workgroup has all 8 head blocks.
 // SK = false: workgroup (split, hg, b) takes keys [split·split_keys, ...) of
 // sequence b, every sequence holding kv_len keys. SK = true (ragged batch,
-// grid (splits, hg, 1)): workgroup `split` is worker w of the balanced split
-// of ragged.h over the tiles of all B sequences (lengths kv_lens[b], at most
-// kv_len); it walks its run one sequence segment at a time and writes each
-// segment's partial to slot w + b.
+// grid (splits + B, hg, 1)): workgroup j takes piece j of the balanced split
+// of ragged.h with `splits` workers over the tiles of all B sequences
+// (lengths kv_lens[b], at most kv_len) — one worker's run within one
+// sequence — and writes its partial to slot j.
 template <int LOM, bool FULL, bool SK>
 __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ ckv,
@@ -148,24 +148,12 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const bool own = wave < nhb;                     // this wave scores heads 16·wave ..
     const int head = hg * MH + wave * 16 + hcol;     // its score head
     const bool hi_wave = wave < MLOADS % MW;
-
-    // SK: this worker's run of tiles [run_t, run_end) and the first tile of
-    // the sequence it starts in
-    int run_t = 0, run_end = 0, seq_first = 0;
-    if constexpr (SK) {
-        const int T = ragged_total(kv_lens, B, kv_len, MBC);
-        const int P_eff = min(splits, T);
-        if (split >= P_eff) return;                  // more workers than tiles
-        run_t = ragged_run_begin(split, T, P_eff);
-        run_end = ragged_run_begin(split + 1, T, P_eff);
-        ragged_locate(kv_lens, B, kv_len, MBC, run_t, b, seq_first);
-    }
-    for (;;) {  // SK: one pass per sequence segment of the run; otherwise one pass
     int seq_len, key_begin, key_end;
     if constexpr (SK) {
-        seq_len = ragged_len(kv_lens, b, kv_len);
-        key_begin = (run_t - seq_first) * MBC;
-        key_end = min(seq_len, (run_end - seq_first) * MBC);
+        int t0, t1;
+        if (!ragged_piece(kv_lens, B, kv_len, MBC, splits, split, b, seq_len, t0, t1)) return;
+        key_begin = t0 * MBC;
+        key_end = min(seq_len, t1 * MBC);
     } else {
         seq_len = kv_len;
         key_begin = split * split_keys;
@@ -425,9 +413,9 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         return;
     }
     // partial records: [row][split] for the uniform split, [slot][row of
-    // the batch's heads] (slot = w + b) for the balanced one
+    // the batch's heads] (slot = piece = w + b) for the balanced one
     auto rec = [&](int h) __attribute__((always_inline)) {
-        return SK ? (size_t)(split + b) * Hq + h : ((size_t)b * Hq + h) * splits + split;
+        return SK ? (size_t)split * Hq + h : ((size_t)b * Hq + h) * splits + split;
     };
     if (own && quad == 0)
         *(float4 *)(ws_ml + 4 * rec(head)) = make_float4(m_ref, l_e, l_o, 0.f);
@@ -437,14 +425,6 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         float *prow = ws_part + rec(hg * MH + 16 * hb + hcol) * MV + MDW * wave + 4 * quad;
 #pragma unroll
         for (int db = 0; db < MDBW; ++db) __builtin_nontemporal_store(oacc[db][hb], (f32x4 *)(prow + 16 * db));
-    }
-    if constexpr (!SK) break;
-    // next segment: the next sequence with keys, if the run goes on
-    run_t = min(run_end, seq_first + (seq_len + MBC - 1) / MBC);
-    if (run_t >= run_end) break;
-    seq_first = run_t;
-    do ++b; while (ragged_len(kv_lens, b, kv_len) == 0);
-    __syncthreads();  // the last tile and weights of this segment are no longer read
     }
 }
 
@@ -475,7 +455,11 @@ bool mla_ragged_plan(int B, int Hq, int max_len, MlaPlan *p)
     if (B < 1 || Hq < 16 || Hq % 16 || max_len < 1) return false;
     const long hgs = (Hq + MH - 1) / MH;
     const long tiles_max = (long)B * ((max_len + MBC - 1) / MBC);
-    long P = (kTargetGroups + hgs - 1) / hgs;        // workers per head group
+    // workers per head group: the P + B pieces (one workgroup each, one
+    // workgroup per CU) should all run at once, or the last pieces, each
+    // nearly a whole run, would start only when the first ones end
+    long P = (kTargetGroups + hgs - 1) / hgs - B;
+    if (P < 16) P = 16;
     if (P > tiles_max) P = tiles_max;
     p->splits = (int)P;
     p->split_keys = 0;
@@ -498,7 +482,7 @@ hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, v
     if (kv_lens) {
         // ragged: balanced split over the tiles of all sequences (kv_len is
         // the longest); short sequences switch the residual product on
-        const dim3 grid(p.splits, hgs, 1);
+        const dim3 grid(p.splits + B, hgs, 1);  // one workgroup per slot (piece)
         auto kern = kv_len <= kLoMaxKeys
                         ? (full ? decode_mla_kernel<1, true, true> : decode_mla_kernel<1, false, true>)
                         : (full ? decode_mla_kernel<2, true, true> : decode_mla_kernel<2, false, true>);

@@ -115,16 +115,20 @@ __global__ __launch_bounds__(128) void merge_ragged_kernel(
         if (t == 0) lse[row] = -INFINITY;
         return;
     }
-    const int T = ragged_total(kv_lens, B, max_len, tile);
-    // first tile of sequence b = tiles of sequences 0 .. b−1
-    int first = 0;
+    // one pass over the lengths: all tiles (T) and those before sequence b
+    int T = 0, first = 0;
     {
         const int lane = __lane_id();
-        for (int c = 0; c < b; c += 64) {
-            int m = c + lane < b ? (ragged_len(kv_lens, c + lane, max_len) + tile - 1) / tile : 0;
+        for (int c = 0; c < B; c += 64) {
+            const int m = c + lane < B ? (ragged_len(kv_lens, c + lane, max_len) + tile - 1) / tile : 0;
+            int all = m, before = c + lane < b ? m : 0;
 #pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) m += __shfl_xor(m, d);
-            first += m;
+            for (int d = 32; d >= 1; d >>= 1) {
+                all += __shfl_xor(all, d);
+                before += __shfl_xor(before, d);
+            }
+            T += all;
+            first += before;
         }
     }
     const int P_eff = min(workers, T);
@@ -155,12 +159,14 @@ hipError_t launch_merge_ragged(const float *ml, const float *part, void *o, floa
                                int tile, int dv, hipStream_t st)
 {
     const dim3 grid((unsigned)(B * Hq)), block(128);
+    // a row of a ragged batch has few records (its sequence's share of
+    // the workers, plus one): passes of 4
     if (dv == 128)
-        merge_ragged_kernel<1, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, kv_lens, B,
-                                                           Hq, max_len, workers, tile);
+        merge_ragged_kernel<1, 4><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, kv_lens, B,
+                                                          Hq, max_len, workers, tile);
     else if (dv == 512)
-        merge_ragged_kernel<4, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, kv_lens, B,
-                                                           Hq, max_len, workers, tile);
+        merge_ragged_kernel<4, 4><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, kv_lens, B,
+                                                          Hq, max_len, workers, tile);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

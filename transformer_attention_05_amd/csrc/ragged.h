@@ -70,4 +70,73 @@ __device__ __forceinline__ int ragged_owner(int t, int T, int P_eff) {
     return (int)((int64_t)t * P_eff / T);
 }
 
+// Piece j of the balanced split: the overlap of worker w's run with
+// sequence b where w + b = j. The pieces of worker w take the consecutive
+// slots w + b_first(w) .. w + b_last(w) (the sequences its run touches), so
+// the worker owning slot j is the last one whose first slot is <= j, found
+// by bisection; a slot between two workers' ranges holds no piece.
+// Returns false if slot j holds no piece; else the sequence, its length and
+// the piece's tiles [t0, t1) counted from the sequence's first tile.
+__device__ __forceinline__ bool ragged_piece(const int *kv_lens, int B, int max_len, int tile,
+                                             int workers, int j, int &b, int &len, int &t0,
+                                             int &t1) {
+    if (B <= 64) {
+        // the whole batch fits one wave: lane l holds sequence l's tile
+        // count and inclusive prefix sum, and every lookup is a ballot
+        const int lane = __lane_id();
+        const int n_l = lane < B ? (ragged_len(kv_lens, lane, max_len) + tile - 1) / tile : 0;
+        int incl = n_l;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(incl, d);
+            if (lane >= d) incl += y;
+        }
+        const int T = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        if (T == 0) return false;
+        const int P = min(workers, T);
+        auto seq_of = [&](int t) {  // sequence holding tile t
+            return __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)__ballot(incl > t)) - 1);
+        };
+        int lo = 0, hi = P - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (mid + seq_of(ragged_run_begin(mid, T, P)) <= j) lo = mid; else hi = mid - 1;
+        }
+        const int w = lo, r0 = ragged_run_begin(w, T, P), r1 = ragged_run_begin(w + 1, T, P);
+        b = j - w;
+        if (b > seq_of(r1 - 1) || b < seq_of(r0)) return false;
+        const int first = __builtin_amdgcn_readfirstlane(__shfl(incl - n_l, b));
+        const int n = __builtin_amdgcn_readfirstlane(__shfl(n_l, b));
+        len = ragged_len(kv_lens, b, max_len);
+        t0 = max(r0, first) - first;
+        t1 = min(r1, first + n) - first;
+        return t0 < t1;
+    }
+    const int T = ragged_total(kv_lens, B, max_len, tile);
+    if (T == 0) return false;
+    const int P = min(workers, T);
+    int lo = 0, hi = P - 1, bl, fl;
+    while (lo < hi) {  // last w with w + b_first(w) <= j
+        const int mid = (lo + hi + 1) / 2;
+        ragged_locate(kv_lens, B, max_len, tile, ragged_run_begin(mid, T, P), bl, fl);
+        if (mid + bl <= j) lo = mid; else hi = mid - 1;
+    }
+    const int w = lo, r0 = ragged_run_begin(w, T, P), r1 = ragged_run_begin(w + 1, T, P);
+    int b_last, f_last;
+    ragged_locate(kv_lens, B, max_len, tile, r1 - 1, b_last, f_last);
+    b = j - w;
+    if (b > b_last) return false;
+    int f_first;
+    ragged_locate(kv_lens, B, max_len, tile, r0, bl, f_first);
+    if (b < bl) return false;
+    // first tile of sequence b: walk from the run's first sequence (few steps)
+    int first = f_first;
+    for (int s = bl; s < b; ++s) first += (ragged_len(kv_lens, s, max_len) + tile - 1) / tile;
+    len = ragged_len(kv_lens, b, max_len);
+    const int n = (len + tile - 1) / tile;
+    t0 = max(r0, first) - first;
+    t1 = min(r1, first + n) - first;
+    return t0 < t1;
+}
+
 }  // namespace attn
