@@ -82,14 +82,22 @@ def default_threads() -> int:
 
 
 def widen(x: np.ndarray) -> np.ndarray:
-    """Stored values → float64, exactly. uint16 means bfloat16 bit patterns."""
+    """Stored values → float64, exactly. uint16 means bfloat16 bit patterns,
+    uint8 means OCP FP8 E4M3 codes (sign, 4-bit exponent with bias 7, 3-bit
+    mantissa; exponent 0 is subnormal, m·2^-9; S.1111.111 is NaN)."""
     x = np.asarray(x)
     if x.dtype == np.uint16:
         f32 = (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
         return np.ascontiguousarray(f32, dtype=np.float64)
+    if x.dtype == np.uint8:
+        c = x.astype(np.int64)
+        e, m = (c >> 3) & 15, c & 7
+        mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.ldexp(1.0, e - 10))
+        mag = np.where((e == 15) & (m == 7), np.nan, mag)
+        return np.ascontiguousarray(np.where(c >> 7, -mag, mag), dtype=np.float64)
     if x.dtype in (np.float32, np.float64):
         return np.ascontiguousarray(x, dtype=np.float64)
-    raise TypeError("oracle inputs must be float32/float64 or bf16 bits (uint16)")
+    raise TypeError("oracle inputs must be float32/float64, bf16 bits (uint16) or E4M3 codes (uint8)")
 
 
 def _ptr(a: np.ndarray):

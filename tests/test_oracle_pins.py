@@ -465,3 +465,37 @@ def test_chunked_and_ragged_reject_bad_lengths():
     d = workloads.gen_decode_gqa(2, 2, 1, D=8, kv_cap=6, kv_lens=[2, 6], seed=41)
     with pytest.raises(ValueError):
         oracle.decode_gqa_ragged(d.q, d.k, d.v, [-1, 3], d.scale)
+
+
+def test_e4m3_widening_matches_the_format_definition():
+    """OCP FP8 E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits,
+    subnormals m·2^-9, no infinity, S.1111.111 = NaN, largest finite 448.
+    Spot values of the definition, and the grid between them: from a code
+    of exponent e the next code is 2^(e−10) higher, and the subnormals
+    continue the first binade's spacing down to 0."""
+    c = np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x7E, 0x80, 0xB8, 0xFE], np.uint8)
+    want = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.5, 448.0, -0.0, -1.0, -448.0]
+    got = oracle.widen(c)
+    np.testing.assert_array_equal(got, want)
+    assert np.signbit(got[7]) and not np.signbit(got[0])
+    assert np.all(np.isnan(oracle.widen(np.array([0x7F, 0xFF], np.uint8))))
+    pos = oracle.widen(np.arange(0x7F, dtype=np.uint8))
+    steps = np.diff(pos)
+    for code in range(1, 0x7F):
+        e = max((code - 1) >> 3, 1)   # the spacing of the lower code's binade
+        assert steps[code - 1] == 2.0 ** (e - 10), code
+    np.testing.assert_array_equal(oracle.widen(np.arange(0x80, 0xFF, dtype=np.uint8)), -pos)
+
+
+def test_decode_over_fp8_cache_is_decode_over_its_values():
+    """An FP8 cache is attended to through its exact values: the decode of
+    E4M3 K/V equals the decode of the same values held in float64, bit for
+    bit, and the NaN tail past kv_len is never read."""
+    w = workloads.gen_decode_gqa(2, 8, 2, 40, D=16, kv_cap=48, seed=5, cache_dtype="fp8")
+    assert w.k.dtype == np.uint8 and np.isnan(oracle.widen(w.k[:, :, 40:])).all()
+    o, lse = oracle.decode_gqa(w.q, w.k, w.v, 40, w.scale)
+    o2, lse2 = oracle.decode_gqa(oracle.widen(w.q), oracle.widen(w.k[:, :, :40]),
+                                 oracle.widen(w.v[:, :, :40]), 40, w.scale)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    assert np.all(np.isfinite(o))

@@ -65,3 +65,30 @@ def test_named_workload_shapes():
     assert workloads.decode_gqa_bytes(8, 32, 8, 4096, 128) == 134_349_824
     assert workloads.prefill_causal_flops(4, 32, 4096, 128) == 549_890_031_616
     assert workloads.decode_mla_bytes(16, 128, 32768, 576, 512) == 608_444_416
+
+
+def test_e4m3_rounding_matches_torch_in_range():
+    """FP8 E4M3 storage rounding (nearest, ties to even) agrees with torch's
+    float8_e4m3fn conversion for every magnitude up to 448, including the
+    exact midpoints between codes; larger magnitudes saturate to ±448."""
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(200000) * 4, rng.uniform(-448, 448, 20000),
+                        [0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -11, 1.0625, 1.1875, 448.0, -448.0]])
+    x = x.astype(np.float32)
+    ours = workloads.round_to_e4m3_bits(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    # midpoints between neighbouring codes go to the even code
+    vals = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    codes = workloads.round_to_e4m3_bits(mids)
+    assert np.all(codes % 2 == 0)
+    np.testing.assert_array_equal(workloads.round_to_e4m3_bits(np.array([500.0, -1e9, 464.0])),
+                                  np.array([0x7E, 0xFE, 0x7E], np.uint8))
+
+
+def test_fp8_decode_cache_poison_and_dtype():
+    w = workloads.gen_decode_gqa(2, 4, 2, 10, D=16, kv_cap=12, seed=3, cache_dtype="fp8")
+    assert w.k.dtype == np.uint8 and w.v.dtype == np.uint8 and w.q.dtype == np.uint16
+    assert np.all(w.k[:, :, 10:] == workloads.E4M3_NAN_BITS)
+    assert np.all(w.k[:, :, :10] != workloads.E4M3_NAN_BITS)

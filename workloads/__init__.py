@@ -41,6 +41,31 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
 
 
+# OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+# infinity; S.1111.111 is NaN; largest finite 448, smallest subnormal 2^-9).
+E4M3_NAN_BITS = np.uint8(0x7F)
+
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """Values of the finite non-negative codes 0x00..0x7E, increasing."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+
+
+def round_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite values to FP8 E4M3 codes: nearest, ties to the even code,
+    magnitudes above 448 saturate to 448."""
+    x = np.asarray(x, dtype=np.float64)
+    vals = _e4m3_magnitudes()
+    a = np.minimum(np.abs(x), 448.0)
+    i = np.clip(np.searchsorted(vals, a), 1, 126)
+    lo, hi = vals[i - 1], vals[i]
+    up = (a - lo > hi - a) | ((a - lo == hi - a) & (i % 2 == 0))
+    code = np.where(up, i, i - 1).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << np.uint8(7))
+
+
 def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
     """Widen bfloat16 bit patterns to float32 (exact)."""
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32)
@@ -59,6 +84,16 @@ def _normal(rng, shape, chunk=1 << 24) -> np.ndarray:
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
         out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+    return out.reshape(shape)
+
+
+def _normal_e4m3(rng, shape, chunk=1 << 22) -> np.ndarray:
+    """N(0,1) float32 draws stored as FP8 E4M3 codes."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = round_to_e4m3_bits(rng.standard_normal(e - s, dtype=np.float32))
     return out.reshape(shape)
 
 
@@ -102,6 +137,7 @@ class DecodeGQA:
     k: np.ndarray
     v: np.ndarray
     kv_lens: np.ndarray | None = None   # [B] int32 per-sequence lengths (ragged batch)
+    cache_dtype: str = "bf16"           # "bf16" (uint16 bits) or "fp8" (E4M3 uint8 codes)
 
 
 @dataclass
@@ -196,11 +232,13 @@ def gen_prefill(B, Hq, Hkv, N, D, dtype="bf16", seed=0, scale=None,
 
 
 def gen_decode_gqa(B, Hq, Hkv, kv_len=None, D=128, kv_cap=None, seed=0, scale=None,
-                   poison_tail=True, kv_lens=None) -> DecodeGQA:
+                   poison_tail=True, kv_lens=None, cache_dtype="bf16") -> DecodeGQA:
     """One query token per sequence; K/V cache of capacity kv_cap filled to
     kv_len (or, for a ragged batch, sequence b filled to kv_lens[b]; kv_len
     is then the longest). Slots past a sequence's length hold NaN when
-    poison_tail is set, so a kernel that reads them produces NaN."""
+    poison_tail is set, so a kernel that reads them produces NaN. The cache
+    holds bf16 or FP8 E4M3 (the same N(0,1) draws, rounded to that format);
+    q is bf16 either way."""
     if kv_lens is not None:
         lens = _lengths(B, kv_lens, None)
         kv_len = int(lens.max())
@@ -212,17 +250,23 @@ def gen_decode_gqa(B, Hq, Hkv, kv_len=None, D=128, kv_cap=None, seed=0, scale=No
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     q = _normal_bf16(rq, (B, Hq, D))
-    k = np.empty((B, Hkv, kv_cap, D), np.uint16)
-    v = np.empty((B, Hkv, kv_cap, D), np.uint16)
-    fill = BF16_NAN_BITS if poison_tail else np.uint16(0)
+    if cache_dtype == "bf16":
+        elt, draw, nan = np.uint16, _normal_bf16, BF16_NAN_BITS
+    elif cache_dtype == "fp8":
+        elt, draw, nan = np.uint8, _normal_e4m3, E4M3_NAN_BITS
+    else:
+        raise ValueError(cache_dtype)
+    k = np.empty((B, Hkv, kv_cap, D), elt)
+    v = np.empty((B, Hkv, kv_cap, D), elt)
+    fill = nan if poison_tail else elt(0)
     for b in range(B):
         n = int(lens[b])
-        k[b, :, :n] = _normal_bf16(rk, (Hkv, n, D))
-        v[b, :, :n] = _normal_bf16(rv, (Hkv, n, D))
+        k[b, :, :n] = draw(rk, (Hkv, n, D))
+        v[b, :, :n] = draw(rv, (Hkv, n, D))
         k[b, :, n:] = fill
         v[b, :, n:] = fill
     return DecodeGQA(B, Hq, Hkv, kv_len, kv_cap, D, float(scale), q, k, v,
-                     lens if kv_lens is not None else None)
+                     lens if kv_lens is not None else None, cache_dtype)
 
 
 def gen_prefill_chunked(B, Hq, Hkv, Nq, kv_lens, D=128, kv_cap=None, seed=0, scale=None,
@@ -317,6 +361,10 @@ WORKLOADS = {
     "decode_gqa_ragged_8k": dict(
         kind="decode_gqa", B=32, Hq=32, Hkv=8, kv_lens=("ragged", 128, 8192, 1107),
         kv_cap=8192, D=128, seed=1007, scale=1.0 / math.sqrt(128)),
+    # the Llama-3-8B decode with an FP8 E4M3 K/V cache (half the bytes)
+    "decode_gqa_fp8_llama3_8b_4k": dict(
+        kind="decode_gqa", B=8, Hq=32, Hkv=8, kv_len=4096, D=128, seed=1009,
+        scale=1.0 / math.sqrt(128), cache_dtype="fp8"),
     "decode_mla_ragged_32k": dict(
         kind="decode_mla", B=16, Hq=128, kv_lens=("ragged", 1024, 32768, 1108),
         kv_cap=32768, Dqk=576, Dv=512, seed=1008, scale=1.0 / math.sqrt(128 + 64)),
