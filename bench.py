@@ -131,12 +131,19 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
     if ragged:
         lens = torch.from_numpy(w.kv_lens).to(dev)
     if kind == "decode_gqa":
-        q, k, v = (_upload_bf16(torch, x, dev) for x in (w.q, w.k, w.v))
+        fp8 = w.cache_dtype == "fp8"
+        q = _upload_bf16(torch, w.q, dev)
+        if fp8:
+            k, v = (torch.from_numpy(x).to(dev) for x in (w.k, w.v))
+        else:
+            k, v = (_upload_bf16(torch, x, dev) for x in (w.k, w.v))
         if ragged:
             nbytes = workloads.decode_gqa_ragged_bytes(w.Hq, w.Hkv, w.kv_lens, w.D)
         else:
-            nbytes = workloads.decode_gqa_bytes(w.B, w.Hq, w.Hkv, w.kv_len, w.D)
-        sets = [(q, k, v)] + [(q, k.clone(), v.clone()) for _ in range(_rotation(2 * k.numel() * 2) - 1)]
+            nbytes = workloads.decode_gqa_bytes(w.B, w.Hq, w.Hkv, w.kv_len, w.D,
+                                                kv_elt=1 if fp8 else 2)
+        sets = [(q, k, v)] + [(q, k.clone(), v.clone())
+                              for _ in range(_rotation(2 * k.numel() * k.element_size()) - 1)]
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
         ws = torch.empty(attn.attn_decode_gqa_workspace_bytes(w.B, w.Hq, w.Hkv, w.kv_len, w.D),
@@ -145,11 +152,14 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
             calls = [lambda s=s: attn.attn_decode_gqa_ragged(s[0], s[1], s[2], lens, w.kv_len,
                                                              w.scale, out=o, lse=lse, ws=ws)
                      for s in sets]
+        elif fp8:
+            calls = [lambda s=s: attn.attn_decode_gqa_fp8(s[0], s[1], s[2], w.kv_len, w.scale, out=o,
+                                                          lse=lse, ws=ws) for s in sets]
         else:
             calls = [lambda s=s: attn.attn_decode_gqa(s[0], s[1], s[2], w.kv_len, w.scale, out=o,
                                                       lse=lse, ws=ws) for s in sets]
         work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
-        kernel = "decode_gqa_kernel + merge_kernel"
+        kernel = "decode_gqa_kernel<%s> + merge_kernel" % ("true" if fp8 else "false")
     elif kind == "decode_mla":
         q, c = _upload_bf16(torch, w.q, dev), _upload_bf16(torch, w.ckv, dev)
         if ragged:

@@ -159,6 +159,25 @@ size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len,
                                        int D);
 
 /*
+ * GQA decode over an FP8 K/V cache: as attn_decode_gqa, but k_cache and
+ * v_cache hold OCP FP8 E4M3 codes, one byte per element ([B, Hkv, kv_cap, D]
+ * bytes; sign, 4-bit exponent with bias 7, 3-bit mantissa, largest finite
+ * 448, S.1111.111 = NaN). The cached values enter the products exactly (each
+ * E4M3 value is converted to bf16 without rounding) and accumulate in fp32,
+ * so only the bytes read from HBM halve ("MLA 矩阵乘法吸收的数值稳定性治理",
+ * §五: low-precision cache storage, FP32 accumulation on chip). Any
+ * per-channel scaling of the stored values (stored = s·k) is the caller's:
+ * fold s⁻¹ into q for K and apply s⁻¹ to O for V. q stays bf16.
+ * Workspace: attn_decode_gqa_workspace_bytes() of the same shape.
+ * Errors as for attn_decode_gqa.
+ */
+attn_status attn_decode_gqa_fp8(const void *q, const void *k_cache,
+                                const void *v_cache, void *o, float *lse, int B,
+                                int Hq, int Hkv, int kv_len, int kv_cap, int D,
+                                float scale, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * GQA decode of a ragged batch: as attn_decode_gqa, but sequence b's cache
  * is filled to kv_lens[b] ("Bộ 06 · Bên trong model", Q3: attend to the
  * filled part only; each sequence of a serving batch has its own length).

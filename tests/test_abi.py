@@ -29,7 +29,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -90,6 +90,20 @@ def test_decode_gqa_workspace_query():
     assert attn.attn_decode_gqa_workspace_bytes(8, 32, 8, 4096, 64) == 0
     assert attn.attn_decode_gqa_workspace_bytes(8, 30, 8, 4096, 128) == 0
     assert attn.attn_decode_gqa_workspace_bytes(8, 32, 8, 0, 128) == 0
+
+
+def test_decode_gqa_fp8_validation(lib):
+    f = lambda **kw: lib.attn_decode_gqa_fp8(*[kw.get(n, d) for n, d in (
+        ("q", P), ("k", P), ("v", P), ("o", P), ("lse", P), ("B", 2), ("Hq", 8), ("Hkv", 2),
+        ("kv_len", 100), ("kv_cap", 128), ("D", 128), ("scale", 0.1), ("ws", P),
+        ("ws_bytes", 1 << 30), ("st", None))])
+    assert f(v=None) == NULLP
+    assert f(kv_len=129) == SHAPE and f(kv_len=0) == SHAPE
+    assert f(D=64) == UNSUP
+    assert f(k=P + 8) == UNSUP
+    assert f(ws_bytes=attn.attn_decode_gqa_workspace_bytes(2, 8, 2, 100) - 1) == WS
+    for s in BAD_SCALES:
+        assert f(scale=s) == SHAPE
 
 
 def _mla(lib, q=P, c=P, o=P, lse=P, B=2, Hq=128, kv_len=1000, kv_cap=1024, Dqk=576, Dv=512,

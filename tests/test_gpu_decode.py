@@ -118,3 +118,40 @@ def test_decode_mla_rising_scores(gpu, kv_len):
     s = oracle.widen(w.q[0]) @ oracle.widen(w.ckv[0, :kv_len]).T * w.scale / np.log(2.0)
     assert (s[:, -32:].max(axis=1) - s[:, :32].max(axis=1)).min() > 3 * 8
     check_bf16(host(o), o_ref, host(lse), lse_ref, "mla rising scores kv_len=%d" % kv_len)
+
+
+# ------------------------------------------------------------ FP8 E4M3 cache ---
+def _dev_u8(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,kv_len,kv_cap", [
+    (1, 4, 1, 1, 8), (2, 8, 2, 5, 64), (2, 32, 8, 255, 300), (3, 16, 4, 257, 512),
+    (1, 16, 1, 4095, 4100), (4, 24, 8, 777, 800), (1, 2, 1, 70000, 70001), (8, 32, 8, 2, 8)])
+def test_decode_gqa_fp8_matches_oracle(gpu, B, Hq, Hkv, kv_len, kv_cap):
+    """E4M3 caches (the NaN code fills the slots past kv_len): the kernel
+    converts the stored codes exactly, so the oracle over the same codes is
+    the reference."""
+    w = workloads.gen_decode_gqa(B, Hq, Hkv, kv_len, D=128, kv_cap=kv_cap, seed=kv_len + 3 * Hq,
+                                 cache_dtype="fp8")
+    o, lse = gpu.attn_decode_gqa_fp8(dev_bf16(w.q), _dev_u8(w.k), _dev_u8(w.v), kv_len, w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_gqa(w.q, w.k, w.v, kv_len, w.scale)
+    check_bf16(host(o), o_ref, host(lse), lse_ref, "gqa fp8 %s" % ((B, Hq, Hkv, kv_len),))
+
+
+def test_decode_gqa_fp8_workload_equals_bf16_copy_of_its_values(gpu):
+    """The Llama-3-8B decode over an E4M3 cache meets the bar, and so does
+    the bf16 kernel run on the same values stored as bf16 (exact widening);
+    the two differ only in the order the products are summed (the E4M3 path
+    takes the head dimension in another order across the MFMA steps)."""
+    w = workloads.make("decode_gqa_fp8_llama3_8b_4k")
+    q = dev_bf16(w.q)
+    o8, l8 = gpu.attn_decode_gqa_fp8(q, _dev_u8(w.k), _dev_u8(w.v), w.kv_len, w.scale)
+    kb = workloads.round_to_bf16_bits(oracle.widen(w.k))
+    vb = workloads.round_to_bf16_bits(oracle.widen(w.v))
+    ob, lb = gpu.attn_decode_gqa(q, dev_bf16(kb), dev_bf16(vb), w.kv_len, w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_gqa(w.q, w.k, w.v, w.kv_len, w.scale)
+    check_bf16(host(o8), o_ref, host(l8), lse_ref, "decode_gqa_fp8_llama3_8b_4k")
+    check_bf16(host(ob), o_ref, host(lb), lse_ref, "bf16 copy of the E4M3 values")

@@ -11,6 +11,7 @@ no fallback: if libattn.so is missing or fails to load, every call raises.
     o, lse = attn_prefill_chunked(q, k_cache, v_cache, kv_lens, scale)  # q [B,Hq,Nq,D]
     o, lse = attn_decode_gqa_ragged(q, k_cache, v_cache, kv_lens, max_kv_len, scale)
     o, lse = attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, 512, scale)
+    o, lse = attn_decode_gqa_fp8(q, k_fp8, v_fp8, kv_len, scale)   # E4M3 caches (uint8)
 (kv_lens: an int32 GPU tensor of per-sequence lengths, read by the kernels.)
 """
 from __future__ import annotations
@@ -55,6 +56,7 @@ def load() -> ctypes.CDLL:
         lib.attn_prefill_causal.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_mla_absorbed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        lib.attn_decode_gqa_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
         lib.attn_decode_gqa_ragged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz,
                                                vp]
@@ -66,7 +68,7 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_mla_workspace_bytes.restype = sz
         lib.attn_decode_mla_ragged_workspace_bytes.restype = sz
         for fn in (lib.attn_prefill_causal, lib.attn_decode_gqa, lib.attn_decode_mla_absorbed,
-                   lib.attn_prefill_chunked, lib.attn_decode_gqa_ragged,
+                   lib.attn_prefill_chunked, lib.attn_decode_gqa_ragged, lib.attn_decode_gqa_fp8,
                    lib.attn_decode_mla_ragged):
             fn.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [i]
@@ -169,6 +171,35 @@ def attn_decode_gqa(q, k_cache, v_cache, kv_len, scale=None, out=None, lse=None,
     st = lib.attn_decode_gqa(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
                              B, Hq, Hkv, int(kv_len), kv_cap, D, float(scale),
                              _ptr(w), w.numel() * w.element_size(), _stream(q.device))
+    _check(st, lib)
+    return o, l
+
+
+def attn_decode_gqa_fp8(q, k_cache, v_cache, kv_len, scale=None, out=None, lse=None, ws=None):
+    """GQA decode over an FP8 E4M3 cache. q [B,Hq,D] bf16; caches
+    [B,Hkv,kv_cap,D] torch.uint8 (E4M3 codes) or torch.float8_e4m3fn, filled
+    to kv_len. Returns (o [B,Hq,D] bf16, lse [B,Hq] fp32)."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype == torch.float8_e4m3fn:
+            t = t.view(torch.uint8)
+        _need(t, name, torch.uint8, 4)
+    B, Hq, D = q.shape
+    _, Hkv, kv_cap, _ = k_cache.shape
+    if k_cache.shape != (B, Hkv, kv_cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, Hkv, kv_cap, D] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "out", torch.bfloat16, 3)
+    _need(l, "lse", torch.float32, 2)
+    need = lib.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, int(kv_len), D)
+    w = workspace(need, q.device) if ws is None else ws
+    st = lib.attn_decode_gqa_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
+                                 B, Hq, Hkv, int(kv_len), kv_cap, D, float(scale),
+                                 _ptr(w), w.numel() * w.element_size(), _stream(q.device))
     _check(st, lib)
     return o, l
 

@@ -45,7 +45,8 @@ attn_status from_hip(hipError_t e, const char *what)
 attn_status decode_gqa_impl(const char *fn, const void *q, const void *k_cache,
                             const void *v_cache, void *o, float *lse, const int *kv_lens,
                             int B, int Hq, int Hkv, int kv_len, int kv_cap, int D, float scale,
-                            void *workspace, size_t workspace_bytes, hipStream_t stream)
+                            void *workspace, size_t workspace_bytes, hipStream_t stream,
+                            bool fp8 = false)
 {
     const char *len_name = kv_lens ? "max_kv_len" : "kv_len";
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 1)
@@ -72,7 +73,7 @@ attn_status decode_gqa_impl(const char *fn, const void *q, const void *k_cache,
         return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, p.ws_total,
                     workspace ? workspace_bytes : (size_t)0);
     return from_hip(attn::launch_decode_gqa(p, q, k_cache, v_cache, o, lse, B, Hq, Hkv, kv_len,
-                                            kv_cap, scale, workspace, stream, kv_lens),
+                                            kv_cap, scale, workspace, stream, kv_lens, fp8),
                     fn);
 }
 
@@ -201,6 +202,17 @@ attn_status attn_decode_gqa(const void *q, const void *k_cache, const void *v_ca
         return fail(ATTN_ERR_NULL_POINTER, "attn_decode_gqa: NULL tensor pointer");
     return decode_gqa_impl("attn_decode_gqa", q, k_cache, v_cache, o, lse, nullptr, B, Hq, Hkv,
                            kv_len, kv_cap, D, scale, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_gqa_fp8(const void *q, const void *k_cache, const void *v_cache,
+                                void *o, float *lse, int B, int Hq, int Hkv, int kv_len,
+                                int kv_cap, int D, float scale, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    if (!q || !k_cache || !v_cache || !o || !lse)
+        return fail(ATTN_ERR_NULL_POINTER, "attn_decode_gqa_fp8: NULL tensor pointer");
+    return decode_gqa_impl("attn_decode_gqa_fp8", q, k_cache, v_cache, o, lse, nullptr, B, Hq, Hkv,
+                           kv_len, kv_cap, D, scale, workspace, workspace_bytes, stream, true);
 }
 
 attn_status attn_decode_gqa_ragged(const void *q, const void *k_cache, const void *v_cache,

@@ -34,6 +34,13 @@
 // log-sum-exp (split-K merge, "AI Infra 入门…", §3). No workgroup waits for
 // another; the kernel boundary orders the partial writes before the merge.
 // Slots at or past kv_len are never read.
+// FP8 cache (OCP E4M3, one byte per element): the same kernel with the K and
+// V bytes converted to bf16 in registers right after they arrive
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1, exact: every E4M3 value is a
+// bf16 value), so the products and the fp32 accumulation are unchanged and
+// only the HBM bytes halve. A lane reads 32 contiguous bytes of its key row
+// (d = 32·quad .. 32·quad + 31) and the MFMA k-steps take them in that
+// order, the query fragments following the same permutation of d.
 // Ragged batches: with a per-sequence length array, workgroup (split, hkv, b)
 // clips its key range to its own sequence's length; splits wholly past it do
 // no work and write an empty partial (m = −∞, ℓ = λ = 0, Õ = 0), which the
@@ -63,31 +70,72 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // (rows of 256 B): spreads the 4-row transposed reads over all banks.
 __device__ __forceinline__ int vswz(int r, int c) { return c ^ (2 * (r & 7)); }
 
-struct Chunk {
+template <bool FP8> struct Chunk;
+template <> struct Chunk<false> {
     u32x4 k[2][4];  // [16-key block][32-d step], MFMA A layout
     u32x4 v[8];     // row 4·i + quad, 16-byte chunk hcol
 };
+template <> struct Chunk<true> {
+    u32x4 k[2][2];  // [16-key block][half]: E4M3 bytes d = 32·quad + 16·half .. + 15
+    u32x4 v[4];     // row 8·i + lane/8, E4M3 bytes d = 16·(lane%8) .. + 15
+};
 
-__device__ __forceinline__ void load_chunk(Chunk &c, const uint16_t *kb, const uint16_t *vb,
-                                           int w0, int key_end, int hcol, int quad)
+// One wave's chunk of 32 keys from w0 (rows past key_end repeat its last).
+// kb, vb: the (b, hkv) cache rows, kD elements of 2 (bf16) or 1 (E4M3) bytes.
+__device__ __forceinline__ void load_chunk(Chunk<false> &c, const char *kb, const char *vb,
+                                           int w0, int key_end, int hcol, int quad, int)
 {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int key = min(w0 + 16 * blk + hcol, key_end - 1);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            c.k[blk][s] = *(const u32x4 *)(kb + (size_t)key * kD + 32 * s + 8 * quad);
+            c.k[blk][s] = *(const u32x4 *)(kb + 2 * ((size_t)key * kD + 32 * s + 8 * quad));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int key = min(w0 + 4 * i + quad, key_end - 1);
-        c.v[i] = *(const u32x4 *)(vb + (size_t)key * kD + 8 * hcol);
+        c.v[i] = *(const u32x4 *)(vb + 2 * ((size_t)key * kD + 8 * hcol));
+    }
+}
+__device__ __forceinline__ void load_chunk(Chunk<true> &c, const char *kb, const char *vb,
+                                           int w0, int key_end, int hcol, int quad, int lane)
+{
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int key = min(w0 + 16 * blk + hcol, key_end - 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            c.k[blk][h] = *(const u32x4 *)(kb + (size_t)key * kD + 32 * quad + 16 * h);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int key = min(w0 + 8 * i + (lane >> 3), key_end - 1);
+        c.v[i] = *(const u32x4 *)(vb + (size_t)key * kD + 16 * (lane & 7));
     }
 }
 
+// Four E4M3 codes (one dword, lowest byte first) as four bf16, exactly.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+// MFMA A operand of k-step s for 16-key block blk.
+__device__ __forceinline__ bf16x8 k_operand(const Chunk<false> &c, int blk, int s) {
+    return as<bf16x8>(c.k[blk][s]);
+}
+__device__ __forceinline__ bf16x8 k_operand(const Chunk<true> &c, int blk, int s) {
+    const u32x4 w = c.k[blk][s >> 1];
+    const u32x2 a = e4m3x4_to_bf16(w[2 * (s & 1)]), b = e4m3x4_to_bf16(w[2 * (s & 1) + 1]);
+    return as<bf16x8>(u32x4{a[0], a[1], b[0], b[1]});
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-    const uint16_t *__restrict__ vc, uint16_t *__restrict__ o, float *__restrict__ lse,
+    const uint16_t *__restrict__ q, const char *__restrict__ kc,
+    const char *__restrict__ vc, uint16_t *__restrict__ o, float *__restrict__ lse,
     int Hq, int Hkv, int G, int kv_len, int kv_cap, float scale_log2, int splits,
     int split_keys, float *__restrict__ ws_ml, float *__restrict__ ws_part,
     const int *__restrict__ kv_lens)
@@ -100,20 +148,23 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     const int bh = b * Hkv + hkv;
     const int key_begin = split * split_keys;
     const int key_end = min(kv_len, key_begin + split_keys);
-    const uint16_t *kbase = kc + (size_t)bh * kv_cap * kD;
-    const uint16_t *vbase = vc + (size_t)bh * kv_cap * kD;
+    constexpr int kElt = FP8 ? 1 : 2;  // cache bytes per element
+    const char *kbase = kc + (size_t)bh * kv_cap * kD * kElt;
+    const char *vbase = vc + (size_t)bh * kv_cap * kD * kElt;
 
     __shared__ __attribute__((aligned(16))) char vbuf[kWaves][kWaveKeys * kD * 2];
     __shared__ float red_o[kWaves][16][kD + 4];
     __shared__ float red_m[kWaves][16], red_l[kWaves][16];
 
-    // qᵀ as the MFMA B operand: column = head (lane % 16), 8 d per lane.
+    // qᵀ as the MFMA B operand: column = head (lane % 16), 8 d per lane
+    // (k-step s: d = 32·s + 8·quad, or 32·quad + 8·s for the E4M3 cache)
     bf16x8 qf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         u32x4 w = {0u, 0u, 0u, 0u};
+        const int d0 = FP8 ? 32 * quad + 8 * s : 32 * s + 8 * quad;
         if (hcol < G)
-            w = *(const u32x4 *)(q + (size_t)(b * Hq + hkv * G + hcol) * kD + 32 * s + 8 * quad);
+            w = *(const u32x4 *)(q + (size_t)(b * Hq + hkv * G + hcol) * kD + d0);
         qf[s] = as<bf16x8>(w);
     }
 
@@ -128,25 +179,38 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     const int ve = (lane >> 2) & 3, vcol = lane & 3;
     const int vr1 = 4 * quad + ve, vr2 = 16 + 4 * quad + ve;
 
-    auto compute = [&](const Chunk &c, int w0) {
+    auto compute = [&](const Chunk<FP8> &c, int w0) {
         // ---- Sᵀ = K qᵀ (two 16-key blocks)
         float sc[8];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as<bf16x8>(c.k[blk][s]), qf[s], acc);
+            for (int s = 0; s < 4; ++s) acc = mfma16x16x32(k_operand(c, blk, s), qf[s], acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = w0 + 16 * blk + 4 * quad + i;
                 sc[4 * blk + i] = key < key_end ? acc[i] * scale_log2 : -INFINITY;
             }
         }
-        // ---- V rows → this wave's LDS buffer (row 4·i + quad, chunk hcol)
+        // ---- V rows → this wave's LDS buffer as bf16 (rows of 256 B)
+        if constexpr (FP8) {
+            // row 8·i + lane/8, bf16 chunks 2·(lane%8) and 2·(lane%8) + 1
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 4 * i + quad;
-            *(u32x4 *)(vb + r * (kD * 2) + 16 * vswz(r, hcol)) = c.v[i];
+            for (int i = 0; i < 4; ++i) {
+                const int r = 8 * i + (lane >> 3), ch = 2 * (lane & 7);
+                const u32x2 a = e4m3x4_to_bf16(c.v[i][0]), b2 = e4m3x4_to_bf16(c.v[i][1]);
+                const u32x2 c2 = e4m3x4_to_bf16(c.v[i][2]), d2 = e4m3x4_to_bf16(c.v[i][3]);
+                *(u32x4 *)(vb + r * (kD * 2) + 16 * vswz(r, ch)) = u32x4{a[0], a[1], b2[0], b2[1]};
+                *(u32x4 *)(vb + r * (kD * 2) + 16 * vswz(r, ch + 1)) = u32x4{c2[0], c2[1], d2[0], d2[1]};
+            }
+        } else {
+            // row 4·i + quad, chunk hcol
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 4 * i + quad;
+                *(u32x4 *)(vb + r * (kD * 2) + 16 * vswz(r, hcol)) = c.v[i];
+            }
         }
         // ---- online softmax for head hcol (its 32 keys live in 4 lanes)
         float mx = sc[0];
@@ -196,17 +260,18 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
         wave_lds_sync();  // the buffer is rewritten by the next chunk
     };
 
-    // ---- software-pipelined chunk loop (ping-pong register buffers)
+    // ---- software-pipelined chunk loop (ping-pong register buffers; for
+    // the E4M3 cache a third buffer, two chunks in flight, measured slower)
     const int first = key_begin + wave * kWaveKeys;
-    Chunk ca, cb;
-    if (first < key_end) load_chunk(ca, kbase, vbase, first, key_end, hcol, quad);
+    Chunk<FP8> ca, cb;
+    if (first < key_end) load_chunk(ca, kbase, vbase, first, key_end, hcol, quad, lane);
     for (int w0 = first; w0 < key_end; w0 += 2 * kChunk) {
         const int w1 = w0 + kChunk;
-        if (w1 < key_end) load_chunk(cb, kbase, vbase, w1, key_end, hcol, quad);
+        if (w1 < key_end) load_chunk(cb, kbase, vbase, w1, key_end, hcol, quad, lane);
         compute(ca, w0);
         if (w1 >= key_end) break;
         const int w2 = w1 + kChunk;
-        if (w2 < key_end) load_chunk(ca, kbase, vbase, w2, key_end, hcol, quad);
+        if (w2 < key_end) load_chunk(ca, kbase, vbase, w2, key_end, hcol, quad, lane);
         compute(cb, w1);
     }
 
@@ -273,14 +338,15 @@ bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p)
 hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, const void *v,
                              void *o, float *lse, int B, int Hq, int Hkv, int kv_len,
                              int kv_cap, float scale, void *ws, hipStream_t st,
-                             const int *kv_lens)
+                             const int *kv_lens, bool fp8)
 {
     char *w = (char *)ws;
     float *ws_ml = (float *)(w + p.ws_ml);
     float *ws_part = (float *)(w + p.ws_part);
     const dim3 grid(p.splits, Hkv, B), block(256);
-    decode_gqa_kernel<<<grid, block, 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, Hq,
+    auto kern = fp8 ? decode_gqa_kernel<true> : decode_gqa_kernel<false>;
+    kern<<<grid, block, 0, st>>>(
+        (const uint16_t *)q, (const char *)k, (const char *)v, (uint16_t *)o, lse, Hq,
         Hkv, Hq / Hkv, kv_len, kv_cap, scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part,
         kv_lens);
     hipError_t e = hipGetLastError();

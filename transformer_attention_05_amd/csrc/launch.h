@@ -16,10 +16,11 @@ struct GqaPlan {
 bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p);
 // kv_lens: NULL (every sequence holds kv_len keys) or a device array of B
 // per-sequence lengths, each clamped to [0, kv_len] by the kernel.
+// fp8: the caches hold OCP FP8 E4M3 codes (one byte per element) instead of bf16.
 hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, const void *v,
                              void *o, float *lse, int B, int Hq, int Hkv, int kv_len,
                              int kv_cap, float scale, void *ws, hipStream_t s,
-                             const int *kv_lens);
+                             const int *kv_lens, bool fp8);
 
 // ---- causal prefill ------------------------------------------------------
 hipError_t launch_prefill_bf16(const void *q, const void *k, const void *v, void *o,

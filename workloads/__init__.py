@@ -402,9 +402,11 @@ def prefill_min_bytes(B, Hq, Hkv, N, D, elt=2):
     return elt * N * D * (2 * B * Hq + 2 * B * Hkv) + 4 * B * Hq * N
 
 
-def decode_gqa_bytes(B, Hq, Hkv, kv_len, D, elt=2):
-    """K and V rows up to kv_len read once, q read, O written, fp32 LSE."""
-    return elt * (2 * B * Hkv * kv_len * D + 2 * B * Hq * D) + 4 * B * Hq
+def decode_gqa_bytes(B, Hq, Hkv, kv_len, D, elt=2, kv_elt=None):
+    """K and V rows up to kv_len read once (kv_elt bytes per element, 1 for
+    an FP8 cache), q read, O written (elt bytes), fp32 LSE."""
+    kv_elt = elt if kv_elt is None else kv_elt
+    return kv_elt * 2 * B * Hkv * kv_len * D + elt * 2 * B * Hq * D + 4 * B * Hq
 
 
 def decode_gqa_flops(B, Hq, kv_len, D):
