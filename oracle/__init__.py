@@ -56,13 +56,15 @@ def _load():
                                                   dp, dp, dp, i]
             lib.oracle_decode_gqa.argtypes = [dp, dp, dp, i, i, i, i, i, i, d, dp, dp, dp, i]
             lib.oracle_decode_mla.argtypes = [dp, dp, i, i, i, i, i, i, d, dp, dp, i]
+            lib.oracle_prefill_causal_backward.argtypes = [dp, dp, dp, dp, i, i, i, i, i, d,
+                                                           dp, dp, dp, i]
             lib.oracle_prefill_chunked.argtypes = [dp, dp, dp, i, i, i, i, ip, i, i, d, ip, i,
                                                    dp, dp, i]
             lib.oracle_decode_gqa_ragged.argtypes = [dp, dp, dp, i, i, i, ip, i, i, d, dp, dp, i]
             lib.oracle_decode_mla_ragged.argtypes = [dp, dp, i, i, ip, i, i, i, d, dp, dp, i]
             for f in (lib.oracle_prefill_causal, lib.oracle_decode_gqa, lib.oracle_decode_mla,
                       lib.oracle_prefill_chunked, lib.oracle_decode_gqa_ragged,
-                      lib.oracle_decode_mla_ragged):
+                      lib.oracle_decode_mla_ragged, lib.oracle_prefill_causal_backward):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -247,3 +249,24 @@ def decode_mla_ragged(q, ckv, kv_lens, dv, scale, threads=None):
     if rc != 0:
         raise ValueError("oracle_decode_mla_ragged rejected its arguments")
     return o, lse
+
+
+def prefill_causal_backward(q, k, v, dout, scale, threads=None):
+    """Gradients of the causal prefill for the upstream gradient dout of O.
+
+    q, dout [B,Hq,N,D]; k, v [B,Hkv,N,D]. Returns (dq, dk, dv) in float64,
+    dk/dv summed over the query heads sharing each K/V head."""
+    q = np.asarray(q)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, D) and v.shape == k.shape and dout.shape == q.shape
+    q64, k64, v64, d64 = widen(q), widen(k), widen(v), widen(dout)
+    dq = np.empty((B, Hq, N, D))
+    dk = np.empty((B, Hkv, N, D))
+    dv = np.empty((B, Hkv, N, D))
+    rc = _load().oracle_prefill_causal_backward(
+        _ptr(q64), _ptr(k64), _ptr(v64), _ptr(d64), B, Hq, Hkv, N, D, float(scale),
+        _ptr(dq), _ptr(dk), _ptr(dv), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_prefill_causal_backward rejected its arguments")
+    return dq, dk, dv

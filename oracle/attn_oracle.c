@@ -34,6 +34,11 @@
  * Decode uses no mask (the single query sees only history, [p1] §3) and
  * reads only the first kv_len cache slots, never unfilled ones ([p4] Q3).
  *
+ * Backward of the causal prefill: the forward weights P are recomputed by
+ * the same definition, then the gradients of the softmax and of the two
+ * products follow the chain rule written out (the LSE kept by the forward
+ * is what lets a fused kernel recompute P exactly, [p1] §3).
+ *
  * Chunked prefill: a chunk of Nq new tokens whose K/V were appended to a
  * cache, so a sequence's keys are [history | chunk] ([p5] §3: K = past K
  * followed by current K). The score matrix [Nq][kv_len] gets the triu(1)
@@ -213,6 +218,99 @@ int oracle_prefill_causal(const double *q, const double *k, const double *v,
     int rc = run_units(prefill_unit, &c, (long)B * Hq * n_rows, N, threads);
     free(mask);
     return rc;
+}
+
+/* ------------------------------------------------ causal prefill backward --- */
+typedef struct {
+    const double *q, *k, *v, *dout;
+    int B, Hq, Hkv, N, D;
+    double scale;
+    double *dq, *dk, *dv;
+} bwd_ctx;
+
+/* One (b, K/V head): every query head of its group in turn. Scratch: the
+ * N×N weights P and the N×N dP of one head, and the causal mask row. */
+static void bwd_unit(void *vctx, long unit, double *scratch)
+{
+    bwd_ctx *c = (bwd_ctx *)vctx;
+    const int N = c->N, D = c->D, G = c->Hq / c->Hkv;
+    const int b = (int)(unit / c->Hkv), hkv = (int)(unit % c->Hkv);
+    double *P = scratch, *dP = scratch + (long)N * N, *s = dP + (long)N * N;
+    unsigned char *mask = (unsigned char *)(s + N);
+    const long kv_off = ((long)b * c->Hkv + hkv) * (long)N * D;
+    const double *K = c->k + kv_off, *V = c->v + kv_off;
+    double *dK = c->dk + kv_off, *dV = c->dv + kv_off;
+    for (long x = 0; x < (long)N * D; ++x)
+        dK[x] = dV[x] = 0.0;
+    for (int g = 0; g < G; ++g) {
+        const long q_off = ((long)b * c->Hq + hkv * G + g) * (long)N * D;
+        const double *Q = c->q + q_off, *dO = c->dout + q_off;
+        double *dQ = c->dq + q_off;
+        /* forward weights, row by row: the same definition as the prefill */
+        for (int i = 0; i < N; ++i) {
+            double o_unused[1], lse_unused;
+            for (int j = 0; j < N; ++j)
+                mask[j] = (unsigned char)(j > i);
+            attend_row(Q + (long)i * D, K, D, D, V, D, 0, N, mask, c->scale, s, o_unused,
+                       &lse_unused, P + (long)i * N);
+        }
+        /* dP_ij = dO_i · V_j ;  dV_j += Σ_i P_ij dO_i */
+        for (int i = 0; i < N; ++i)
+            for (int j = 0; j < N; ++j) {
+                double acc = 0.0;
+                for (int t = 0; t < D; ++t)
+                    acc += dO[(long)i * D + t] * V[(long)j * D + t];
+                dP[(long)i * N + j] = acc;
+            }
+        for (int j = 0; j < N; ++j)
+            for (int i = 0; i < N; ++i) {
+                const double p = P[(long)i * N + j];
+                for (int t = 0; t < D; ++t)
+                    dV[(long)j * D + t] += p * dO[(long)i * D + t];
+            }
+        /* softmax Jacobian: dS_ij = P_ij (dP_ij − Σ_l P_il dP_il), kept in dP */
+        for (int i = 0; i < N; ++i) {
+            double Di = 0.0;
+            for (int j = 0; j < N; ++j)
+                Di += P[(long)i * N + j] * dP[(long)i * N + j];
+            for (int j = 0; j < N; ++j)
+                dP[(long)i * N + j] = P[(long)i * N + j] * (dP[(long)i * N + j] - Di);
+        }
+        /* S = scale·Q·Kᵀ:  dQ_i = scale Σ_j dS_ij K_j ;  dK_j += scale Σ_i dS_ij Q_i */
+        for (int i = 0; i < N; ++i)
+            for (int t = 0; t < D; ++t) {
+                double acc = 0.0;
+                for (int j = 0; j < N; ++j)
+                    acc += dP[(long)i * N + j] * K[(long)j * D + t];
+                dQ[(long)i * D + t] = c->scale * acc;
+            }
+        for (int j = 0; j < N; ++j)
+            for (int t = 0; t < D; ++t) {
+                double acc = 0.0;
+                for (int i = 0; i < N; ++i)
+                    acc += dP[(long)i * N + j] * Q[(long)i * D + t];
+                dK[(long)j * D + t] += c->scale * acc;
+            }
+    }
+}
+
+/* Gradients of the causal prefill (N queries against N keys, mask j > i)
+ * for an upstream gradient dout = ∂L/∂O:
+ *   dV = Pᵀ·dO,  dP = dO·Vᵀ,  dS = P ∘ (dP − rowsum(P ∘ dP)),
+ *   dQ = scale·dS·K,  dK = scale·dSᵀ·Q,
+ * with dK and dV summed over the query heads that share a K/V head.
+ * q, dout, dq: [B][Hq][N][D]; k, v, dk, dv: [B][Hkv][N][D]. */
+int oracle_prefill_causal_backward(const double *q, const double *k, const double *v,
+                                   const double *dout, int B, int Hq, int Hkv, int N, int D,
+                                   double scale, double *dq, double *dk, double *dv,
+                                   int threads)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1 || Hq % Hkv)
+        return -1;
+    bwd_ctx c = {q, k, v, dout, B, Hq, Hkv, N, D, scale, dq, dk, dv};
+    /* scratch: P and dP (N×N each), the score row, and N mask bytes */
+    const long scratch = 2L * N * N + N + (N + 7) / 8 + 1;
+    return run_units(bwd_unit, &c, (long)B * Hkv, (int)scratch, threads);
 }
 
 /* ------------------------------------------- chunked prefill on a cache --- */

@@ -499,3 +499,70 @@ def test_decode_over_fp8_cache_is_decode_over_its_values():
     np.testing.assert_array_equal(o, o2)
     np.testing.assert_array_equal(lse, lse2)
     assert np.all(np.isfinite(o))
+
+
+# ------------------------------------------------------------------- backward ---
+def _loss(q, k, v, dout, scale):
+    """L = Σ O ∘ dO, whose gradient with respect to O is dO."""
+    o, _ = oracle.prefill_causal(q, k, v, scale)
+    return float(np.sum(o * dout))
+
+
+def test_backward_matches_central_differences():
+    """The gradients are the derivatives of L = Σ O∘dO: central differences
+    of the forward oracle (fp64, step 1e-5) at sampled elements of Q, K, V."""
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, N, D = 1, 4, 2, 9, 6
+    q, k, v = (rng.standard_normal(s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D)))
+    dout = rng.standard_normal((B, Hq, N, D))
+    scale = 0.7
+    dq, dk, dv = oracle.prefill_causal_backward(q, k, v, dout, scale)
+    h = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [(0, 0, 0, 0), (0, 1, 4, 2), (0, x.shape[1] - 1, N - 1, D - 1), (0, 0, N // 2, 3)]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            lp = _loss(**{**args, name: xp}, dout=dout, scale=scale)
+            lm = _loss(**{**args, name: xm}, dout=dout, scale=scale)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+
+
+def test_backward_matches_torch_autograd():
+    """Library special case: torch's CPU float64 SDPA (is_causal, contiguous
+    GQA groups) differentiated by autograd."""
+    import torch
+    import torch.nn.functional as F
+    w = workloads.gen_prefill(2, 6, 2, 37, 16, dtype="bf16", seed=23)
+    rng = np.random.default_rng(4)
+    dout = rng.standard_normal((2, 6, 37, 16))
+    dq, dk, dv = oracle.prefill_causal_backward(w.q, w.k, w.v, dout, w.scale)
+    q, k, v = (torch.from_numpy(oracle.widen(x)).requires_grad_() for x in (w.q, w.k, w.v))
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.scale, enable_gqa=True)
+    o.backward(torch.from_numpy(dout))
+    np.testing.assert_allclose(dq, q.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, k.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, v.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_backward_closed_forms():
+    """Equal value rows make O constant in Q and K: dQ = dK = 0. The last key
+    is seen by the last query only: dV[N−1] = Σ_heads P[N−1,N−1]·dO[N−1].
+    The first query sees key 0 alone (weight 1, no softmax gradient):
+    dQ[0] = 0."""
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, N, D = 1, 4, 2, 11, 8
+    q, k = rng.standard_normal((B, Hq, N, D)), rng.standard_normal((B, Hkv, N, D))
+    v = np.repeat(rng.standard_normal((B, Hkv, 1, D)), N, axis=2)
+    dout = rng.standard_normal((B, Hq, N, D))
+    dq, dk, dv = oracle.prefill_causal_backward(q, k, v, dout, 0.5)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    v = rng.standard_normal((B, Hkv, N, D))
+    dq, dk, dv = oracle.prefill_causal_backward(q, k, v, dout, 0.5)
+    assert np.abs(dq[:, :, 0]).max() < 1e-14
+    _, _, p = oracle.prefill_causal(q, k, v, 0.5, return_p=True)
+    for hkv in range(Hkv):
+        want = sum(p[0, h, N - 1, N - 1] * dout[0, h, N - 1] for h in (2 * hkv, 2 * hkv + 1))
+        np.testing.assert_allclose(dv[0, hkv, N - 1], want, rtol=1e-14, atol=1e-15)
