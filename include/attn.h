@@ -89,6 +89,40 @@ attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
                                 hipStream_t stream);
 
 /*
+ * Backward of attn_prefill_causal (bf16, D = 128): given the forward's
+ * inputs, its output o and per-row lse, and the upstream gradient
+ * dout = ∂L/∂O, writes
+ *   dq = scale·dS·K,  dk = scale·dSᵀ·Q,  dv = Pᵀ·dout,
+ * with P = exp(scale·q·k − lse) recomputed from the stored LSE ("AI Infra
+ * 入门…", §3: the LSE lets the backward recompute P exactly) and
+ * dS = P ∘ (dout·Vᵀ − rowsum(dout ∘ o)); dk and dv sum over the Hq/Hkv query
+ * heads sharing each K/V head. All products accumulate in fp32; each
+ * gradient is rounded once to bf16. Deterministic (no atomics).
+ *
+ *   q, o, dout, dq  [B, Hq,  N, D]   bf16 (dq: output)
+ *   k, v, dk, dv    [B, Hkv, N, D]   bf16 (dk, dv: outputs)
+ *   lse             [B, Hq,  N]      fp32, natural log, as written by the forward
+ *   workspace       attn_prefill_causal_backward_workspace_bytes() bytes
+ *                   (16-byte aligned; contents on entry do not matter)
+ *
+ * Errors: NULL pointer → ATTN_ERR_NULL_POINTER; B, Hq, Hkv, N < 1,
+ * Hq % Hkv, a tensor above 2^31 elements or a bad scale → ATTN_ERR_BAD_SHAPE;
+ * D != 128 or misaligned tensors → ATTN_ERR_UNSUPPORTED; workspace too small
+ * → ATTN_ERR_WORKSPACE; launch failure → ATTN_ERR_HIP.
+ */
+attn_status attn_prefill_causal_backward(const void *q, const void *k,
+                                         const void *v, const void *o,
+                                         const float *lse, const void *dout,
+                                         void *dq, void *dk, void *dv, int B,
+                                         int Hq, int Hkv, int N, int D,
+                                         float scale, void *workspace,
+                                         size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/* Bytes of workspace attn_prefill_causal_backward needs (0 if invalid). */
+size_t attn_prefill_causal_backward_workspace_bytes(int B, int Hq, int N, int D);
+
+/*
  * Chunked prefill against a K/V cache: for each sequence, Nq new tokens whose
  * K/V are already appended to the cache attend to the whole filled cache.
  * Sequence b's cache holds kv_lens[b] positions; its last Nq are the chunk's

@@ -29,7 +29,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -85,6 +85,10 @@ def test_decode_gqa_validation(lib):
     assert "workspace" in attn.last_error()
 
 
+def test_backward_workspace_query():
+    assert attn.attn_prefill_causal_backward_workspace_bytes(2, 4, 100, 128) == 3328
+
+
 def test_decode_gqa_workspace_query():
     assert attn.attn_decode_gqa_workspace_bytes(8, 32, 8, 4096, 128) > 0
     assert attn.attn_decode_gqa_workspace_bytes(8, 32, 8, 4096, 64) == 0
@@ -102,6 +106,21 @@ def test_decode_gqa_fp8_validation(lib):
     assert f(D=64) == UNSUP
     assert f(k=P + 8) == UNSUP
     assert f(ws_bytes=attn.attn_decode_gqa_workspace_bytes(2, 8, 2, 100) - 1) == WS
+    for s in BAD_SCALES:
+        assert f(scale=s) == SHAPE
+
+
+def test_prefill_backward_validation(lib):
+    f = lambda **kw: lib.attn_prefill_causal_backward(*[kw.get(n, d) for n, d in (
+        ("q", P), ("k", P), ("v", P), ("o", P), ("lse", P), ("do", P), ("dq", P), ("dk", P),
+        ("dv", P), ("B", 1), ("Hq", 8), ("Hkv", 2), ("N", 300), ("D", 128), ("scale", 0.1),
+        ("ws", P), ("ws_bytes", 1 << 30), ("st", None))])
+    assert f(do=None) == NULLP and f(dk=None) == NULLP
+    assert f(N=0) == SHAPE and f(Hq=6, Hkv=4) == SHAPE
+    assert f(D=64) == UNSUP and f(dv=P + 4) == UNSUP
+    need = attn.attn_prefill_causal_backward_workspace_bytes(1, 8, 300, 128)
+    assert need >= 4 * 8 * 300 and attn.attn_prefill_causal_backward_workspace_bytes(1, 8, 300, 64) == 0
+    assert f(ws_bytes=need - 1) == WS
     for s in BAD_SCALES:
         assert f(scale=s) == SHAPE
 

@@ -12,6 +12,7 @@ no fallback: if libattn.so is missing or fails to load, every call raises.
     o, lse = attn_decode_gqa_ragged(q, k_cache, v_cache, kv_lens, max_kv_len, scale)
     o, lse = attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, 512, scale)
     o, lse = attn_decode_gqa_fp8(q, k_fp8, v_fp8, kv_len, scale)   # E4M3 caches (uint8)
+    dq, dk, dv = attn_prefill_causal_backward(q, k, v, o, lse, dout, scale)
 (kv_lens: an int32 GPU tensor of per-sequence lengths, read by the kernels.)
 """
 from __future__ import annotations
@@ -57,6 +58,10 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_mla_absorbed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_gqa_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        lib.attn_prefill_causal_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
+                                                     i, f, vp, sz, vp]
+        lib.attn_prefill_causal_backward_workspace_bytes.argtypes = [i, i, i, i]
+        lib.attn_prefill_causal_backward_workspace_bytes.restype = sz
         lib.attn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
         lib.attn_decode_gqa_ragged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz,
                                                vp]
@@ -69,6 +74,7 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_mla_ragged_workspace_bytes.restype = sz
         for fn in (lib.attn_prefill_causal, lib.attn_decode_gqa, lib.attn_decode_mla_absorbed,
                    lib.attn_prefill_chunked, lib.attn_decode_gqa_ragged, lib.attn_decode_gqa_fp8,
+                   lib.attn_prefill_causal_backward,
                    lib.attn_decode_mla_ragged):
             fn.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [i]
@@ -145,8 +151,41 @@ def attn_prefill_causal(q, k, v, scale=None, out=None, lse=None):
     return o, l
 
 
+def attn_prefill_causal_backward(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None,
+                                 ws=None):
+    """Backward of attn_prefill_causal (bf16, D = 128). q, o, dout [B,Hq,N,D];
+    k, v [B,Hkv,N,D]; lse [B,Hq,N] fp32 from the forward. Returns (dq, dk, dv)."""
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _need(t, name, torch.bfloat16, 4)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shapes must be q/o/dout [B,Hq,N,D], k/v [B,Hkv,N,D]")
+    _need(lse, "lse", torch.float32, 3)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _need(t, name, torch.bfloat16, 4)
+    need = lib.attn_prefill_causal_backward_workspace_bytes(B, Hq, N, D)
+    w = workspace(need, q.device) if ws is None else ws
+    st = lib.attn_prefill_causal_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                          _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, D,
+                                          float(scale), _ptr(w), w.numel() * w.element_size(),
+                                          _stream(q.device))
+    _check(st, lib)
+    return dq, dk, dv
+
+
 def attn_decode_gqa_workspace_bytes(B, Hq, Hkv, kv_len, D=128) -> int:
     return int(load().attn_decode_gqa_workspace_bytes(B, Hq, Hkv, kv_len, D))
+
+
+def attn_prefill_causal_backward_workspace_bytes(B, Hq, N, D=128) -> int:
+    return int(load().attn_prefill_causal_backward_workspace_bytes(B, Hq, N, D))
 
 
 def attn_decode_gqa(q, k_cache, v_cache, kv_len, scale=None, out=None, lse=None, ws=None):

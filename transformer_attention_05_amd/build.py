@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_api.cpp", "decode_gqa.hip", "prefill_bf16.hip", "prefill_f32.hip",
-           "prefill_bf16_d128.hip", "decode_mla.hip", "merge.hip"]
+           "prefill_bf16_d128.hip", "prefill_bwd_d128.hip", "decode_mla.hip", "merge.hip"]
 FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]

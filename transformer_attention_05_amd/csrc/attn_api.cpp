@@ -186,6 +186,46 @@ attn_status attn_prefill_chunked(const void *q, const void *k_cache, const void 
                     fn);
 }
 
+size_t attn_prefill_causal_backward_workspace_bytes(int B, int Hq, int N, int D)
+{
+    if (B < 1 || Hq < 1 || N < 1 || D != 128) return 0;
+    return attn::prefill_bwd_workspace_bytes(B, Hq, N);
+}
+
+attn_status attn_prefill_causal_backward(const void *q, const void *k, const void *v,
+                                         const void *o, const float *lse, const void *dout,
+                                         void *dq, void *dk, void *dv, int B, int Hq, int Hkv,
+                                         int N, int D, float scale, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream)
+{
+    static const char fn[] = "attn_prefill_causal_backward";
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+        return fail(ATTN_ERR_NULL_POINTER, "%s: NULL tensor pointer", fn);
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: B, Hq, Hkv, N, D must be >= 1", fn);
+    if (Hq % Hkv)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: Hq (%d) not a multiple of Hkv (%d)", fn, Hq, Hkv);
+    if (!good_scale(scale))
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: scale must be finite and > 0", fn);
+    if ((long long)B * Hq * N * D > kMaxElems)
+        return fail(ATTN_ERR_BAD_SHAPE, "%s: tensor exceeds 2^31 elements", fn);
+    if (D != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d (only 128)", fn, D);
+    const void *t16[] = {q, k, v, o, dout, dq, dk, dv};
+    for (const void *p : t16)
+        if (!aligned16(p))
+            return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned", fn);
+    if (!aligned4(lse))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: lse must be 4-byte aligned", fn);
+    const size_t need = attn::prefill_bwd_workspace_bytes(B, Hq, N);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    return from_hip(attn::launch_prefill_bwd_d128(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv,
+                                                  N, scale, workspace, stream),
+                    fn);
+}
+
 size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len, int D)
 {
     attn::GqaPlan p;

@@ -35,6 +35,12 @@ hipError_t launch_prefill_bf16_d128(const void *q, const void *k, const void *v,
 hipError_t launch_prefill_chunked_d128(const void *q, const void *k, const void *v, void *o,
                                        float *lse, const int *kv_lens, int B, int Hq, int Hkv,
                                        int N, int kv_cap, float scale, hipStream_t s);
+// Backward of the causal prefill, d = 128, bf16; ws holds B·Hq·N fp32 (D = dO·O).
+size_t prefill_bwd_workspace_bytes(int B, int Hq, int N);
+hipError_t launch_prefill_bwd_d128(const void *q, const void *k, const void *v, const void *o,
+                                   const float *lse, const void *dout, void *dq, void *dk,
+                                   void *dv, int B, int Hq, int Hkv, int N, float scale,
+                                   void *ws, hipStream_t s);
 hipError_t launch_prefill_f32(const float *q, const float *k, const float *v, float *o,
                               float *lse, int B, int Hq, int Hkv, int N, int D,
                               float scale, hipStream_t s);

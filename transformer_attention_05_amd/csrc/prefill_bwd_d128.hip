@@ -1,0 +1,393 @@
+// Backward of the causal prefill, head dimension 128, bf16 in/out, fp32
+// accumulation, gfx950.
+//
+// The forward keeps the per-row log-sum-exp; the backward recomputes the
+// weights from it exactly, P = 2^(s·scale·log2 e − LSE·log2 e), instead of
+// storing the N×N matrix ("AI Infra 入门…", §3: the LSE turns the softmax
+// division into a subtraction, which is what lets the backward recompute P).
+// With dO = ∂L/∂O and D_i = dO_i·O_i (= Σ_j P_ij dP_ij):
+//   dV = Pᵀ·dO,  dP = dO·Vᵀ,  dS = P ∘ (dP − D),  dQ = scale·dS·K,
+//   dK = scale·dSᵀ·Q,
+// dK and dV summed over the query heads that share a K/V head.
+//
+// Three kernels, no atomics (the result is bitwise reproducible):
+//   dot    D_i = dO_i·O_i in fp32 (16 lanes per row).
+//   dkdv   workgroup (b, K/V head, 128-key block), 4 waves of 32 keys each
+//          with their K and V rows in registers as MFMA B operands. For each
+//          query head of the group and each 32-query tile at or after the
+//          block (tiles staged through LDS, double-buffered):
+//            S  = Q·Kᵀ, dP = dO·Vᵀ          (v_mfma_f32_32x32x16_bf16; the
+//                                           lane holds one key's column)
+//            P, dS element-wise (masked on the diagonal tiles)
+//            dVᵀ += dOᵀ·P, dKᵀ += Qᵀ·dS      (P and dS rounded to bf16 in
+//                                           registers: their accumulator
+//                                           layout is the B-operand layout;
+//                                           dOᵀ and Qᵀ by ds_read_b64_tr_b16)
+//   dq     workgroup (b, query head, 128-query block), 4 waves of 32 queries
+//          with Qᵀ and dOᵀ fragments in registers; over the 32-key tiles up
+//          to the diagonal:
+//            Sᵀ = K·Qᵀ, dPᵀ = V·dOᵀ, Pᵀ and dSᵀ, dQᵀ += Kᵀ·dSᵀ
+// so S and dP are computed twice (in dkdv and in dq) rather than summed into
+// dQ across workgroups with atomics. Each LDS tile that is read both by rows
+// (ds_read_b128) and transposed (ds_read_b64_tr_b16) is stored twice, with
+// row pitches of 272 B and 320 B, the conflict-free pitch for each pattern.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int D = 128, KS = D / 16, DB = D / 32;
+constexpr int T = 32;                       // rows per wave and per tile
+constexpr int NWV = 4;                      // waves per workgroup
+constexpr int BLK = T * NWV;                // keys (dkdv) or queries (dq) per workgroup
+constexpr int RP = 136, TP = 160;           // row pitches (elements): 272 B and 320 B
+constexpr int RPB = 2 * RP, TPB = 2 * TP;   // in bytes
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposed MFMA A operand (32 rows of d × 16 k) from a row-major LDS tile
+// whose rows are the k index: slot t of lane 16g + 4e + c holds tile row
+// 16·mm + 8·(t/4) + 4·half + t%4, column 32·db + 16·(g&1) + 4·c + (t%4 ...)
+// — the layout the Sᵀ/P accumulator registers 8·mm .. 8·mm + 7 match.
+__device__ __forceinline__ bf16x8 tr_operand(const char *tile, int lane_off, int mm, int db) {
+    const char *p = tile + lane_off + 16 * mm * TPB + 64 * db;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 8 * TPB));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return as<bf16x8>(u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+
+// B operands of the two 16-row k-steps of a 32×32 accumulator, rounded to bf16.
+__device__ __forceinline__ void pack_b(const f32x16 &acc, bf16x8 (&out)[2]) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+        u32x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(acc[8 * mm + 2 * t], acc[8 * mm + 2 * t + 1]);
+        out[mm] = as<bf16x8>(w);
+    }
+}
+
+// ---------------------------------------------------------------- D = dO·O ---
+__global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t *__restrict__ o,
+                                                      const uint16_t *__restrict__ dout,
+                                                      float *__restrict__ dd, long rows)
+{
+    const long row = (long)blockIdx.x * 16 + threadIdx.x / 16;
+    const int c = threadIdx.x % 16;  // 8 elements each
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 a = *(const u32x4 *)(o + row * D + 8 * c);
+        const u32x4 b = *(const u32x4 *)(dout + row * D + 8 * c);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            acc += bf16lo(a[t]) * bf16lo(b[t]) + bf16hi(a[t]) * bf16hi(b[t]);
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
+    if (row < rows && c == 0) dd[row] = acc;
+}
+
+// ------------------------------------------------------------------- dK, dV ---
+struct TileBuf {           // one 32-row query tile of Q and dO, in two pitches
+    uint16_t qr[T * RP], qt[T * TP], dr[T * RP], dt[T * TP];
+    float lse2[T], dd[T];
+};
+
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dd,
+    uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, int Hq, int Hkv, int N, int n_kblk,
+    float scale_log2, float scale)
+{
+    __shared__ __attribute__((aligned(16))) TileBuf buf[2];
+
+    const int G = Hq / Hkv;
+    // heaviest first: key block 0 sees every query
+    const int kblk = blockIdx.x % n_kblk, bh = blockIdx.x / n_kblk;
+    const int b = bh / Hkv, hkv = bh % Hkv;
+    const int k0 = kblk * BLK;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, half = lane >> 5;
+    const int kw0 = k0 + T * wave;          // this wave's keys
+    const int key = kw0 + col;              // this lane's key (column)
+    const size_t kvoff = (size_t)bh * N * D;
+
+    // K and V rows of the wave's keys as B operands (k = d): d = 16·ks + 8·half
+    bf16x8 kf[KS], vf[KS];
+    {
+        const int kr = min(key, N - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kf[ks] = as<bf16x8>(*(const u32x4 *)(k + kvoff + (size_t)kr * D + 16 * ks + 8 * half));
+            vf[ks] = as<bf16x8>(*(const u32x4 *)(v + kvoff + (size_t)kr * D + 16 * ks + 8 * half));
+        }
+    }
+    f32x16 dkacc[DB], dvacc[DB];  // dKᵀ, dVᵀ: rows d = 32·db + row(i), column = key
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dkacc[db][i] = dvacc[db][i] = 0.f;
+
+    // staging: thread tid moves 16-byte chunks (tid, tid + 256) of the
+    // 32 × 256 B Q and dO tiles, row r = chunk / 16, column chunk c = chunk % 16
+    const int g4 = lane >> 4, e4 = (lane >> 2) & 3, cq = lane & 3;
+    const int tr_lane = (4 * half + e4) * TPB + 32 * (g4 & 1) + 8 * cq;
+    const int q_first = (k0 / T) * T;                   // first tile with a query >= k0
+    const int n_qt = (N - q_first + T - 1) / T;         // query tiles per head
+    const int n_it = G * n_qt;
+    u32x4 sq[2], sd[2];
+    float sl = 0.f, sdd = 0.f;
+    auto load = [&](int it) __attribute__((always_inline)) {
+        const int h = hkv * G + it / n_qt, q0 = q_first + T * (it % n_qt);
+        const size_t qoff = ((size_t)b * Hq + h) * N;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ch = tid + 256 * u, r = min(q0 + ch / 16, N - 1), c = ch % 16;
+            sq[u] = *(const u32x4 *)(q + (qoff + r) * D + 8 * c);
+            sd[u] = *(const u32x4 *)(dout + (qoff + r) * D + 8 * c);
+        }
+        if (tid < T) {
+            const int r = min(q0 + tid, N - 1);
+            sl = lse[qoff + r] * kLog2e;
+            sdd = dd[qoff + r];
+        }
+    };
+    auto store = [&](TileBuf &t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ch = tid + 256 * u, r = ch / 16, c = ch % 16;
+            *(u32x4 *)&t.qr[r * RP + 8 * c] = sq[u];
+            *(u32x4 *)&t.qt[r * TP + 8 * c] = sq[u];
+            *(u32x4 *)&t.dr[r * RP + 8 * c] = sd[u];
+            *(u32x4 *)&t.dt[r * TP + 8 * c] = sd[u];
+        }
+        if (tid < T) {
+            t.lse2[tid] = sl;
+            t.dd[tid] = sdd;
+        }
+    };
+
+    load(0);
+    store(buf[0]);
+    __syncthreads();
+    for (int it = 0; it < n_it; ++it) {
+        const int cur = it & 1;
+        if (it + 1 < n_it) load(it + 1);
+        const int q0 = q_first + T * (it % n_qt);
+        const TileBuf &tb = buf[cur];
+        if (q0 + T - 1 >= kw0) {  // some query of the tile sees some key of the wave
+            // ---- S = Q·Kᵀ and dP = dO·Vᵀ: rows = queries, lane column = key
+            f32x16 s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = as<bf16x8>(*(const u32x4 *)&tb.qr[col * RP + 16 * ks + 8 * half]);
+                const bf16x8 c = as<bf16x8>(*(const u32x4 *)&tb.dr[col * RP + 16 * ks + 8 * half]);
+                s = mfma32x32x16(a, kf[ks], s);
+                dp = mfma32x32x16(c, vf[ks], dp);
+            }
+            // ---- P = 2^(s·scale·log2 e − LSE₂), dS = P ∘ (dP − D); query rows
+            // 8·(i/4) + 4·half + i%4 (their LSE and D come as float4 runs)
+            const bool edge = q0 < kw0 + T - 1 || q0 + T > N;  // masked keys or padded queries
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int r0 = 8 * gi + 4 * half;
+                const float4 L4 = *(const float4 *)&tb.lse2[r0];
+                const float4 D4 = *(const float4 *)&tb.dd[r0];
+                const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 4 * gi + j, qi = q0 + r0 + j;
+                    float p = exp2_fast(fmaf(s[i], scale_log2, -Lr[j]));
+                    if (edge && (key > qi || qi >= N)) p = 0.f;
+                    s[i] = p;
+                    dp[i] = p * (dp[i] - Dr[j]);
+                }
+            }
+            bf16x8 pf[2], sf[2];
+            pack_b(s, pf);
+            pack_b(dp, sf);
+            // ---- dVᵀ += dOᵀ·P, dKᵀ += Qᵀ·dS (k = the tile's queries)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dvacc[db] = mfma32x32x16(tr_operand((const char *)tb.dt, tr_lane, mm, db), pf[mm], dvacc[db]);
+                    dkacc[db] = mfma32x32x16(tr_operand((const char *)tb.qt, tr_lane, mm, db), sf[mm], dkacc[db]);
+                }
+        }
+        if (it + 1 < n_it) store(buf[cur ^ 1]);
+        __syncthreads();
+    }
+
+    // ---- epilogue: dK = scale·(dKᵀ)ᵀ, dV; lane writes column `key`, rows d
+    if (key < N) {
+        uint16_t *dkr = dk + kvoff + (size_t)key * D, *dvr = dv + kvoff + (size_t)key * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int d0 = 32 * db + 8 * gi + 4 * half;
+                const u32x2 wk = {pack_bf16x2(dkacc[db][4 * gi] * scale, dkacc[db][4 * gi + 1] * scale),
+                                  pack_bf16x2(dkacc[db][4 * gi + 2] * scale, dkacc[db][4 * gi + 3] * scale)};
+                const u32x2 wv = {pack_bf16x2(dvacc[db][4 * gi], dvacc[db][4 * gi + 1]),
+                                  pack_bf16x2(dvacc[db][4 * gi + 2], dvacc[db][4 * gi + 3])};
+                *(u32x2 *)(dkr + d0) = wk;
+                *(u32x2 *)(dvr + d0) = wv;
+            }
+    }
+}
+
+// ----------------------------------------------------------------------- dQ ---
+struct KTileBuf {          // one 32-key tile: K in both pitches, V by rows
+    uint16_t kr[T * RP], kt[T * TP], vr[T * RP];
+};
+
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dd,
+    uint16_t *__restrict__ dq, int Hq, int Hkv, int N, int n_qblk, float scale_log2, float scale)
+{
+    __shared__ __attribute__((aligned(16))) KTileBuf buf[2];
+
+    // heaviest first: the last query block sees every key
+    const int qblk = n_qblk - 1 - (int)(blockIdx.x % n_qblk), bhq = blockIdx.x / n_qblk;
+    const int b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv);
+    const int q0 = qblk * BLK;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, half = lane >> 5;
+    const int qw0 = q0 + T * wave, qrow = qw0 + col;  // this lane's query (column)
+    const size_t qoff = (size_t)bhq * N * D, kvoff = ((size_t)b * Hkv + hkv) * N * D;
+
+    // Qᵀ and dOᵀ as B operands (k = d): d = 16·ks + 8·half
+    bf16x8 qf[KS], df[KS];
+    {
+        const int r = min(qrow, N - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[ks] = as<bf16x8>(*(const u32x4 *)(q + qoff + (size_t)r * D + 16 * ks + 8 * half));
+            df[ks] = as<bf16x8>(*(const u32x4 *)(dout + qoff + (size_t)r * D + 16 * ks + 8 * half));
+        }
+    }
+    const float lse2 = lse[(size_t)bhq * N + min(qrow, N - 1)] * kLog2e;
+    const float dq_d = dd[(size_t)bhq * N + min(qrow, N - 1)];
+    f32x16 acc[DB];  // dQᵀ: rows d, column = query
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+    const int g4 = lane >> 4, e4 = (lane >> 2) & 3, cq = lane & 3;
+    const int tr_lane = (4 * half + e4) * TPB + 32 * (g4 & 1) + 8 * cq;
+    const int n_kt = min(N - 1, q0 + BLK - 1) / T + 1;   // key tiles up to the block's last row
+    u32x4 sk[2], sv[2];
+    auto load = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ch = tid + 256 * u, r = min(T * j + ch / 16, N - 1), c = ch % 16;
+            sk[u] = *(const u32x4 *)(k + kvoff + (size_t)r * D + 8 * c);
+            sv[u] = *(const u32x4 *)(v + kvoff + (size_t)r * D + 8 * c);
+        }
+    };
+    auto store = [&](KTileBuf &t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ch = tid + 256 * u, r = ch / 16, c = ch % 16;
+            *(u32x4 *)&t.kr[r * RP + 8 * c] = sk[u];
+            *(u32x4 *)&t.kt[r * TP + 8 * c] = sk[u];
+            *(u32x4 *)&t.vr[r * RP + 8 * c] = sv[u];
+        }
+    };
+
+    load(0);
+    store(buf[0]);
+    __syncthreads();
+    for (int j = 0; j < n_kt; ++j) {
+        const int cur = j & 1;
+        if (j + 1 < n_kt) load(j + 1);
+        const int kt0 = T * j;
+        const KTileBuf &tb = buf[cur];
+        if (kt0 <= qw0 + T - 1 && qw0 < N) {
+            // ---- Sᵀ = K·Qᵀ, dPᵀ = V·dOᵀ: rows = keys, lane column = query
+            f32x16 s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = as<bf16x8>(*(const u32x4 *)&tb.kr[col * RP + 16 * ks + 8 * half]);
+                const bf16x8 c = as<bf16x8>(*(const u32x4 *)&tb.vr[col * RP + 16 * ks + 8 * half]);
+                s = mfma32x32x16(a, qf[ks], s);
+                dp = mfma32x32x16(c, df[ks], dp);
+            }
+            const bool diag = kt0 + T - 1 > qw0;  // keys after some query of the wave
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kj = kt0 + 8 * (i / 4) + 4 * half + (i % 4);
+                float p = exp2_fast(fmaf(s[i], scale_log2, -lse2));
+                if (diag && kj > qrow) p = 0.f;
+                dp[i] = p * (dp[i] - dq_d);
+            }
+            bf16x8 sf[2];
+            pack_b(dp, sf);
+            // ---- dQᵀ += Kᵀ·dSᵀ (k = the tile's keys)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    acc[db] = mfma32x32x16(tr_operand((const char *)tb.kt, tr_lane, mm, db), sf[mm], acc[db]);
+        }
+        if (j + 1 < n_kt) store(buf[cur ^ 1]);
+        __syncthreads();
+    }
+
+    if (qrow < N) {
+        uint16_t *row = dq + qoff + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const u32x2 w = {pack_bf16x2(acc[db][4 * gi] * scale, acc[db][4 * gi + 1] * scale),
+                                 pack_bf16x2(acc[db][4 * gi + 2] * scale, acc[db][4 * gi + 3] * scale)};
+                *(u32x2 *)(row + 32 * db + 8 * gi + 4 * half) = w;
+            }
+    }
+}
+
+}  // namespace
+
+size_t prefill_bwd_workspace_bytes(int B, int Hq, int N)
+{
+    return align_up(sizeof(float) * (size_t)B * Hq * N, 256);
+}
+
+hipError_t launch_prefill_bwd_d128(const void *q, const void *k, const void *v, const void *o,
+                                   const float *lse, const void *dout, void *dq, void *dk,
+                                   void *dv, int B, int Hq, int Hkv, int N, float scale,
+                                   void *ws, hipStream_t st)
+{
+    float *dd = (float *)ws;
+    const long rows = (long)B * Hq * N;
+    bwd_dot_kernel<<<dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st>>>(
+        (const uint16_t *)o, (const uint16_t *)dout, dd, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const float sl2 = scale * kLog2e;
+    const int n_blk = (N + BLK - 1) / BLK;
+    bwd_dkdv_kernel<<<dim3((unsigned)(n_blk * B * Hkv)), dim3(256), 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse,
+        dd, (uint16_t *)dk, (uint16_t *)dv, Hq, Hkv, N, n_blk, sl2, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    bwd_dq_kernel<<<dim3((unsigned)(n_blk * B * Hq)), dim3(256), 0, st>>>(
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse,
+        dd, (uint16_t *)dq, Hq, Hkv, N, n_blk, sl2, scale);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -231,6 +231,11 @@ def gen_prefill(B, Hq, Hkv, N, D, dtype="bf16", seed=0, scale=None,
     return Prefill(B, Hq, Hkv, N, D, dtype, float(scale), q, k, v, rows)
 
 
+def gen_upstream_grad(shape, seed) -> np.ndarray:
+    """An upstream gradient dL/dO for the backward: N(0,1) draws in bf16."""
+    return _normal_bf16(np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed))), shape)
+
+
 def gen_decode_gqa(B, Hq, Hkv, kv_len=None, D=128, kv_cap=None, seed=0, scale=None,
                    poison_tail=True, kv_lens=None, cache_dtype="bf16") -> DecodeGQA:
     """One query token per sequence; K/V cache of capacity kv_cap filled to
@@ -442,3 +447,11 @@ def decode_mla_ragged_bytes(Hq, kv_lens, Dqk, Dv, elt=2):
     lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
     B = lens.shape[0]
     return int(elt * (int(lens.sum()) * Dqk + B * Hq * Dqk + B * Hq * Dv) + 4 * B * Hq)
+
+
+def prefill_backward_flops(B, Hq, N, D):
+    """Algorithmic flops of the backward over the visible pairs: the five
+    products of the standard recomputing backward (S, dP, dV, dQ, dK), 2·D
+    flops each per pair. (The kernels here form S and dP twice, once for
+    dK/dV and once for dQ; that extra work is not counted.)"""
+    return 10 * D * (N * (N + 1) // 2) * B * Hq
