@@ -180,6 +180,22 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
                                                                out=o, lse=lse, ws=ws) for s in sets]
         work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
         kernel = "decode_mla_kernel + merge_kernel"
+    elif kind == "prefill_backward":
+        q, k, v = (_upload_bf16(torch, x, dev) for x in (w.q, w.k, w.v))
+        dout = _upload_bf16(torch, workloads.gen_upstream_grad((w.B, w.Hq, w.N, w.D), seed=1010), dev)
+        o, lse = attn.attn_prefill_causal(q, k, v, w.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(attn.attn_prefill_causal_backward_workspace_bytes(w.B, w.Hq, w.N, w.D),
+                         dtype=torch.uint8, device=dev)
+        flops = workloads.prefill_backward_flops(w.B, w.Hq, w.N, w.D)
+        calls = [lambda: attn.attn_prefill_causal_backward(q, k, v, o, lse, dout, w.scale, dq=dq,
+                                                           dk=dk, dv=dv, ws=ws)]
+        work, unit, peak, bound = flops / 1e12, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS, "mfma"
+        kernel = "bwd_dot_kernel + bwd_dkdv_kernel + bwd_dq_kernel"
+        nsteps = max(5, min(steps, int(1e14 // max(flops, 1))))
+        if nsteps >= 20:
+            nsteps -= nsteps % 20
+        steps, warmup = nsteps, max(min(warmup, 5), min(200, int(2e13 // max(flops, 1))))
     elif kind == "prefill_chunked":
         q, k, v = (_upload_bf16(torch, x, dev) for x in (w.q, w.k, w.v))
         lens = torch.from_numpy(w.kv_lens).to(dev)

@@ -366,6 +366,10 @@ WORKLOADS = {
     "decode_gqa_ragged_8k": dict(
         kind="decode_gqa", B=32, Hq=32, Hkv=8, kv_lens=("ragged", 128, 8192, 1107),
         kv_cap=8192, D=128, seed=1007, scale=1.0 / math.sqrt(128)),
+    # the backward of the 4k prefill (upstream gradient seed 1010)
+    "prefill_bf16_4k_backward": dict(
+        kind="prefill_backward", B=4, Hq=32, Hkv=8, N=4096, D=128, dtype="bf16", seed=1003,
+        scale=1.0 / math.sqrt(128)),
     # the Llama-3-8B decode with an FP8 E4M3 K/V cache (half the bytes)
     "decode_gqa_fp8_llama3_8b_4k": dict(
         kind="decode_gqa", B=8, Hq=32, Hkv=8, kv_len=4096, D=128, seed=1009,
@@ -386,6 +390,8 @@ def make(name: str, **overrides):
         cfg["kv_lens"] = ragged_lengths(cfg["B"], *lens[1:])
     if kind == "prefill_chunked":
         return gen_prefill_chunked(**cfg)
+    if kind == "prefill_backward":
+        return gen_prefill(**cfg)
     if kind == "prefill":
         return gen_prefill(**cfg)
     if kind == "decode_gqa":
