@@ -202,9 +202,13 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
         flops = workloads.prefill_chunked_flops(w.Hq, w.Nq, w.kv_lens, w.D)
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
-        calls = [lambda: attn.attn_prefill_chunked(q, k, v, lens, w.scale, out=o, lse=lse)]
+        ws = torch.empty(attn.attn_prefill_chunked_workspace_bytes(w.B, w.Hq, w.Nq, w.kv_cap, w.D),
+                         dtype=torch.uint8, device=dev)
+        calls = [lambda: attn.attn_prefill_chunked(q, k, v, lens, w.scale, out=o, lse=lse, ws=ws)]
         work, unit, peak, bound = flops / 1e12, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS, "mfma"
-        kernel = "prefill_d128_kernel<true>"
+        kernel = "prefill_d128_kernel<true>" + (
+            " + merge_kernel" if attn.attn_prefill_chunked_workspace_bytes(
+                w.B, w.Hq, w.Nq, w.kv_cap, w.D) > 256 else "")
         nsteps = max(5, min(steps, int(1e14 // max(flops, 1))))
         if nsteps >= 20:
             nsteps -= nsteps % 20

@@ -141,18 +141,31 @@ size_t attn_prefill_causal_backward_workspace_bytes(int B, int Hq, int N, int D)
  *            lengths); each value must lie in [Nq, kv_cap] — values outside
  *            are clamped into that range, they are not reported.
  *
+ *   workspace  attn_prefill_chunked_workspace_bytes() bytes, 16-byte aligned
+ *            (contents on entry do not matter). When the chunk's query
+ *            tiles alone would leave compute units idle (short chunks), the
+ *            keys are split over several workgroups whose fp32 partials go
+ *            here and are merged through their log-sum-exp by a second
+ *            kernel on the same stream.
+ *
  * Query head hq uses K/V head hq / (Hq/Hkv). D must be 128. Nq = 1 is a
  * decode step; Nq = kv_lens[b] with kv_cap = Nq is attn_prefill_causal.
  * Errors: NULL pointer → ATTN_ERR_NULL_POINTER; B, Hq, Hkv, Nq < 1,
  * Hq % Hkv, Nq > kv_cap, a tensor above 2^31 elements, or a scale that is
  * not finite and positive → ATTN_ERR_BAD_SHAPE; other D → ATTN_ERR_UNSUPPORTED;
- * launch failure → ATTN_ERR_HIP.
+ * workspace NULL or too small → ATTN_ERR_WORKSPACE; launch failure →
+ * ATTN_ERR_HIP.
  */
 attn_status attn_prefill_chunked(const void *q, const void *k_cache,
                                  const void *v_cache, void *o, float *lse,
                                  const int *kv_lens, int B, int Hq, int Hkv,
                                  int Nq, int kv_cap, int D, float scale,
+                                 void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/* Bytes of workspace attn_prefill_chunked needs (0 if invalid). */
+size_t attn_prefill_chunked_workspace_bytes(int B, int Hq, int Nq, int kv_cap,
+                                            int D);
 
 /*
  * Single-query GQA decode over a bf16 K/V cache (no mask: the one query sees

@@ -29,7 +29,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -146,8 +146,9 @@ def test_decode_mla_validation(lib):
 
 
 def _chunked(lib, q=P, k=P, v=P, o=P, lse=P, lens=P, B=2, Hq=8, Hkv=2, Nq=100, kv_cap=512,
-             D=128, scale=0.1):
-    return lib.attn_prefill_chunked(q, k, v, o, lse, lens, B, Hq, Hkv, Nq, kv_cap, D, scale, None)
+             D=128, scale=0.1, ws=P, ws_bytes=1 << 30):
+    return lib.attn_prefill_chunked(q, k, v, o, lse, lens, B, Hq, Hkv, Nq, kv_cap, D, scale, ws,
+                                    ws_bytes, None)
 
 
 def test_prefill_chunked_validation(lib):
@@ -161,6 +162,11 @@ def test_prefill_chunked_validation(lib):
     assert _chunked(lib, lens=P + 2) == UNSUP            # misaligned length array
     for s in BAD_SCALES:
         assert _chunked(lib, scale=s) == SHAPE
+    # a short chunk over a long cache splits the keys and needs a workspace
+    need = attn.attn_prefill_chunked_workspace_bytes(1, 8, 100, 32768)
+    assert need > 1 << 20 and attn.attn_prefill_chunked_workspace_bytes(4, 32, 4096, 32768) == 256
+    assert _chunked(lib, B=1, kv_cap=32768, ws_bytes=need - 1) == WS
+    assert _chunked(lib, ws=None) == WS
 
 
 def _gqa_r(lib, q=P, k=P, v=P, o=P, lse=P, lens=P, B=2, Hq=8, Hkv=2, max_len=100, kv_cap=128,

@@ -39,7 +39,9 @@ def _chunked(gpu, w, lens=None):
     (1, 32, 8, 300, [1300], 1400),             # two query tiles, the second partial
     (3, 16, 4, 257, [257, 1000, 2048], 2048),  # mixed history lengths in one batch
     (1, 4, 4, 513, [4000], 4096),              # history not a multiple of the key tile
-    (2, 2, 1, 256, [256, 4096], 4100)])        # whole query tile, long history
+    (2, 2, 1, 256, [256, 4096], 4100),         # whole query tile, long history
+    (1, 8, 2, 16, [6000], 6000),               # a short chunk: keys split over 8 workgroups
+    (2, 4, 1, 100, [7000, 150], 7000)])        # split ranges that end before the chunk
 def test_prefill_chunked_matches_oracle(gpu, B, Hq, Hkv, Nq, lens, kv_cap):
     """Slots past each sequence's length hold NaN: a kernel that read them
     would fail the finiteness check."""

@@ -62,7 +62,9 @@ def load() -> ctypes.CDLL:
                                                      i, f, vp, sz, vp]
         lib.attn_prefill_causal_backward_workspace_bytes.argtypes = [i, i, i, i]
         lib.attn_prefill_causal_backward_workspace_bytes.restype = sz
-        lib.attn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+        lib.attn_prefill_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        lib.attn_prefill_chunked_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.attn_prefill_chunked_workspace_bytes.restype = sz
         lib.attn_decode_gqa_ragged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz,
                                                vp]
         lib.attn_decode_mla_ragged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
@@ -283,7 +285,11 @@ def _need_lens(kv_lens, B):
         raise ValueError("kv_lens must hold one length per sequence")
 
 
-def attn_prefill_chunked(q, k_cache, v_cache, kv_lens, scale=None, out=None, lse=None):
+def attn_prefill_chunked_workspace_bytes(B, Hq, Nq, kv_cap, D=128) -> int:
+    return int(load().attn_prefill_chunked_workspace_bytes(B, Hq, Nq, kv_cap, D))
+
+
+def attn_prefill_chunked(q, k_cache, v_cache, kv_lens, scale=None, out=None, lse=None, ws=None):
     """Chunked prefill against a cache. q [B,Hq,Nq,D] bf16; caches
     [B,Hkv,kv_cap,D] bf16 filled to kv_lens[b] (int32 GPU tensor [B], each
     in [Nq, kv_cap]), the last Nq slots being the chunk's own tokens.
@@ -303,9 +309,11 @@ def attn_prefill_chunked(q, k_cache, v_cache, kv_lens, scale=None, out=None, lse
     l = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
     _need(o, "out", torch.bfloat16, 4)
     _need(l, "lse", torch.float32, 3)
+    need = lib.attn_prefill_chunked_workspace_bytes(B, Hq, Nq, kv_cap, D)
+    w = workspace(need, q.device) if ws is None else ws
     st = lib.attn_prefill_chunked(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
                                   _ptr(kv_lens), B, Hq, Hkv, Nq, kv_cap, D, float(scale),
-                                  _stream(q.device))
+                                  _ptr(w), w.numel() * w.element_size(), _stream(q.device))
     _check(st, lib)
     return o, l
 

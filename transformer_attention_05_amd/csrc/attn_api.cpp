@@ -158,10 +158,16 @@ attn_status attn_prefill_causal(attn_dtype dtype, const void *q, const void *k,
                     "attn_prefill_causal");
 }
 
+size_t attn_prefill_chunked_workspace_bytes(int B, int Hq, int Nq, int kv_cap, int D)
+{
+    if (B < 1 || Hq < 1 || Nq < 1 || kv_cap < Nq || D != 128) return 0;
+    return attn::prefill_chunked_workspace_bytes(B, Hq, Nq, kv_cap);
+}
+
 attn_status attn_prefill_chunked(const void *q, const void *k_cache, const void *v_cache,
                                  void *o, float *lse, const int *kv_lens, int B, int Hq,
                                  int Hkv, int Nq, int kv_cap, int D, float scale,
-                                 hipStream_t stream)
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     static const char fn[] = "attn_prefill_chunked";
     if (!q || !k_cache || !v_cache || !o || !lse || !kv_lens)
@@ -181,8 +187,12 @@ attn_status attn_prefill_chunked(const void *q, const void *k_cache, const void 
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
         !aligned4(lse) || !aligned4(kv_lens))
         return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned (lse, kv_lens: 4)", fn);
+    const size_t need = attn::prefill_chunked_workspace_bytes(B, Hq, Nq, kv_cap);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
     return from_hip(attn::launch_prefill_chunked_d128(q, k_cache, v_cache, o, lse, kv_lens, B, Hq,
-                                                      Hkv, Nq, kv_cap, scale, stream),
+                                                      Hkv, Nq, kv_cap, scale, workspace, stream),
                     fn);
 }
 

@@ -32,9 +32,13 @@ hipError_t launch_prefill_bf16_d128(const void *q, const void *k, const void *v,
 // N queries per sequence against caches of kv_cap slots filled to kv_lens[b]
 // (a device array, clamped to [N, kv_cap]); the queries are the last N
 // positions (bottom-right causal mask).
+// Short chunks split the keys over several workgroups (fp32 partials in ws,
+// prefill_chunked_workspace_bytes(), merged through the LSE).
+int prefill_chunked_splits(int B, int Hq, int Nq, int kv_cap);
+size_t prefill_chunked_workspace_bytes(int B, int Hq, int Nq, int kv_cap);
 hipError_t launch_prefill_chunked_d128(const void *q, const void *k, const void *v, void *o,
                                        float *lse, const int *kv_lens, int B, int Hq, int Hkv,
-                                       int N, int kv_cap, float scale, hipStream_t s);
+                                       int N, int kv_cap, float scale, void *ws, hipStream_t s);
 // Backward of the causal prefill, d = 128, bf16; ws holds B·Hq·N fp32 (D = dO·O).
 size_t prefill_bwd_workspace_bytes(int B, int Hq, int N);
 hipError_t launch_prefill_bwd_d128(const void *q, const void *k, const void *v, const void *o,

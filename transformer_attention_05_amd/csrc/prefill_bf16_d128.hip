@@ -108,12 +108,16 @@ __device__ __forceinline__ uint32_t tile_src(int idx, int lane, int slots, int r
 // (rows of N slots). CHUNK = true: K/V are caches of kv_cap slots per (batch,
 // K/V head) filled to kv_lens[b], whose last N entries are the queries' own
 // positions, so query i sits at position kv_lens[b] − N + i.
+// CHUNK with gridDim.y = S > 1: workgroup (item, s) takes the s-th of S
+// contiguous ranges of its query tile's key tiles and writes an fp32 partial
+// (m, ℓ, λ, Õ) to ws_ml / ws_part ([row][s], row = bhq·N + query) for the
+// LSE merge, instead of O and the LSE.
 template <bool CHUNK>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
     int Hq, int Hkv, int N, int n_qtiles, float scale_log2, int kv_cap,
-    const int *__restrict__ kv_lens)
+    const int *__restrict__ kv_lens, float *__restrict__ ws_ml, float *__restrict__ ws_part)
 {
     __shared__ __attribute__((aligned(1024))) char kt[NBUF][KTILEB];
     __shared__ __attribute__((aligned(1024))) char vt[NBUF][VTILEB];
@@ -208,11 +212,18 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     const int v_lane = (4 * half + e) * VROWB + 32 * (g & 1) + 8 * cq;
 
     const int n_kt = min(kv_len - 1, q_off + q0 + BR - 1) / BC + 1;
+    // key tiles [t_lo, t_hi) of this workgroup (a split's share, or all)
+    int t_lo = 0, t_hi = n_kt;
+    const int S = CHUNK ? (int)gridDim.y : 1, split = CHUNK ? (int)blockIdx.y : 0;
+    if constexpr (CHUNK) {
+        t_lo = (int)((long)split * n_kt / S);
+        t_hi = (int)((long)(split + 1) * n_kt / S);
+    }
 #pragma unroll
     for (int t = 0; t < NBUF - 1; ++t)
-        if (t < n_kt) load_tile(t, t);
-    // tile 0 resident: only the loads of tiles 1 .. NBUF-2 may be outstanding
-    if (NBUF == 3 && n_kt > 1) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
+        if (t_lo + t < t_hi) load_tile(t_lo + t, t);
+    // the first tile resident: only the loads of later tiles may be outstanding
+    if (NBUF == 3 && t_hi - t_lo > 1) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
     __syncthreads();
 
     // One key tile for this wave: Sᵀ, online softmax, Oᵀ update. MASK is set
@@ -258,7 +269,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
 #endif
         if (__builtin_amdgcn_ballot_w64(move)) {
             const float m_new = move ? m_tile : m_ref;
-            const float alpha = exp2_fast(m_ref - m_new);  // 1 where not moved, 0 at first
+            float alpha = exp2_fast(m_ref - m_new);  // 1 where not moved, 0 at first
+            // a split's range can begin at a diagonal tile whose keys all lie
+            // after some rows of the wave: those rows have seen no key yet
+            // (reference −∞ on both sides), and their empty sums stay empty
+            if (CHUNK && m_new == -INFINITY) alpha = 1.f;
             l_run *= alpha;
             lq_run *= alpha;
 #pragma unroll
@@ -270,7 +285,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = exp2_fast(fmaf(sacc[kb][i], scale_log2, -m_ref));
+                // (rows that have seen no key: every score −∞, weight 0)
+                const float p = exp2_fast(fmaf(sacc[kb][i], scale_log2,
+                                               CHUNK && m_ref == -INFINITY ? 0.f : -m_ref));
                 sacc[kb][i] = p;
                 ps += p;
             }
@@ -319,19 +336,19 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     // (in a ragged last query tile the waves past the last query run the
     // bulk tiles too; their rows are never written)
     const int n_bulk = ATTN_PF_BULK ? (q_off + q0 + 1) / BC : 0;
-    for (int j = 0; j < n_bulk; ++j) {
-        const int cur = j % NBUF;
+    for (int j = t_lo; j < min(n_bulk, t_hi); ++j) {
+        const int cur = (j - t_lo) % NBUF;
         const int jn = j + NBUF - 1;  // tile to prefetch
-        if (jn < n_kt) load_tile(jn, jn % NBUF);
+        if (jn < t_hi) load_tile(jn, (jn - t_lo) % NBUF);
         tile_step(kt[cur], vt[cur], j * BC, std::false_type{});
-        if (NBUF == 3 && jn < n_kt) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
+        if (NBUF == 3 && jn < t_hi) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
         __syncthreads();
     }
     // Tail: the tiles around the diagonal, classified per wave.
-    for (int j = n_bulk; j < n_kt; ++j) {
-        const int cur = j % NBUF;
+    for (int j = max(n_bulk, t_lo); j < t_hi; ++j) {
+        const int cur = (j - t_lo) % NBUF;
         const int jn = j + NBUF - 1;  // tile to prefetch
-        if (jn < n_kt) load_tile(jn, jn % NBUF);
+        if (jn < t_hi) load_tile(jn, (jn - t_lo) % NBUF);
         const int kt0 = j * BC;
 #if ATTN_PF_SPLITMASK
         if (wrow0 < N && kt0 + BC - 1 <= wrow0 + q_off)  // wholly visible to the wave
@@ -342,12 +359,31 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         if (wrow0 < N && kt0 <= wrow1 + q_off) tile_step(kt[cur], vt[cur], kt0, std::true_type{});
 #endif
         // tile j+1 resident before the barrier; newer prefetches may stay in flight
-        if (NBUF == 3 && jn < n_kt) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
+        if (NBUF == 3 && jn < t_hi) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
         __syncthreads();
     }
 
     // ---- epilogue: O = Oᵀ/ℓq, one rounding; LSE (natural log) from the fp32 sum
     const float l_tot = half_sum(l_run), lq_tot = half_sum(lq_run);
+    if (CHUNK && S > 1) {
+        // partial of this key range: Õ relative to m_ref (rows that saw no
+        // key here: m = −∞, sums and Õ zero), merged through the LSE later
+        if (qrow < N) {
+            const size_t slot = ((size_t)bhq * N + qrow) * S + split;
+            float *prow = ws_part + slot * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    const f32x4 w4 = {oacc[db][4 * gg], oacc[db][4 * gg + 1], oacc[db][4 * gg + 2],
+                                      oacc[db][4 * gg + 3]};
+                    __builtin_nontemporal_store(w4, (f32x4 *)(prow + db * 32 + 8 * gg + 4 * half));
+                }
+            if (half == 0)
+                *(float4 *)(ws_ml + 4 * slot) = make_float4(m_ref, l_tot, ATTN_PF_LAZY ? lq_tot : l_tot, 0.f);
+        }
+        return;
+    }
     if (qrow < N) {
         const float inv = 1.f / (ATTN_PF_LAZY ? lq_tot : l_tot);
         uint16_t *orow = o + ((size_t)bhq * N + qrow) * D;
@@ -373,20 +409,47 @@ hipError_t launch_prefill_bf16_d128(const void *q, const void *k, const void *v,
     const dim3 grid((unsigned)(n_qtiles * B * Hq)), block(64 * NW);
     prefill_d128_kernel<false><<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, Hq,
-        Hkv, N, n_qtiles, scale * kLog2e, N, nullptr);
+        Hkv, N, n_qtiles, scale * kLog2e, N, nullptr, nullptr, nullptr);
     return hipGetLastError();
+}
+
+// Key splits of a chunked prefill: one unless the query tiles alone leave
+// CUs idle (fewer than 256 workgroups); then enough splits for ≈ 512
+// workgroups, each keeping at least 8 key tiles of the longest cache.
+int prefill_chunked_splits(int B, int Hq, int Nq, int kv_cap)
+{
+    const long items = (long)B * Hq * ((Nq + BR - 1) / BR);
+    if (items >= 256) return 1;
+    const long tiles = (kv_cap + BC - 1) / BC;
+    long s = (512 + items - 1) / items;
+    s = s < tiles / 8 ? s : tiles / 8;
+    s = s < kMaxSplits ? s : kMaxSplits;
+    return s < 1 ? 1 : (int)s;
+}
+
+size_t prefill_chunked_workspace_bytes(int B, int Hq, int Nq, int kv_cap)
+{
+    const int S = prefill_chunked_splits(B, Hq, Nq, kv_cap);
+    if (S == 1) return 256;
+    const size_t slots = (size_t)B * Hq * Nq * S;
+    return align_up(16 * slots, 256) + align_up(sizeof(float) * D * slots, 256);
 }
 
 hipError_t launch_prefill_chunked_d128(const void *q, const void *k, const void *v, void *o,
                                        float *lse, const int *kv_lens, int B, int Hq, int Hkv,
-                                       int Nq, int kv_cap, float scale, hipStream_t st)
+                                       int Nq, int kv_cap, float scale, void *ws, hipStream_t st)
 {
     const int n_qtiles = (Nq + BR - 1) / BR;
-    const dim3 grid((unsigned)(n_qtiles * B * Hq)), block(64 * NW);
+    const int S = prefill_chunked_splits(B, Hq, Nq, kv_cap);
+    const size_t slots = (size_t)B * Hq * Nq * S;
+    float *ws_ml = (float *)ws, *ws_part = (float *)((char *)ws + align_up(16 * slots, 256));
+    const dim3 grid((unsigned)(n_qtiles * B * Hq), (unsigned)S), block(64 * NW);
     prefill_d128_kernel<true><<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, Hq,
-        Hkv, Nq, n_qtiles, scale * kLog2e, kv_cap, kv_lens);
-    return hipGetLastError();
+        Hkv, Nq, n_qtiles, scale * kLog2e, kv_cap, kv_lens, ws_ml, ws_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    return launch_merge(ws_ml, ws_part, o, lse, B * Hq * Nq, S, D, st);
 }
 
 }  // namespace attn

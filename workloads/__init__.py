@@ -363,6 +363,9 @@ WORKLOADS = {
     "prefill_chunked_4k_on_32k": dict(
         kind="prefill_chunked", B=1, Hq=32, Hkv=8, Nq=4096, kv_lens=32768, D=128,
         seed=1006, scale=1.0 / math.sqrt(128)),
+    "prefill_chunked_512_on_32k": dict(
+        kind="prefill_chunked", B=1, Hq=32, Hkv=8, Nq=512, kv_lens=32768, D=128,
+        seed=1011, scale=1.0 / math.sqrt(128)),
     "decode_gqa_ragged_8k": dict(
         kind="decode_gqa", B=32, Hq=32, Hkv=8, kv_lens=("ragged", 128, 8192, 1107),
         kv_cap=8192, D=128, seed=1007, scale=1.0 / math.sqrt(128)),
