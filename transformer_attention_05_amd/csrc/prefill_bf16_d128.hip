@@ -70,12 +70,15 @@ namespace {
 #ifndef ATTN_PF_SCHED
 #define ATTN_PF_SCHED 0      // keep each 16-key step's transposed reads together
 #endif
+#ifndef ATTN_PF_PAIR
+#define ATTN_PF_PAIR 1       // bulk tiles two per barrier, ring of 4 tiles
+#endif
 #ifndef ATTN_PF_BULK
 #define ATTN_PF_BULK 1       // separate loop for the tiles wholly visible to every wave
 #endif
 
 
-constexpr int NW = ATTN_PF_WAVES, NBUF = ATTN_PF_NBUF;
+constexpr int NW = ATTN_PF_WAVES, NBUF = ATTN_PF_PAIR ? 4 : ATTN_PF_NBUF;
 constexpr int D = 128, BR = 32 * NW, BC = 64;
 constexpr int KROWB = 272, VROWB = ATTN_PF_VROWB;   // padded LDS row strides (bytes)
 constexpr int KSLOT = KROWB / 16, VSLOT = VROWB / 16;
@@ -219,11 +222,18 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         t_lo = (int)((long)split * n_kt / S);
         t_hi = (int)((long)(split + 1) * n_kt / S);
     }
+    if (ATTN_PF_PAIR) {
+        // the first two tiles resident
+        for (int t = 0; t < 2; ++t)
+            if (t_lo + t < t_hi) load_tile(t_lo + t, t);
+        wait_vmcnt<0>();
+    } else {
 #pragma unroll
-    for (int t = 0; t < NBUF - 1; ++t)
-        if (t_lo + t < t_hi) load_tile(t_lo + t, t);
-    // the first tile resident: only the loads of later tiles may be outstanding
-    if (NBUF == 3 && t_hi - t_lo > 1) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
+        for (int t = 0; t < NBUF - 1; ++t)
+            if (t_lo + t < t_hi) load_tile(t_lo + t, t);
+        // the first tile resident: only the loads of later tiles may be outstanding
+        if (NBUF == 3 && t_hi - t_lo > 1) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
+    }
     __syncthreads();
 
     // One key tile for this wave: Sᵀ, online softmax, Oᵀ update. MASK is set
@@ -336,6 +346,39 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     // (in a ragged last query tile the waves past the last query run the
     // bulk tiles too; their rows are never written)
     const int n_bulk = ATTN_PF_BULK ? (q_off + q0 + 1) / BC : 0;
+#if ATTN_PF_PAIR
+    // Bulk tiles two at a time, one barrier per pair: the next pair's copies
+    // go into the two buffers the last barrier freed while this pair is
+    // computed (ring of 4).
+    int j = t_lo;
+    const int bulk_end = min(n_bulk, t_hi);
+    for (; j + 1 < bulk_end; j += 2) {
+        if (j + 2 < t_hi) load_tile(j + 2, (j + 2 - t_lo) & 3);
+        if (j + 3 < t_hi) load_tile(j + 3, (j + 3 - t_lo) & 3);
+        tile_step(kt[(j - t_lo) & 3], vt[(j - t_lo) & 3], j * BC, std::false_type{});
+        tile_step(kt[(j + 1 - t_lo) & 3], vt[(j + 1 - t_lo) & 3], (j + 1) * BC, std::false_type{});
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+    // The rest (a last bulk tile, then the tiles around the diagonal,
+    // classified per wave), one per barrier: tiles j and j + 1 are resident
+    // or in flight on entry; tile j + 2 is fetched two steps ahead.
+    for (; j < t_hi; ++j) {
+        const int cur = (j - t_lo) & 3;
+        const bool ahead = j + 2 < t_hi;
+        if (ahead) load_tile(j + 2, (j + 2 - t_lo) & 3);
+        const int kt0 = j * BC;
+        if (j < n_bulk)
+            tile_step(kt[cur], vt[cur], kt0, std::false_type{});
+        else if (wrow0 < N && kt0 + BC - 1 <= wrow0 + q_off)  // wholly visible to the wave
+            tile_step(kt[cur], vt[cur], kt0, std::false_type{});
+        else if (wrow0 < N && kt0 <= wrow1 + q_off)      // crosses the wave's diagonal
+            tile_step(kt[cur], vt[cur], kt0, std::true_type{});
+        // tile j + 1 resident before the barrier; tile j + 2 may stay in flight
+        if (ahead) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
+        __syncthreads();
+    }
+#else
     for (int j = t_lo; j < min(n_bulk, t_hi); ++j) {
         const int cur = (j - t_lo) % NBUF;
         const int jn = j + NBUF - 1;  // tile to prefetch
@@ -362,6 +405,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         if (NBUF == 3 && jn < t_hi) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
         __syncthreads();
     }
+
+#endif
 
     // ---- epilogue: O = Oᵀ/ℓq, one rounding; LSE (natural log) from the fp32 sum
     const float l_tot = half_sum(l_run), lq_tot = half_sum(lq_run);
