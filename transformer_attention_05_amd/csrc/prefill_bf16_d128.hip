@@ -4,8 +4,9 @@
 // each wave owns 32 query rows and keeps their Q fragments in registers for
 // the whole pass (Q outer, K/V inner: the loop order "AI Infra 入门…", §3
 // credits to FlashAttention-2). 64-key K and V tiles stream HBM → LDS with
-// global_load_lds_dwordx4 one tile ahead of use (double-buffered, no register
-// staging), both row-major with padded rows: K rows take 272 B (16 B pad) so
+// global_load_lds_dwordx4 two tiles ahead of use (a ring of four, no register
+// staging; the bulk tiles take one barrier per pair), both row-major with
+// padded rows: K rows take 272 B (16 B pad) so
 // the rows of a score read start 4 banks apart, V rows take 320 B (64 B pad)
 // so the 8 rows × 32 B that one 32-lane phase of a transposed read touches
 // fall on distinct banks (both measured conflict-free). With padding (rather than a swizzle) every LDS read address is a
