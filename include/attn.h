@@ -283,10 +283,10 @@ size_t attn_decode_mla_workspace_bytes(int B, int Hq, int kv_len, int Dqk,
  * sequence b's latent cache filled to kv_lens[b] (DEVICE int32 [B], read at
  * run time, clamped to [0, max_kv_len]; length 0 gives O = 0, LSE = −∞).
  * The work is split evenly over the 32-key tiles of all sequences together
- * (one workgroup per compute unit, each taking an equal run of tiles, across
- * sequence boundaries), so short and long sequences in one batch keep the
- * whole GPU busy; the split is recomputed on the device from kv_lens on
- * every call. max_kv_len (the longest length, or a bound of it, at most
+ * (equal runs of tiles across sequence boundaries, one workgroup per piece
+ * of a run within one sequence), so short and long sequences in one batch
+ * keep the whole GPU busy; the split is recomputed on the device from
+ * kv_lens on every call. max_kv_len (the longest length, or a bound of it, at most
  * kv_cap) bounds the lengths. Workspace: attn_decode_mla_ragged_workspace_bytes().
  * Errors as for attn_decode_mla_absorbed with max_kv_len in the place of
  * kv_len; kv_lens NULL → ATTN_ERR_NULL_POINTER.

@@ -51,13 +51,14 @@
 // (non-temporal) stores that do not stay dirty in L2; the shared merge kernel
 // combines them through their log-sum-exp. Rows at or past kv_len are never
 // read.
-// Ragged batches (per-sequence lengths in device memory): one workgroup per
-// CU, each taking an equal run of the 32-key tiles of all sequences in batch
-// order (ragged.h), so a mix of short and long sequences keeps every CU
-// busy; a run that crosses sequence boundaries produces one partial per
-// sequence, and the merge finds a row's partials from the same arithmetic.
-// The residual product is switched on per segment for sequences of at most
-// kLoMaxKeys keys. A sequence with no key gets O = 0 and LSE = −∞.
+// Ragged batches (per-sequence lengths in device memory): the 32-key tiles of
+// all sequences, in batch order, are cut into P equal runs (ragged.h), so a
+// mix of short and long sequences keeps every CU busy; each piece of a run
+// that lies in one sequence is one workgroup (P + B of them, all resident at
+// once) writing one partial, and the merge finds a row's partials from the
+// same arithmetic. The residual product is switched on per piece for
+// sequences of at most kLoMaxKeys keys. A sequence with no key gets O = 0
+// and LSE = −∞.
 #include "common.h"
 #include "launch.h"
 #include "ragged.h"
