@@ -48,6 +48,37 @@ def test_decode_gqa_llama3_workload_and_repeat(gpu):
     check_bf16(host(outs[0][0]), o_ref, host(outs[0][1]), lse_ref, "decode_gqa_llama3_8b_4k")
 
 
+def test_decode_gqa_workspace_contents_do_not_matter(gpu):
+    """Nothing in the workspace is read before the call writes it: a
+    workspace holding random bytes, all ones, zeros, or what a call of
+    another shape left in it gives the same bits as a fresh one, call after
+    call."""
+    w = workloads.gen_decode_gqa(2, 32, 8, 3000, D=128, kv_cap=3072, seed=5)
+    q, k, v = dev_bf16(w.q), dev_bf16(w.k), dev_bf16(w.v)
+    o_ref, l_ref = gpu.attn_decode_gqa(q, k, v, w.kv_len, w.scale)
+    need = gpu.attn_decode_gqa_workspace_bytes(2, 32, 8, 3000)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    w2 = workloads.gen_decode_gqa(1, 8, 2, 2000, D=128, seed=6)
+    gen = torch.Generator().manual_seed(7)
+    for fill in ("random", "ones", "zeros", "other call"):
+        if fill == "random":
+            ws.copy_(torch.randint(0, 256, (need,), generator=gen, dtype=torch.uint8))
+        elif fill == "ones":
+            ws.fill_(255)
+        elif fill == "zeros":
+            ws.zero_()
+        else:
+            gpu.attn_decode_gqa(dev_bf16(w2.q), dev_bf16(w2.k), dev_bf16(w2.v), w2.kv_len, w2.scale,
+                                ws=ws)
+        for rep in range(2):
+            o, l = gpu.attn_decode_gqa(q, k, v, w.kv_len, w.scale, ws=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), (fill, rep)
+            assert torch.equal(l, l_ref), (fill, rep)
+    o_or, l_or = oracle.decode_gqa(w.q, w.k, w.v, w.kv_len, w.scale)
+    check_bf16(host(o_ref), o_or, host(l_ref), l_or, "gqa workspace")
+
+
 def test_decode_matches_prefill_rows(gpu):
     """A cached decode step for token t equals row t of a causal prefill over
     the same tokens (earlier rows never see later tokens)."""
