@@ -279,6 +279,27 @@ size_t attn_decode_mla_workspace_bytes(int B, int Hq, int kv_len, int Dqk,
                                        int Dv);
 
 /*
+ * Absorbed MLA decode over an FP8 latent cache: as attn_decode_mla_absorbed,
+ * but ckv holds OCP FP8 E4M3 codes, one byte per element ([B, kv_cap, Dqk]
+ * bytes; sign, 4-bit exponent with bias 7, 3-bit mantissa, largest finite
+ * 448, S.1111.111 = NaN). The stored rows must be the channel-balanced
+ * latent S·c ("MLA 矩阵乘法吸收的数值稳定性治理", §二.1: the static channel
+ * scale S brings every latent channel into a common range; raw latent
+ * channels span orders of magnitude that E4M3 cannot hold), with the query
+ * in bf16 carrying S⁻¹. Each cached value enters the products exactly
+ * (converted to bf16 without rounding) and every product accumulates in
+ * fp32 (§五: low-precision storage, fp32 accumulation), so only the bytes
+ * read from HBM halve. O is returned in the S-scaled latent space.
+ * Workspace: attn_decode_mla_workspace_bytes() of the same shape.
+ * Errors as for attn_decode_mla_absorbed.
+ */
+attn_status attn_decode_mla_fp8(const void *q, const void *ckv, void *o,
+                                float *lse, int B, int Hq, int kv_len,
+                                int kv_cap, int Dqk, int Dv, float scale,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * Absorbed MLA decode of a ragged batch: as attn_decode_mla_absorbed, with
  * sequence b's latent cache filled to kv_lens[b] (DEVICE int32 [B], read at
  * run time, clamped to [0, max_kv_len]; length 0 gives O = 0, LSE = −∞).

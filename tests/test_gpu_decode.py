@@ -186,3 +186,42 @@ def test_decode_gqa_fp8_workload_equals_bf16_copy_of_its_values(gpu):
     o_ref, lse_ref = oracle.decode_gqa(w.q, w.k, w.v, w.kv_len, w.scale)
     check_bf16(host(o8), o_ref, host(l8), lse_ref, "decode_gqa_fp8_llama3_8b_4k")
     check_bf16(host(ob), o_ref, host(lb), lse_ref, "bf16 copy of the E4M3 values")
+
+
+@pytest.mark.parametrize("B,Hq,kv_len,kv_cap", [
+    (1, 16, 1, 32), (4, 128, 2, 8), (2, 64, 3, 3), (2, 16, 31, 64), (1, 128, 33, 40),
+    (2, 64, 512, 520), (2, 64, 513, 520), (2, 32, 1000, 1024), (1, 128, 5000, 5000),
+    (1, 144, 70, 100)])
+def test_decode_mla_fp8_matches_oracle(gpu, B, Hq, kv_len, kv_cap):
+    """E4M3 latent cache (balanced rows S·c, the NaN code past kv_len):
+    partial tiles, 16..144 heads (partial head groups), one and many splits,
+    both sides of the 512-key weight-residual cut. The oracle reads the same
+    codes."""
+    w = workloads.gen_decode_mla(B, Hq, kv_len, kv_cap=kv_cap, seed=kv_len + 5 * Hq,
+                                 cache_dtype="fp8")
+    o, lse = gpu.attn_decode_mla_fp8(dev_bf16(w.q), _dev_u8(w.ckv), kv_len, w.Dv, w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_mla_absorbed(w.q, w.ckv, kv_len, w.Dv, w.scale)
+    check_bf16(host(o), o_ref, host(lse), lse_ref, "mla fp8 %s" % ((B, Hq, kv_len),))
+
+
+def test_decode_mla_fp8_32k_workload(gpu):
+    """The 32K MLA workload over an E4M3 cache: every output finite, two
+    batches against the oracle, and the same bits as the bf16 kernel given a
+    bf16 copy of the cached values (every E4M3 value is a bf16 value; the
+    two paths feed the same operands to the same products in the same
+    order, so this checks the E4M3 tile layout and its transposed reads
+    element for element)."""
+    w = workloads.make("decode_mla_fp8_32k")
+    q = dev_bf16(w.q)
+    o8, l8 = gpu.attn_decode_mla_fp8(q, _dev_u8(w.ckv), w.kv_len, w.Dv, w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o8.float()).all()) and bool(torch.isfinite(l8).all())
+    c16 = torch.from_numpy(w.ckv).to("cuda").view(torch.float8_e4m3fn).to(torch.bfloat16)
+    o16, l16 = gpu.attn_decode_mla_absorbed(q, c16, w.kv_len, w.Dv, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o8.view(torch.int16), o16.view(torch.int16))
+    assert torch.equal(l8, l16)
+    bs = [0, w.B - 1]
+    o_ref, lse_ref = oracle.decode_mla_absorbed(w.q[bs], w.ckv[bs], w.kv_len, w.Dv, w.scale)
+    check_bf16(host(o8[bs]), o_ref, host(l8[bs]), lse_ref, "decode_mla_fp8_32k")

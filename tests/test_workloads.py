@@ -2,6 +2,7 @@
 import numpy as np
 import torch
 
+import oracle
 import workloads
 
 
@@ -92,3 +93,26 @@ def test_fp8_decode_cache_poison_and_dtype():
     assert w.k.dtype == np.uint8 and w.v.dtype == np.uint8 and w.q.dtype == np.uint16
     assert np.all(w.k[:, :, 10:] == workloads.E4M3_NAN_BITS)
     assert np.all(w.k[:, :, :10] != workloads.E4M3_NAN_BITS)
+
+
+def test_channel_scale_makes_latent_fit_e4m3():
+    """The static channel scale S is what lets the MLA latent live in E4M3
+    ("MLA 矩阵乘法吸收的数值稳定性治理", §二.1). The raw latent c (channel
+    magnitudes over six decades) overflows E4M3's largest finite value, 448,
+    in a large share of its entries; the balanced S·c that is stored never
+    does, and every balanced entry in E4M3's normal range (≥ 2^-6) keeps a
+    relative error of at most 2^-4 (3 mantissa bits, round to nearest)."""
+    w = workloads.gen_decode_mla(1, 16, 2000, seed=4)
+    bal = oracle.widen(w.ckv[0, :, :w.Dv])      # stored S·c (bf16)
+    raw = bal / w.s                              # the model's latent c
+    assert np.mean(np.abs(raw) > 448.0) > 0.1
+    assert np.abs(bal).max() < 448.0
+    q = oracle.widen(workloads.round_to_e4m3_bits(bal))
+    normal = np.abs(bal) >= 2.0 ** -6
+    assert normal.mean() > 0.98          # N(0,1): about 1.2 % lie below 2^-6
+    assert np.all(np.abs(q - bal)[normal] <= 2.0 ** -4 * np.abs(bal)[normal])
+    # the E4M3 generator rounds the same balanced draws (from fp64, so within
+    # half an E4M3 step of them, plus the bf16 copy's own rounding)
+    w8 = workloads.gen_decode_mla(1, 16, 2000, seed=4, cache_dtype="fp8")
+    q8 = oracle.widen(w8.ckv[0, :, :w.Dv])
+    assert np.all(np.abs(q8 - bal) <= 2.0 ** -4 * np.abs(bal) + 2.0 ** -10)

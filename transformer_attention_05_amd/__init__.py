@@ -12,6 +12,7 @@ no fallback: if libattn.so is missing or fails to load, every call raises.
     o, lse = attn_decode_gqa_ragged(q, k_cache, v_cache, kv_lens, max_kv_len, scale)
     o, lse = attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, 512, scale)
     o, lse = attn_decode_gqa_fp8(q, k_fp8, v_fp8, kv_len, scale)   # E4M3 caches (uint8)
+    o, lse = attn_decode_mla_fp8(q, ckv_fp8, kv_len)                 # E4M3 latent cache
     dq, dk, dv = attn_prefill_causal_backward(q, k, v, o, lse, dout, scale)
 (kv_lens: an int32 GPU tensor of per-sequence lengths, read by the kernels.)
 """
@@ -58,6 +59,7 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_mla_absorbed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_gqa_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        lib.attn_decode_mla_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_prefill_causal_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
                                                      i, f, vp, sz, vp]
         lib.attn_prefill_causal_backward_workspace_bytes.argtypes = [i, i, i, i]
@@ -77,7 +79,7 @@ def load() -> ctypes.CDLL:
         for fn in (lib.attn_prefill_causal, lib.attn_decode_gqa, lib.attn_decode_mla_absorbed,
                    lib.attn_prefill_chunked, lib.attn_decode_gqa_ragged, lib.attn_decode_gqa_fp8,
                    lib.attn_prefill_causal_backward,
-                   lib.attn_decode_mla_ragged):
+                   lib.attn_decode_mla_ragged, lib.attn_decode_mla_fp8):
             fn.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
@@ -275,6 +277,33 @@ def attn_decode_mla_absorbed(q, ckv, kv_len, dv=512, scale=None, out=None, lse=N
     st = lib.attn_decode_mla_absorbed(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), B, Hq, int(kv_len),
                                       kv_cap, Dqk, dv, float(scale), _ptr(w),
                                       w.numel() * w.element_size(), _stream(q.device))
+    _check(st, lib)
+    return o, l
+
+
+def attn_decode_mla_fp8(q, ckv, kv_len, dv=512, scale=None, out=None, lse=None, ws=None):
+    """Absorbed MLA decode over an FP8 E4M3 latent cache. q [B,Hq,Dqk] bf16
+    (absorbed, channel-balanced query | rope); ckv [B,kv_cap,Dqk]
+    torch.uint8 (E4M3 codes of the balanced latent | rope) or
+    torch.float8_e4m3fn. Returns (o [B,Hq,dv] bf16, lse [B,Hq] fp32)."""
+    lib = load()
+    _need(q, "q", torch.bfloat16, 3)
+    _need(ckv.view(torch.uint8) if ckv.dtype == torch.float8_e4m3fn else ckv, "ckv", torch.uint8, 3)
+    B, Hq, Dqk = q.shape
+    kv_cap = ckv.shape[1]
+    if ckv.shape != (B, kv_cap, Dqk):
+        raise ValueError("ckv must be [B, kv_cap, Dqk] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(128 + 64)
+    o = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "out", torch.bfloat16, 3)
+    _need(l, "lse", torch.float32, 2)
+    need = lib.attn_decode_mla_workspace_bytes(B, Hq, int(kv_len), Dqk, dv)
+    w = workspace(need, q.device) if ws is None else ws
+    st = lib.attn_decode_mla_fp8(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), B, Hq, int(kv_len), kv_cap,
+                                 Dqk, dv, float(scale), _ptr(w), w.numel() * w.element_size(),
+                                 _stream(q.device))
     _check(st, lib)
     return o, l
 

@@ -80,7 +80,7 @@ attn_status decode_gqa_impl(const char *fn, const void *q, const void *k_cache,
 attn_status decode_mla_impl(const char *fn, const void *q, const void *ckv, void *o, float *lse,
                             const int *kv_lens, int B, int Hq, int kv_len, int kv_cap, int Dqk,
                             int Dv, float scale, void *workspace, size_t workspace_bytes,
-                            hipStream_t stream)
+                            hipStream_t stream, bool fp8 = false)
 {
     const char *len_name = kv_lens ? "max_kv_len" : "kv_len";
     if (B < 1 || Hq < 1 || Dqk < 1 || Dv < 1 || Dv > Dqk)
@@ -107,7 +107,7 @@ attn_status decode_mla_impl(const char *fn, const void *q, const void *ckv, void
         return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, p.ws_total,
                     workspace ? workspace_bytes : (size_t)0);
     return from_hip(attn::launch_decode_mla(p, q, ckv, o, lse, B, Hq, kv_len, kv_cap, scale,
-                                            workspace, stream, kv_lens),
+                                            workspace, stream, kv_lens, fp8),
                     fn);
 }
 
@@ -292,6 +292,16 @@ attn_status attn_decode_mla_absorbed(const void *q, const void *ckv, void *o, fl
         return fail(ATTN_ERR_NULL_POINTER, "attn_decode_mla_absorbed: NULL tensor pointer");
     return decode_mla_impl("attn_decode_mla_absorbed", q, ckv, o, lse, nullptr, B, Hq, kv_len,
                            kv_cap, Dqk, Dv, scale, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_mla_fp8(const void *q, const void *ckv, void *o, float *lse, int B,
+                                int Hq, int kv_len, int kv_cap, int Dqk, int Dv, float scale,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!q || !ckv || !o || !lse)
+        return fail(ATTN_ERR_NULL_POINTER, "attn_decode_mla_fp8: NULL tensor pointer");
+    return decode_mla_impl("attn_decode_mla_fp8", q, ckv, o, lse, nullptr, B, Hq, kv_len, kv_cap,
+                           Dqk, Dv, scale, workspace, workspace_bytes, stream, true);
 }
 
 size_t attn_decode_mla_ragged_workspace_bytes(int B, int Hq, int max_kv_len, int Dqk, int Dv)

@@ -86,11 +86,26 @@ constexpr int MTHREADS = 64 * MW;
 constexpr int kTargetGroups = 256;
 constexpr float kLazy = 8.f;      // reference-max slack, log2 units
 constexpr int kLoMaxKeys = 512;   // caches this short get the second P product
+
+// Tile geometry of the bf16 cache (F8 = false) and of the E4M3 cache (one
+// byte per element: rows, tiles and copies halve).
+template <bool F8>
+struct MGeo {
+    static constexpr int ROWB = F8 ? MD : MROWB;           // bytes per latent row
+    static constexpr int CH = ROWB / 16;                   // 16-byte chunks per row
+    static constexpr int TILEB = MBC * ROWB;               // bytes per tile
+    static constexpr int LOADS = TILEB / 1024;             // wave-wide 1 KiB copies per tile
+    static constexpr int LOADS_HI = (LOADS + MW - 1) / MW; // copies of waves < LOADS % MW
+    static constexpr int LOADS_LO = LOADS / MW;            // copies of the other waves
+};
+static_assert(MGeo<true>::LOADS * 1024 == MGeo<true>::TILEB, "whole copies");
 // LDS: tile ring, weights (hi and lo), per-head factors, LDS-held Q fragments
 static_assert(MNBUF * MTILEB + 2 * MHB * 1024 + MH * 4 + MKQ * MW * 1024 <= 160 * 1024, "LDS");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_v2i32;
 
 // HBM → LDS like copy_to_lds16, addressed as a wave-uniform base plus a
 // per-lane 32-bit byte offset (the scalar-base form of the instruction), so
@@ -105,11 +120,34 @@ __device__ __forceinline__ int swz(int r, int c) {
     return (c & ~7) | ((c & 7) ^ (r & 7) ^ ((r >> 4) & 1));
 }
 
+// E4M3 tile rows (576 B = 36 chunks): the low two bits of the chunk index
+// are XORed with bit 2 of the row and with bit 3 ^ bit 4 of the row. A score
+// read takes one chunk of 16 consecutive rows (0–15 or 16–31) per 32-lane
+// phase and a transposed value read one chunk of rows {0–7, 16–23} or
+// {8–15, 24–31}; in both, the rows that fall on the same banks (equal
+// row mod 4, rows being 36 chunks apart) get four different XOR values.
+__device__ __forceinline__ int swz8(int r, int c) {
+    return c ^ (((r >> 2) & 1) | ((((r >> 3) ^ (r >> 4)) & 1) << 1));
+}
+template <bool F8>
+__device__ __forceinline__ int swz_t(int r, int c) { return F8 ? swz8(r, c) : swz(r, c); }
+
+// 8 E4M3 codes → 8 bf16 (exact: every E4M3 value is a bf16 value)
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x2 w) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true);
+    return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                 __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+}
+
 // Wait until this wave's copies of a tile have landed while the copies of
 // `ahead` later tiles (0 or 1) may still be in flight.
+template <bool F8>
 __device__ __forceinline__ void wait_tile(int ahead, bool hi_wave) {
     if (ahead > 0) {
-        if (hi_wave) wait_vmcnt<MLOADS_HI>(); else wait_vmcnt<MLOADS_LO>();
+        if (hi_wave) wait_vmcnt<MGeo<F8>::LOADS_HI>(); else wait_vmcnt<MGeo<F8>::LOADS_LO>();
     } else {
         wait_vmcnt<0>();
     }
@@ -123,14 +161,15 @@ __device__ __forceinline__ void wait_tile(int ahead, bool hi_wave) {
 // of ragged.h with `splits` workers over the tiles of all B sequences
 // (lengths kv_lens[b], at most kv_len) — one worker's run within one
 // sequence — and writes its partial to slot j.
-template <int LOM, bool FULL, bool SK>
+template <int LOM, bool FULL, bool SK, bool F8>
 __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ ckv,
+    const uint16_t *__restrict__ q, const char *__restrict__ ckv,
     uint16_t *__restrict__ o, float *__restrict__ lse, int Hq, int kv_len, int kv_cap,
     float scale_log2, int splits, int split_keys, float *__restrict__ ws_ml,
     float *__restrict__ ws_part, const int *__restrict__ kv_lens, int B)
 {
-    __shared__ __attribute__((aligned(1024))) char tile[MNBUF][MTILEB];
+    using G = MGeo<F8>;
+    __shared__ __attribute__((aligned(1024))) char tile[MNBUF][G::TILEB];
     // weights in B-operand order and per-head α (then λ)
     constexpr int NPB = 1;
     __shared__ __attribute__((aligned(16))) u32x4 p_hi[NPB][MHB][64];
@@ -148,7 +187,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const int nhb = FULL ? MHB : min(MHB, (Hq - hg * MH) / 16);  // head blocks here (Hq % 16 == 0)
     const bool own = wave < nhb;                     // this wave scores heads 16·wave ..
     const int head = hg * MH + wave * 16 + hcol;     // its score head
-    const bool hi_wave = wave < MLOADS % MW;
+    const bool hi_wave = wave < G::LOADS % MW;
     int seq_len, key_begin, key_end;
     if constexpr (SK) {
         int t0, t1;
@@ -161,7 +200,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         key_end = min(kv_len, key_begin + split_keys);
     }
     const bool lo_on = LOM == 1 || (LOM == 2 && seq_len <= kLoMaxKeys);  // wave-uniform
-    const uint16_t *cb = ckv + (size_t)b * kv_cap * MD;
+    const char *cb = ckv + (size_t)b * kv_cap * G::ROWB;
 
     bf16x8 qf[MKR];
     {
@@ -182,29 +221,29 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     // 64 i + l = (row r, physical chunk pc), and come from row r, logical
     // chunk swz(r, pc). The byte offsets within a full tile are fixed.
     // (each offset is below 2^16: two per register)
-    uint32_t voffp[(MLOADS_HI + 1) / 2] = {};
+    uint32_t voffp[(G::LOADS_HI + 1) / 2] = {};
 #pragma unroll
-    for (int j = 0; j < MLOADS_HI; ++j) {
+    for (int j = 0; j < G::LOADS_HI; ++j) {
         const int pos = 64 * (wave + MW * j) + lane;
-        const int r = min(pos / MCH, MBC - 1), pc = pos % MCH;
-        voffp[j / 2] |= (uint32_t)(r * MROWB + 16 * swz(r, pc)) << (16 * (j & 1));
+        const int r = min(pos / G::CH, MBC - 1), pc = pos % G::CH;
+        voffp[j / 2] |= (uint32_t)(r * G::ROWB + 16 * swz_t<F8>(r, pc)) << (16 * (j & 1));
     }
-    static_assert(MTILEB <= 65536, "tile offsets fit 16 bits");
+    static_assert(G::TILEB <= 65536, "tile offsets fit 16 bits");
     auto voff = [&](int j) __attribute__((always_inline)) { return (voffp[j / 2] >> (16 * (j & 1))) & 0xffffu; };
     // Rows past the split's end repeat its last row (their scores are masked).
     auto load_tile = [&](int t0, int buf) __attribute__((always_inline)) {
         if (t0 + MBC <= key_end) {
-            const uint16_t *base = cb + (size_t)t0 * MD;
+            const char *base = cb + (size_t)t0 * G::ROWB;
 #pragma unroll
-            for (int j = 0; j < MLOADS_HI; ++j)
-                if (j < MLOADS_LO || hi_wave)
+            for (int j = 0; j < G::LOADS_HI; ++j)
+                if (j < G::LOADS_LO || hi_wave)
                     copy_to_lds16_sv(base, voff(j), &tile[buf][1024 * (wave + MW * j)]);
         } else {
-            for (int i = wave; i < MLOADS; i += MW) {
+            for (int i = wave; i < G::LOADS; i += MW) {
                 const int pos = 64 * i + lane;
-                const int r = pos / MCH, pc = pos % MCH;
+                const int r = pos / G::CH, pc = pos % G::CH;
                 const int key = min(t0 + r, key_end - 1);
-                copy_to_lds16(cb + (size_t)key * MD + 8 * swz(r, pc), &tile[buf][1024 * i]);
+                copy_to_lds16(cb + (size_t)key * G::ROWB + 16 * swz_t<F8>(r, pc), &tile[buf][1024 * i]);
             }
         }
     };
@@ -229,36 +268,47 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     // PARTIAL: the tile runs past the split's end (its last keys are masked).
     // cbase (if set): the next full tile's copies into buffer cbuf are issued
     // between the score steps instead of in one burst
-    auto scores = [&](const char *tb, int t0, int pb, const uint16_t *cbase, int cbuf,
+    auto scores = [&](const char *tb, int t0, int pb, const char *cbase, int cbuf,
                       auto partial_tag) __attribute__((always_inline)) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
         float sc[8];  // raw scores q·c (the scale is applied in the exponent)
         {
             // the two 16-key halves of the tile as two independent MFMA chains,
             // the operands of step ks + 1 requested before the MFMAs of step ks
-            const char *row0 = tb + hcol * MROWB, *row1 = row0 + 16 * MROWB;
+            // A operand of k-step ks: d = 32·ks + 8·quad .. + 7 of the lane's row
+            // (bf16: one 16-byte chunk; E4M3: 8 bytes, widened at the MFMA)
+            const char *row0 = tb + hcol * G::ROWB, *row1 = row0 + 16 * G::ROWB;
+            using Raw = std::conditional_t<F8, u32x2, u32x4>;
             auto ld = [&](const char *rowp, int r, int ks) __attribute__((always_inline)) {
-                return *(const u32x4 *)(rowp + 16 * swz(r, 4 * ks + quad));
+                if constexpr (F8)
+                    return *(const u32x2 *)(rowp + 16 * swz8(r, 2 * ks + (quad >> 1)) + 8 * (quad & 1));
+                else
+                    return *(const u32x4 *)(rowp + 16 * swz(r, 4 * ks + quad));
+            };
+            auto opnd = [&](Raw a) __attribute__((always_inline)) {
+                if constexpr (F8) return as<bf16x8>(e4m3x8_to_bf16(a));
+                else return as<bf16x8>(a);
             };
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-            u32x4 a0 = ld(row0, hcol, 0), a1 = ld(row1, 16 + hcol, 0);
+            Raw a0 = ld(row0, hcol, 0), a1 = ld(row1, 16 + hcol, 0);
 #pragma unroll
             for (int ks = 0; ks < MKS; ++ks) {
-                constexpr int kEvery = (MKS + MLOADS_HI - 1) / MLOADS_HI;  // score steps per copy
+                constexpr int kEvery = (MKS + G::LOADS_HI - 1) / G::LOADS_HI;  // score steps per copy
                 if (cbase && ks % kEvery == 0) {
                     const int j = ks / kEvery;
-                    if (j < MLOADS_LO || hi_wave)
+                    if (j < G::LOADS_LO || hi_wave)
                         copy_to_lds16_sv(cbase, voff(j), &tile[cbuf][1024 * (wave + MW * j)]);
                 }
-                u32x4 n0 = a0, n1 = a1, qn;
+                Raw n0 = a0, n1 = a1;
+                u32x4 qn;
                 if (ks + 1 < MKS) {
                     n0 = ld(row0, hcol, ks + 1);
                     n1 = ld(row1, 16 + hcol, ks + 1);
                 }
                 if (ks >= MKR) qn = q_lds[ks - MKR][wave][lane];
                 const bf16x8 qk = ks < MKR ? qf[ks < MKR ? ks : 0] : as<bf16x8>(qn);
-                acc0 = mfma16x16x32(as<bf16x8>(a0), qk, acc0);
-                acc1 = mfma16x16x32(as<bf16x8>(a1), qk, acc1);
+                acc0 = mfma16x16x32(opnd(a0), qk, acc0);
+                acc1 = mfma16x16x32(opnd(a1), qk, acc1);
                 a0 = n0;
                 a1 = n1;
                 // keep the compiler from hoisting later reads (hoisting spills)
@@ -326,17 +376,34 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
             }
         }
         u32x4 va[MDBW];
-        const char *row1 = tb + vr1 * MROWB + 8 * (vc & 1);
-        const char *row2 = tb + vr2 * MROWB + 8 * (vc & 1);
+        if constexpr (F8) {
+            // ds_read_b64_tr_b8: lane 16·g + 2·r + h names row r of an 8-row
+            // block (bytes 8h .. 8h + 7 of a 16-byte column block) and receives
+            // column lane % 16 of the 8 rows, row k in byte k. Rows: keys
+            // 4·g + r (r < 4) and 16 + 4·g + r − 4 (r ≥ 4), the slot order of
+            // the weights; column block = 16 latent channels.
+            const int r8 = (lane >> 1) & 7;
+            const int kr = r8 < 4 ? 4 * quad + r8 : 12 + 4 * quad + r8;
+            const char *rowp = tb + kr * G::ROWB + 8 * (lane & 1);
 #pragma unroll
-        for (int db = 0; db < MDBW; ++db) {
-            const int c = 2 * (MDBW * wave + db) + (vc >> 1);
-            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(row1 + 16 * swz(vr1, c)));
-            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(row2 + 16 * swz(vr2, c)));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
-            va[db] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+            for (int db = 0; db < MDBW; ++db) {
+                const int c = MDBW * wave + db;
+                const auto x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(rowp + 16 * swz8(kr, c)));
+                va[db] = e4m3x8_to_bf16(__builtin_bit_cast(u32x2, x));
+            }
+        } else {
+            const char *row1 = tb + vr1 * MROWB + 8 * (vc & 1);
+            const char *row2 = tb + vr2 * MROWB + 8 * (vc & 1);
+#pragma unroll
+            for (int db = 0; db < MDBW; ++db) {
+                const int c = 2 * (MDBW * wave + db) + (vc >> 1);
+                const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(row1 + 16 * swz(vr1, c)));
+                const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(row2 + 16 * swz(vr2, c)));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
+                va[db] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+            }
         }
 #pragma unroll
         for (int hb = 0; hb < MHB; ++hb) {
@@ -354,7 +421,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     };
 
     const int n_t = max(0, key_end - key_begin + MBC - 1) / MBC;  // 0: split past the end
-    auto do_scores = [&](const char *tb, int t0, int pb, const uint16_t *cbase, int cbuf) __attribute__((always_inline)) {
+    auto do_scores = [&](const char *tb, int t0, int pb, const char *cbase, int cbuf) __attribute__((always_inline)) {
         if (own) {
             if (t0 + MBC > key_end) scores(tb, t0, pb, cbase, cbuf, std::true_type{});
             else scores(tb, t0, pb, cbase, cbuf, std::false_type{});
@@ -371,7 +438,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         if (p < n_t) load_tile(key_begin + p * MBC, p);
     for (int t = 0; t < n_t; ++t) {
         const int t0 = key_begin + t * MBC;
-        wait_tile(min(MNBUF - 2, n_t - 1 - t), hi_wave);
+        wait_tile<F8>(min(MNBUF - 2, n_t - 1 - t), hi_wave);
         __syncthreads();  // tile t visible; tile t − 1 and the last weights no longer read
         // refill: a full next tile is copied from inside the score steps of
         // the waves that score; a partial one (clamped rows), or the copies of
@@ -380,7 +447,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
         const bool refill = t + MNBUF - 1 < n_t, spread = refill && own && tn + MBC <= key_end;
         if (refill && !spread) load_tile(tn, bn);
         const char *tb = tile[t % MNBUF];
-        do_scores(tb, t0, 0, spread ? cb + (size_t)tn * MD : nullptr, bn);
+        do_scores(tb, t0, 0, spread ? cb + (size_t)tn * G::ROWB : nullptr, bn);
         __syncthreads();  // weights and rescale factors of every head visible
         values(tb, 0);
     }
@@ -471,9 +538,10 @@ bool mla_ragged_plan(int B, int Hq, int max_len, MlaPlan *p)
     return true;
 }
 
-hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, void *o,
-                             float *lse, int B, int Hq, int kv_len, int kv_cap,
-                             float scale, void *ws, hipStream_t st, const int *kv_lens)
+template <bool F8>
+static hipError_t launch_decode_mla_t(const MlaPlan &p, const void *q, const void *ckv, void *o,
+                                      float *lse, int B, int Hq, int kv_len, int kv_cap,
+                                      float scale, void *ws, hipStream_t st, const int *kv_lens)
 {
     char *w = (char *)ws;
     float *ws_ml = (float *)(w + p.ws_ml);
@@ -483,28 +551,39 @@ hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, v
     if (kv_lens) {
         // ragged: balanced split over the tiles of all sequences (kv_len is
         // the longest); short sequences switch the residual product on
+        if constexpr (F8) return hipErrorNotSupported;  // no E4M3 ragged entry point
+        else {
         const dim3 grid(p.splits + B, hgs, 1);  // one workgroup per slot (piece)
         auto kern = kv_len <= kLoMaxKeys
-                        ? (full ? decode_mla_kernel<1, true, true> : decode_mla_kernel<1, false, true>)
-                        : (full ? decode_mla_kernel<2, true, true> : decode_mla_kernel<2, false, true>);
+                        ? (full ? decode_mla_kernel<1, true, true, F8> : decode_mla_kernel<1, false, true, F8>)
+                        : (full ? decode_mla_kernel<2, true, true, F8> : decode_mla_kernel<2, false, true, F8>);
         kern<<<grid, dim3(MTHREADS), 0, st>>>(
-            (const uint16_t *)q, (const uint16_t *)ckv, (uint16_t *)o, lse, Hq, kv_len, kv_cap,
+            (const uint16_t *)q, (const char *)ckv, (uint16_t *)o, lse, Hq, kv_len, kv_cap,
             scale * kLog2e, p.splits, 0, ws_ml, ws_part, kv_lens, B);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         return launch_merge_ragged(ws_ml, ws_part, o, lse, kv_lens, B, Hq, kv_len, p.splits, MBC,
                                    MV, st);
+        }
     }
     const dim3 grid(p.splits, hgs, B);
     auto kern = kv_len <= kLoMaxKeys
-                    ? (full ? decode_mla_kernel<1, true, false> : decode_mla_kernel<1, false, false>)
-                    : (full ? decode_mla_kernel<0, true, false> : decode_mla_kernel<0, false, false>);
+                    ? (full ? decode_mla_kernel<1, true, false, F8> : decode_mla_kernel<1, false, false, F8>)
+                    : (full ? decode_mla_kernel<0, true, false, F8> : decode_mla_kernel<0, false, false, F8>);
     kern<<<grid, dim3(MTHREADS), 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)ckv, (uint16_t *)o, lse, Hq, kv_len, kv_cap,
+        (const uint16_t *)q, (const char *)ckv, (uint16_t *)o, lse, Hq, kv_len, kv_cap,
         scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part, nullptr, B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, MV, st);
+}
+
+hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, void *o,
+                             float *lse, int B, int Hq, int kv_len, int kv_cap,
+                             float scale, void *ws, hipStream_t st, const int *kv_lens, bool fp8)
+{
+    return fp8 ? launch_decode_mla_t<true>(p, q, ckv, o, lse, B, Hq, kv_len, kv_cap, scale, ws, st, kv_lens)
+               : launch_decode_mla_t<false>(p, q, ckv, o, lse, B, Hq, kv_len, kv_cap, scale, ws, st, kv_lens);
 }
 
 }  // namespace attn

@@ -61,7 +61,7 @@ bool mla_ragged_plan(int B, int Hq, int max_len, MlaPlan *p);
 // kv_len = the longest sequence).
 hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, void *o,
                              float *lse, int B, int Hq, int kv_len, int kv_cap,
-                             float scale, void *ws, hipStream_t s, const int *kv_lens);
+                             float scale, void *ws, hipStream_t s, const int *kv_lens, bool fp8);
 
 // ---- split-K merge through the log-sum-exp (shared by both decodes) -------
 constexpr int kMaxSplits = 128;  // upper bound the planners respect

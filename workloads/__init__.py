@@ -163,7 +163,8 @@ class PrefillChunked:
 
 @dataclass
 class DecodeMLA:
-    """Absorbed MLA decode. q [B,Hq,Dqk]; ckv [B,kv_cap,Dqk] bf16.
+    """Absorbed MLA decode. q [B,Hq,Dqk] bf16; ckv [B,kv_cap,Dqk] bf16 or
+    FP8 E4M3 codes.
 
     Each row is [latent (Dv) | rope (Dqk-Dv)]. The latent part is stored
     channel-balanced: q holds q̃·S⁻¹ and ckv holds S·c, S = diag(s).
@@ -180,6 +181,7 @@ class DecodeMLA:
     ckv: np.ndarray
     s: np.ndarray = field(default=None)   # channel scale, [Dv] float64
     kv_lens: np.ndarray | None = None     # [B] int32 per-sequence lengths (ragged batch)
+    cache_dtype: str = "bf16"             # "bf16" (uint16 bits) or "fp8" (E4M3 uint8 codes)
 
 
 def ragged_lengths(B, lo, hi, seed) -> np.ndarray:
@@ -303,7 +305,7 @@ def gen_prefill_chunked(B, Hq, Hkv, Nq, kv_lens, D=128, kv_cap=None, seed=0, sca
 
 def gen_decode_mla(B, Hq, kv_len=None, Dqk=576, Dv=512, kv_cap=None, seed=0,
                    scale=None, mag_lo=1e-4, mag_hi=1e2, poison_tail=True,
-                   kv_lens=None) -> DecodeMLA:
+                   kv_lens=None, cache_dtype="bf16") -> DecodeMLA:
     """Absorbed-MLA decode inputs, channel-balanced before storage.
 
     s_k = 10^U(log10 mag_lo, log10 mag_hi) per latent channel. The model-side
@@ -312,8 +314,13 @@ def gen_decode_mla(B, Hq, kv_len=None, Dqk=576, Dv=512, kv_cap=None, seed=0,
     channels (Dqk - Dv of them) are N(0,1) and not scaled. Default scale is
     1/√192 (128 no-rope + 64 rope dims of the pre-absorption head).
     With kv_lens (a ragged batch) sequence b is filled to kv_lens[b] and
-    kv_len is the longest.
+    kv_len is the longest. cache_dtype "fp8" stores the cache as OCP E4M3
+    codes of the same balanced rows S·c (round to nearest even; the
+    balanced values lie far inside E4M3's range), the query staying bf16.
     """
+    if cache_dtype not in ("bf16", "fp8"):
+        raise ValueError(cache_dtype)
+    fp8 = cache_dtype == "fp8"
     if kv_lens is not None:
         lens = _lengths(B, kv_lens, None)
         kv_len = int(lens.max())
@@ -329,16 +336,17 @@ def gen_decode_mla(B, Hq, kv_len=None, Dqk=576, Dv=512, kv_cap=None, seed=0,
     q_tilde = qn[..., :Dv] * s                      # raw absorbed query
     qn[..., :Dv] = q_tilde / s                      # q̃·S⁻¹
     q = round_to_bf16_bits(qn)
-    ckv = np.empty((B, kv_cap, Dqk), np.uint16)
+    elt, nan = (np.uint8, E4M3_NAN_BITS) if fp8 else (np.uint16, BF16_NAN_BITS)
+    ckv = np.empty((B, kv_cap, Dqk), elt)
     for b in range(B):                              # per batch to bound memory
         n = int(lens[b])
         cn = _normal(rc, (n, Dqk)).astype(np.float64)
         c_raw = cn[:, :Dv] / s                      # raw latent
         cn[:, :Dv] = s * c_raw                      # S·c
-        ckv[b, :n] = round_to_bf16_bits(cn)
-        ckv[b, n:] = BF16_NAN_BITS if poison_tail else np.uint16(0)
+        ckv[b, :n] = round_to_e4m3_bits(cn) if fp8 else round_to_bf16_bits(cn)
+        ckv[b, n:] = nan if poison_tail else elt(0)
     return DecodeMLA(B, Hq, kv_len, kv_cap, Dqk, Dv, float(scale), q, ckv, s,
-                     lens if kv_lens is not None else None)
+                     lens if kv_lens is not None else None, cache_dtype)
 
 
 # --------------------------------------------------------- named workloads ---
@@ -377,6 +385,9 @@ WORKLOADS = {
     "decode_gqa_fp8_llama3_8b_4k": dict(
         kind="decode_gqa", B=8, Hq=32, Hkv=8, kv_len=4096, D=128, seed=1009,
         scale=1.0 / math.sqrt(128), cache_dtype="fp8"),
+    "decode_mla_fp8_32k": dict(
+        kind="decode_mla", B=16, Hq=128, kv_len=32768, Dqk=576, Dv=512, seed=1010,
+        scale=1.0 / math.sqrt(128 + 64), cache_dtype="fp8"),
     "decode_mla_ragged_32k": dict(
         kind="decode_mla", B=16, Hq=128, kv_lens=("ragged", 1024, 32768, 1108),
         kv_cap=32768, Dqk=576, Dv=512, seed=1008, scale=1.0 / math.sqrt(128 + 64)),
@@ -427,9 +438,11 @@ def decode_gqa_flops(B, Hq, kv_len, D):
     return 4 * B * Hq * kv_len * D
 
 
-def decode_mla_bytes(B, Hq, kv_len, Dqk, Dv, elt=2):
-    """Latent rows read once (V is a prefix of each row), q, O, fp32 LSE."""
-    return elt * (B * kv_len * Dqk + B * Hq * Dqk + B * Hq * Dv) + 4 * B * Hq
+def decode_mla_bytes(B, Hq, kv_len, Dqk, Dv, elt=2, kv_elt=None):
+    """Latent rows read once (V is a prefix of each row; kv_elt bytes per
+    element, 1 for an FP8 cache), q, O (elt bytes), fp32 LSE."""
+    kv_elt = elt if kv_elt is None else kv_elt
+    return kv_elt * B * kv_len * Dqk + elt * (B * Hq * Dqk + B * Hq * Dv) + 4 * B * Hq
 
 
 def decode_mla_flops(B, Hq, kv_len, Dqk, Dv):
