@@ -161,12 +161,16 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
         work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
         kernel = "decode_gqa_kernel<%s> + merge_kernel" % ("true" if fp8 else "false")
     elif kind == "decode_mla":
-        q, c = _upload_bf16(torch, w.q, dev), _upload_bf16(torch, w.ckv, dev)
+        fp8 = w.cache_dtype == "fp8"
+        q = _upload_bf16(torch, w.q, dev)
+        c = torch.from_numpy(w.ckv).to(dev) if fp8 else _upload_bf16(torch, w.ckv, dev)
         if ragged:
             nbytes = workloads.decode_mla_ragged_bytes(w.Hq, w.kv_lens, w.Dqk, w.Dv)
         else:
-            nbytes = workloads.decode_mla_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv)
-        sets = [(q, c)] + [(q, c.clone()) for _ in range(_rotation(c.numel() * 2) - 1)]
+            nbytes = workloads.decode_mla_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv,
+                                                kv_elt=1 if fp8 else 2)
+        sets = [(q, c)] + [(q, c.clone())
+                           for _ in range(_rotation(c.numel() * c.element_size()) - 1)]
         o = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
         ws_fn = attn.attn_decode_mla_ragged_workspace_bytes if ragged else attn.attn_decode_mla_workspace_bytes
@@ -175,11 +179,14 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev):
             calls = [lambda s=s: attn.attn_decode_mla_ragged(s[0], s[1], lens, w.kv_len, w.Dv,
                                                              w.scale, out=o, lse=lse, ws=ws)
                      for s in sets]
+        elif fp8:
+            calls = [lambda s=s: attn.attn_decode_mla_fp8(s[0], s[1], w.kv_len, w.Dv, w.scale,
+                                                          out=o, lse=lse, ws=ws) for s in sets]
         else:
             calls = [lambda s=s: attn.attn_decode_mla_absorbed(s[0], s[1], w.kv_len, w.Dv, w.scale,
                                                                out=o, lse=lse, ws=ws) for s in sets]
         work, unit, peak, bound = nbytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
-        kernel = "decode_mla_kernel + merge_kernel"
+        kernel = "decode_mla_kernel%s + merge_kernel" % ("<E4M3>" if fp8 else "")
     elif kind == "prefill_backward":
         q, k, v = (_upload_bf16(torch, x, dev) for x in (w.q, w.k, w.v))
         dout = _upload_bf16(torch, workloads.gen_upstream_grad((w.B, w.Hq, w.N, w.D), seed=1010), dev)

@@ -1,4 +1,5 @@
-// Absorbed MLA decode, gfx950: bf16 latent cache, fp32 accumulation.
+// Absorbed MLA decode, gfx950: bf16 or FP8 E4M3 latent cache, fp32
+// accumulation.
 //
 // With W_UK folded into the query ("MLA 矩阵乘法吸收的数值稳定性治理", §一),
 // every query head attends to one shared latent cache whose rows are
@@ -51,6 +52,17 @@
 // (non-temporal) stores that do not stay dirty in L2; the shared merge kernel
 // combines them through their log-sum-exp. Rows at or past kv_len are never
 // read.
+// E4M3 cache (F8): the stored rows are the channel-balanced latent S·c, so
+// every channel fits E4M3's range ("MLA 矩阵乘法吸收的数值稳定性治理", §二.1).
+// Tiles of 32 rows × 576 B are copied the same way; a score operand is
+// 8 bytes (ds_read_b64) and a value operand one ds_read_b64_tr_b8 (8 rows
+// of one 16-channel column block per lane group, row k in byte k), each
+// widened to 8 bf16 in registers (v_cvt_scalef32_pk_bf16_fp8 with scale 1:
+// exact). The value rows a lane names are chosen so the keys arrive in the
+// weights' slot order, and the products, their operands and their order are
+// those of the bf16 path: given a bf16 copy of the same values the two give
+// the same bits. A different chunk swizzle (swz8) keeps both reads
+// conflict-free on the 576-byte rows.
 // Ragged batches (per-sequence lengths in device memory): the 32-key tiles of
 // all sequences, in batch order, are cut into P equal runs (ragged.h), so a
 // mix of short and long sequences keeps every CU busy; each piece of a run
