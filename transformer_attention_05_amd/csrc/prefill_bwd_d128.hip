@@ -59,6 +59,22 @@ __device__ __forceinline__ bf16x8 tr_operand(const char *tile, int lane_off, int
     return as<bf16x8>(u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 
+// The same operand from a swizzled tile (256-byte rows, chunk c of row r at
+// c ^ (4·(r & 3) + (r / 4 & 3))): rows 16·mm + 4·half + e (and + 8) have
+// swizzle 4·e + half (+ 2), so chunk 4·db + low lands at
+// 4·(db ^ e) + (low ^ (half [+ 2])).
+__device__ __forceinline__ bf16x8 tr_operand_sw(const char *tile, int lane, int mm, int db) {
+    const int half = lane >> 5, g = lane >> 4, e = (lane >> 2) & 3, c = lane & 3;
+    const int low = 2 * (g & 1) + (c >> 1);
+    const int rlo = 16 * mm + 4 * half + e;
+    const char *plo = tile + rlo * 256 + 64 * (db ^ e) + 16 * (low ^ half) + 8 * (c & 1);
+    const char *phi = tile + (rlo + 8) * 256 + 64 * (db ^ e) + 16 * (low ^ (half + 2)) + 8 * (c & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)plo);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)phi);
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return as<bf16x8>(u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+
 // B operands of the two 16-row k-steps of a 32×32 accumulator, rounded to bf16.
 __device__ __forceinline__ void pack_b(const f32x16 &acc, bf16x8 (&out)[2]) {
 #pragma unroll
@@ -91,10 +107,30 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t *__restrict
 }
 
 // ------------------------------------------------------------------- dK, dV ---
+#ifndef ATTN_BWD_RING
+#define ATTN_BWD_RING 1   // Q/dO tiles copied HBM → LDS three ahead, one swizzled copy each
+#endif
+#if ATTN_BWD_RING
+// One 32-row query tile: Q and dO rows of 256 B, unpadded, 16-byte chunk c
+// of row r stored at chunk c ^ bswz(r); then the 32 raw LSE (natural log)
+// and D values. The swizzle spreads both reads over all 64 banks: a row
+// read (ds_read_b128) takes one chunk of 16 rows per 16-lane phase, a
+// transposed read (ds_read_b64_tr_b16) 4 chunks of 4 consecutive rows per
+// 32-lane phase. A wave-wide 1 KiB copy fills 4 whole rows.
+struct TileBuf {
+    uint16_t qs[T * D], ds[T * D];
+    float lse[T], dd[T];
+};
+constexpr int NRING = 4;                                    // tiles in LDS
+constexpr int TILE_COPIES = 2 * (T * D * 2 / 1024) + 1;     // 8 + 8 + LSE/D
+constexpr int COPIES_MIN = TILE_COPIES / NWV;               // copies every wave issues per tile
+__device__ __forceinline__ int bswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+#else
 struct TileBuf {           // one 32-row query tile of Q and dO, in two pitches
     uint16_t qr[T * RP], qt[T * TP], dr[T * RP], dt[T * TP];
     float lse2[T], dd[T];
 };
+#endif
 
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -102,7 +138,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, int Hq, int Hkv, int N, int n_kblk,
     float scale_log2, float scale)
 {
+#if ATTN_BWD_RING
+    __shared__ __attribute__((aligned(1024))) TileBuf buf[NRING];
+#else
     __shared__ __attribute__((aligned(16))) TileBuf buf[2];
+#endif
 
     const int G = Hq / Hkv;
     // heaviest first: key block 0 sees every query
@@ -139,6 +179,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const int q_first = (k0 / T) * T;                   // first tile with a query >= k0
     const int n_qt = (N - q_first + T - 1) / T;         // query tiles per head
     const int n_it = G * n_qt;
+#if ATTN_BWD_RING
+    // copy j of a tile (wave w issues j = w, w + 4, ...): 0..7 Q rows
+    // 4j .. 4j + 3, 8..15 dO rows, 16 LSE (lanes 0..31) and D (32..63).
+    // Lane l lands at row 4j + l/16, physical chunk l % 16, so it reads
+    // logical chunk (l % 16) ^ bswz(row).
+    auto issue_tile = [&](int it, TileBuf &t) __attribute__((always_inline)) {
+        const int h = hkv * G + it / n_qt, q0 = q_first + T * (it % n_qt);
+        const size_t qoff = ((size_t)b * Hq + h) * N;
+        for (int j = wave; j < TILE_COPIES; j += NWV) {  // wave-uniform
+            if (j == TILE_COPIES - 1) {
+                const int r = min(q0 + (lane & 31), N - 1);
+                const float *src = lane < 32 ? lse + qoff + r : dd + qoff + r;
+                __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)t.lse, 4, 0, 0);
+                continue;
+            }
+            const bool isd = j >= 8;
+            const int i = isd ? j - 8 : j;
+            const int r = 4 * i + (lane >> 4), c = (lane & 15) ^ bswz(r);
+            const uint16_t *src = (isd ? dout : q) + (qoff + min(q0 + r, N - 1)) * D + 8 * c;
+            uint16_t *dst = (isd ? t.ds : t.qs) + 512 * i;
+            __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+        }
+    };
+#else
     u32x4 sq[2], sd[2];
     float sl = 0.f, sdd = 0.f;
     auto load = [&](int it) __attribute__((always_inline)) {
@@ -170,15 +234,39 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             t.dd[tid] = sdd;
         }
     };
+#endif
 
+#if ATTN_BWD_RING
+    for (int t = 0; t < NRING - 1; ++t)
+        if (t < n_it) issue_tile(t, buf[t]);
+    wait_vmcnt<0>();
+    __syncthreads();
+#else
     load(0);
     store(buf[0]);
     __syncthreads();
+#endif
     for (int it = 0; it < n_it; ++it) {
         const int cur = it & 1;
+#if ATTN_BWD_RING
+        // into the buffer of tile it − 1, which every wave is done with
+        if (it + NRING - 1 < n_it) issue_tile(it + NRING - 1, buf[(it + NRING - 1) % NRING]);
+#else
         if (it + 1 < n_it) load(it + 1);
+#endif
         const int q0 = q_first + T * (it % n_qt);
+#if ATTN_BWD_RING
+        const TileBuf &tb = buf[it % NRING];
+#else
         const TileBuf &tb = buf[cur];
+#endif
+#if ATTN_BWD_RING
+        // per-lane swizzle inputs, opaque to the compiler inside the loop so
+        // the few XORs are redone per tile rather than kept in registers
+        int lane_x = lane;
+        asm volatile("" : "+v"(lane_x));
+        const int col_x = lane_x & 31;
+#endif
         if (q0 + T - 1 >= kw0) {  // some query of the tile sees some key of the wave
             // ---- S = Q·Kᵀ and dP = dO·Vᵀ: rows = queries, lane column = key
             f32x16 s, dp;
@@ -186,8 +274,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
+#if ATTN_BWD_RING
+                const int off = col_x * 256 + 16 * ((2 * ks + half) ^ bswz(col_x));
+                const bf16x8 a = as<bf16x8>(*(const u32x4 *)((const char *)tb.qs + off));
+                const bf16x8 c = as<bf16x8>(*(const u32x4 *)((const char *)tb.ds + off));
+#else
                 const bf16x8 a = as<bf16x8>(*(const u32x4 *)&tb.qr[col * RP + 16 * ks + 8 * half]);
                 const bf16x8 c = as<bf16x8>(*(const u32x4 *)&tb.dr[col * RP + 16 * ks + 8 * half]);
+#endif
                 s = mfma32x32x16(a, kf[ks], s);
                 dp = mfma32x32x16(c, vf[ks], dp);
             }
@@ -197,9 +291,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi) {
                 const int r0 = 8 * gi + 4 * half;
+#if ATTN_BWD_RING
+                const float4 L4 = *(const float4 *)&tb.lse[r0];  // natural log: to base 2 here
+                const float Lr[4] = {L4.x * kLog2e, L4.y * kLog2e, L4.z * kLog2e, L4.w * kLog2e};
+#else
                 const float4 L4 = *(const float4 *)&tb.lse2[r0];
+                const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+#endif
                 const float4 D4 = *(const float4 *)&tb.dd[r0];
-                const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+                const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int i = 4 * gi + j, qi = q0 + r0 + j;
@@ -217,11 +317,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
+#if ATTN_BWD_RING
+                    dvacc[db] = mfma32x32x16(tr_operand_sw((const char *)tb.ds, lane_x, mm, db), pf[mm], dvacc[db]);
+                    dkacc[db] = mfma32x32x16(tr_operand_sw((const char *)tb.qs, lane_x, mm, db), sf[mm], dkacc[db]);
+#else
                     dvacc[db] = mfma32x32x16(tr_operand((const char *)tb.dt, tr_lane, mm, db), pf[mm], dvacc[db]);
                     dkacc[db] = mfma32x32x16(tr_operand((const char *)tb.qt, tr_lane, mm, db), sf[mm], dkacc[db]);
+#endif
                 }
         }
+#if ATTN_BWD_RING
+        // this wave's copies of tile it + 1 done; those of later tiles may fly
+        {
+            const int newer = min(it + NRING - 1, n_it - 1) - (it + 1);
+            if (newer >= 2) wait_vmcnt<2 * COPIES_MIN>();
+            else if (newer == 1) wait_vmcnt<COPIES_MIN>();
+            else wait_vmcnt<0>();
+        }
+#else
         if (it + 1 < n_it) store(buf[cur ^ 1]);
+#endif
         __syncthreads();
     }
 
