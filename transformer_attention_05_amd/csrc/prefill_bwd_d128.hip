@@ -15,7 +15,7 @@
 //   dkdv   workgroup (b, K/V head, 128-key block), 4 waves of 32 keys each
 //          with their K and V rows in registers as MFMA B operands. For each
 //          query head of the group and each 32-query tile at or after the
-//          block (tiles staged through LDS, double-buffered):
+//          block (tiles in an LDS ring of four, see below):
 //            S  = Q·Kᵀ, dP = dO·Vᵀ          (v_mfma_f32_32x32x16_bf16; the
 //                                           lane holds one key's column)
 //            P, dS element-wise (masked on the diagonal tiles)
@@ -28,9 +28,15 @@
 //          to the diagonal:
 //            Sᵀ = K·Qᵀ, dPᵀ = V·dOᵀ, Pᵀ and dSᵀ, dQᵀ += Kᵀ·dSᵀ
 // so S and dP are computed twice (in dkdv and in dq) rather than summed into
-// dQ across workgroups with atomics. Each LDS tile that is read both by rows
-// (ds_read_b128) and transposed (ds_read_b64_tr_b16) is stored twice, with
-// row pitches of 272 B and 320 B, the conflict-free pitch for each pattern.
+// dQ across workgroups with atomics.
+// Tiles (Q and dO for dkdv, K and V for dq; 32 rows of 256 B each) move HBM →
+// LDS by direct wave-wide copies (global_load_lds_dwordx4, no register
+// staging) into a ring of four, three tiles ahead of use: with two buffers
+// filled through registers, the next tile's load latency was exposed once
+// per tile and took half of dkdv's time. One copy of each tile serves both
+// the row reads (ds_read_b128) and the transposed reads (ds_read_b64_tr_b16):
+// 16-byte chunk c of row r sits at chunk c ^ (4·(r & 3) + (r / 4 & 3)),
+// which puts both patterns on all 64 banks.
 #include "common.h"
 #include "launch.h"
 
@@ -41,29 +47,18 @@ constexpr int D = 128, KS = D / 16, DB = D / 32;
 constexpr int T = 32;                       // rows per wave and per tile
 constexpr int NWV = 4;                      // waves per workgroup
 constexpr int BLK = T * NWV;                // keys (dkdv) or queries (dq) per workgroup
-constexpr int RP = 136, TP = 160;           // row pitches (elements): 272 B and 320 B
-constexpr int RPB = 2 * RP, TPB = 2 * TP;   // in bytes
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Transposed MFMA A operand (32 rows of d × 16 k) from a row-major LDS tile
-// whose rows are the k index: slot t of lane 16g + 4e + c holds tile row
-// 16·mm + 8·(t/4) + 4·half + t%4, column 32·db + 16·(g&1) + 4·c + (t%4 ...)
-// — the layout the Sᵀ/P accumulator registers 8·mm .. 8·mm + 7 match.
-__device__ __forceinline__ bf16x8 tr_operand(const char *tile, int lane_off, int mm, int db) {
-    const char *p = tile + lane_off + 16 * mm * TPB + 64 * db;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 8 * TPB));
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    return as<bf16x8>(u32x4{l2[0], l2[1], h2[0], h2[1]});
-}
-
-// The same operand from a swizzled tile (256-byte rows, chunk c of row r at
-// c ^ (4·(r & 3) + (r / 4 & 3))): rows 16·mm + 4·half + e (and + 8) have
+// Transposed MFMA A operand (32 rows of d × 16 k) from a swizzled tile whose
+// rows are the k index (256-byte rows, chunk c of row r at
+// c ^ (4·(r & 3) + (r / 4 & 3))). Slot t of lane 16g + 4e + c holds tile
+// row 16·mm + 8·(t/4) + 4·half + t%4 — the layout the Sᵀ/P accumulator
+// registers 8·mm .. 8·mm + 7 match. Rows 16·mm + 4·half + e (and + 8) have
 // swizzle 4·e + half (+ 2), so chunk 4·db + low lands at
 // 4·(db ^ e) + (low ^ (half [+ 2])).
-__device__ __forceinline__ bf16x8 tr_operand_sw(const char *tile, int lane, int mm, int db) {
+__device__ __forceinline__ bf16x8 tr_operand(const char *tile, int lane, int mm, int db) {
     const int half = lane >> 5, g = lane >> 4, e = (lane >> 2) & 3, c = lane & 3;
     const int low = 2 * (g & 1) + (c >> 1);
     const int rlo = 16 * mm + 4 * half + e;
@@ -107,10 +102,6 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t *__restrict
 }
 
 // ------------------------------------------------------------------- dK, dV ---
-#ifndef ATTN_BWD_RING
-#define ATTN_BWD_RING 1   // Q/dO tiles copied HBM → LDS three ahead, one swizzled copy each
-#endif
-#if ATTN_BWD_RING
 // One 32-row query tile: Q and dO rows of 256 B, unpadded, 16-byte chunk c
 // of row r stored at chunk c ^ bswz(r); then the 32 raw LSE (natural log)
 // and D values. The swizzle spreads both reads over all 64 banks: a row
@@ -125,12 +116,6 @@ constexpr int NRING = 4;                                    // tiles in LDS
 constexpr int TILE_COPIES = 2 * (T * D * 2 / 1024) + 1;     // 8 + 8 + LSE/D
 constexpr int COPIES_MIN = TILE_COPIES / NWV;               // copies every wave issues per tile
 __device__ __forceinline__ int bswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
-#else
-struct TileBuf {           // one 32-row query tile of Q and dO, in two pitches
-    uint16_t qr[T * RP], qt[T * TP], dr[T * RP], dt[T * TP];
-    float lse2[T], dd[T];
-};
-#endif
 
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -138,11 +123,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, int Hq, int Hkv, int N, int n_kblk,
     float scale_log2, float scale)
 {
-#if ATTN_BWD_RING
     __shared__ __attribute__((aligned(1024))) TileBuf buf[NRING];
-#else
-    __shared__ __attribute__((aligned(16))) TileBuf buf[2];
-#endif
 
     const int G = Hq / Hkv;
     // heaviest first: key block 0 sees every query
@@ -174,12 +155,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 
     // staging: thread tid moves 16-byte chunks (tid, tid + 256) of the
     // 32 × 256 B Q and dO tiles, row r = chunk / 16, column chunk c = chunk % 16
-    const int g4 = lane >> 4, e4 = (lane >> 2) & 3, cq = lane & 3;
-    const int tr_lane = (4 * half + e4) * TPB + 32 * (g4 & 1) + 8 * cq;
     const int q_first = (k0 / T) * T;                   // first tile with a query >= k0
     const int n_qt = (N - q_first + T - 1) / T;         // query tiles per head
     const int n_it = G * n_qt;
-#if ATTN_BWD_RING
     // copy j of a tile (wave w issues j = w, w + 4, ...): 0..7 Q rows
     // 4j .. 4j + 3, 8..15 dO rows, 16 LSE (lanes 0..31) and D (32..63).
     // Lane l lands at row 4j + l/16, physical chunk l % 16, so it reads
@@ -202,71 +180,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
         }
     };
-#else
-    u32x4 sq[2], sd[2];
-    float sl = 0.f, sdd = 0.f;
-    auto load = [&](int it) __attribute__((always_inline)) {
-        const int h = hkv * G + it / n_qt, q0 = q_first + T * (it % n_qt);
-        const size_t qoff = ((size_t)b * Hq + h) * N;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ch = tid + 256 * u, r = min(q0 + ch / 16, N - 1), c = ch % 16;
-            sq[u] = *(const u32x4 *)(q + (qoff + r) * D + 8 * c);
-            sd[u] = *(const u32x4 *)(dout + (qoff + r) * D + 8 * c);
-        }
-        if (tid < T) {
-            const int r = min(q0 + tid, N - 1);
-            sl = lse[qoff + r] * kLog2e;
-            sdd = dd[qoff + r];
-        }
-    };
-    auto store = [&](TileBuf &t) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ch = tid + 256 * u, r = ch / 16, c = ch % 16;
-            *(u32x4 *)&t.qr[r * RP + 8 * c] = sq[u];
-            *(u32x4 *)&t.qt[r * TP + 8 * c] = sq[u];
-            *(u32x4 *)&t.dr[r * RP + 8 * c] = sd[u];
-            *(u32x4 *)&t.dt[r * TP + 8 * c] = sd[u];
-        }
-        if (tid < T) {
-            t.lse2[tid] = sl;
-            t.dd[tid] = sdd;
-        }
-    };
-#endif
 
-#if ATTN_BWD_RING
     for (int t = 0; t < NRING - 1; ++t)
         if (t < n_it) issue_tile(t, buf[t]);
     wait_vmcnt<0>();
     __syncthreads();
-#else
-    load(0);
-    store(buf[0]);
-    __syncthreads();
-#endif
     for (int it = 0; it < n_it; ++it) {
-        const int cur = it & 1;
-#if ATTN_BWD_RING
         // into the buffer of tile it − 1, which every wave is done with
         if (it + NRING - 1 < n_it) issue_tile(it + NRING - 1, buf[(it + NRING - 1) % NRING]);
-#else
-        if (it + 1 < n_it) load(it + 1);
-#endif
         const int q0 = q_first + T * (it % n_qt);
-#if ATTN_BWD_RING
         const TileBuf &tb = buf[it % NRING];
-#else
-        const TileBuf &tb = buf[cur];
-#endif
-#if ATTN_BWD_RING
         // per-lane swizzle inputs, opaque to the compiler inside the loop so
         // the few XORs are redone per tile rather than kept in registers
         int lane_x = lane;
         asm volatile("" : "+v"(lane_x));
         const int col_x = lane_x & 31;
-#endif
         if (q0 + T - 1 >= kw0) {  // some query of the tile sees some key of the wave
             // ---- S = Q·Kᵀ and dP = dO·Vᵀ: rows = queries, lane column = key
             f32x16 s, dp;
@@ -274,14 +202,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-#if ATTN_BWD_RING
                 const int off = col_x * 256 + 16 * ((2 * ks + half) ^ bswz(col_x));
                 const bf16x8 a = as<bf16x8>(*(const u32x4 *)((const char *)tb.qs + off));
                 const bf16x8 c = as<bf16x8>(*(const u32x4 *)((const char *)tb.ds + off));
-#else
-                const bf16x8 a = as<bf16x8>(*(const u32x4 *)&tb.qr[col * RP + 16 * ks + 8 * half]);
-                const bf16x8 c = as<bf16x8>(*(const u32x4 *)&tb.dr[col * RP + 16 * ks + 8 * half]);
-#endif
                 s = mfma32x32x16(a, kf[ks], s);
                 dp = mfma32x32x16(c, vf[ks], dp);
             }
@@ -291,13 +214,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi) {
                 const int r0 = 8 * gi + 4 * half;
-#if ATTN_BWD_RING
                 const float4 L4 = *(const float4 *)&tb.lse[r0];  // natural log: to base 2 here
                 const float Lr[4] = {L4.x * kLog2e, L4.y * kLog2e, L4.z * kLog2e, L4.w * kLog2e};
-#else
-                const float4 L4 = *(const float4 *)&tb.lse2[r0];
-                const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
-#endif
                 const float4 D4 = *(const float4 *)&tb.dd[r0];
                 const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
@@ -317,16 +235,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-#if ATTN_BWD_RING
-                    dvacc[db] = mfma32x32x16(tr_operand_sw((const char *)tb.ds, lane_x, mm, db), pf[mm], dvacc[db]);
-                    dkacc[db] = mfma32x32x16(tr_operand_sw((const char *)tb.qs, lane_x, mm, db), sf[mm], dkacc[db]);
-#else
-                    dvacc[db] = mfma32x32x16(tr_operand((const char *)tb.dt, tr_lane, mm, db), pf[mm], dvacc[db]);
-                    dkacc[db] = mfma32x32x16(tr_operand((const char *)tb.qt, tr_lane, mm, db), sf[mm], dkacc[db]);
-#endif
+                    dvacc[db] = mfma32x32x16(tr_operand((const char *)tb.ds, lane_x, mm, db), pf[mm], dvacc[db]);
+                    dkacc[db] = mfma32x32x16(tr_operand((const char *)tb.qs, lane_x, mm, db), sf[mm], dkacc[db]);
                 }
         }
-#if ATTN_BWD_RING
         // this wave's copies of tile it + 1 done; those of later tiles may fly
         {
             const int newer = min(it + NRING - 1, n_it - 1) - (it + 1);
@@ -334,9 +246,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             else if (newer == 1) wait_vmcnt<COPIES_MIN>();
             else wait_vmcnt<0>();
         }
-#else
-        if (it + 1 < n_it) store(buf[cur ^ 1]);
-#endif
         __syncthreads();
     }
 
@@ -359,16 +268,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 }
 
 // ----------------------------------------------------------------------- dQ ---
-struct KTileBuf {          // one 32-key tile: K in both pitches, V by rows
-    uint16_t kr[T * RP], kt[T * TP], vr[T * RP];
+struct KTileBuf {          // one 32-key tile of K and V, 256-byte rows, swizzled (bswz)
+    uint16_t ks[T * D], vs[T * D];
 };
+constexpr int KTILE_COPIES = 2 * (T * D * 2 / 1024);         // 8 + 8
+static_assert(KTILE_COPIES % NWV == 0, "every wave issues the same copies per tile");
 
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dd,
     uint16_t *__restrict__ dq, int Hq, int Hkv, int N, int n_qblk, float scale_log2, float scale)
 {
-    __shared__ __attribute__((aligned(16))) KTileBuf buf[2];
+    __shared__ __attribute__((aligned(1024))) KTileBuf buf[NRING];
 
     // heaviest first: the last query block sees every key
     const int qblk = n_qblk - 1 - (int)(blockIdx.x % n_qblk), bhq = blockIdx.x / n_qblk;
@@ -398,36 +309,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-    const int g4 = lane >> 4, e4 = (lane >> 2) & 3, cq = lane & 3;
-    const int tr_lane = (4 * half + e4) * TPB + 32 * (g4 & 1) + 8 * cq;
     const int n_kt = min(N - 1, q0 + BLK - 1) / T + 1;   // key tiles up to the block's last row
-    u32x4 sk[2], sv[2];
-    auto load = [&](int j) __attribute__((always_inline)) {
+    // copy i of a tile (wave w issues i = w, w + 4, ...): 0..7 K rows
+    // 4i .. 4i + 3, 8..15 V rows; lane l lands at row 4i + l/16, physical
+    // chunk l % 16, and reads logical chunk (l % 16) ^ bswz(row)
+    auto issue_tile = [&](int j, KTileBuf &t) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ch = tid + 256 * u, r = min(T * j + ch / 16, N - 1), c = ch % 16;
-            sk[u] = *(const u32x4 *)(k + kvoff + (size_t)r * D + 8 * c);
-            sv[u] = *(const u32x4 *)(v + kvoff + (size_t)r * D + 8 * c);
-        }
-    };
-    auto store = [&](KTileBuf &t) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ch = tid + 256 * u, r = ch / 16, c = ch % 16;
-            *(u32x4 *)&t.kr[r * RP + 8 * c] = sk[u];
-            *(u32x4 *)&t.kt[r * TP + 8 * c] = sk[u];
-            *(u32x4 *)&t.vr[r * RP + 8 * c] = sv[u];
+        for (int u = 0; u < KTILE_COPIES / NWV; ++u) {
+            const int i = wave + NWV * u;
+            const bool isv = i >= 8;
+            const int ii = isv ? i - 8 : i;
+            const int r = 4 * ii + (lane >> 4), c = (lane & 15) ^ bswz(r);
+            const uint16_t *src = (isv ? v : k) + kvoff + (size_t)min(T * j + r, N - 1) * D + 8 * c;
+            uint16_t *dst = (isv ? t.vs : t.ks) + 512 * ii;
+            __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
         }
     };
 
-    load(0);
-    store(buf[0]);
+    for (int t = 0; t < NRING - 1; ++t)
+        if (t < n_kt) issue_tile(t, buf[t]);
+    wait_vmcnt<0>();
     __syncthreads();
     for (int j = 0; j < n_kt; ++j) {
-        const int cur = j & 1;
-        if (j + 1 < n_kt) load(j + 1);
+        // into the buffer of tile j − 1, which every wave is done with
+        if (j + NRING - 1 < n_kt) issue_tile(j + NRING - 1, buf[(j + NRING - 1) % NRING]);
+        const KTileBuf &tb = buf[j % NRING];
+        int lane_x = lane;  // opaque: the swizzle XORs are redone per tile
+        asm volatile("" : "+v"(lane_x));
+        const int col_x = lane_x & 31;
         const int kt0 = T * j;
-        const KTileBuf &tb = buf[cur];
         if (kt0 <= qw0 + T - 1 && qw0 < N) {
             // ---- Sᵀ = K·Qᵀ, dPᵀ = V·dOᵀ: rows = keys, lane column = query
             f32x16 s, dp;
@@ -435,8 +345,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = as<bf16x8>(*(const u32x4 *)&tb.kr[col * RP + 16 * ks + 8 * half]);
-                const bf16x8 c = as<bf16x8>(*(const u32x4 *)&tb.vr[col * RP + 16 * ks + 8 * half]);
+                const int off = col_x * 256 + 16 * ((2 * ks + half) ^ bswz(col_x));
+                const bf16x8 a = as<bf16x8>(*(const u32x4 *)((const char *)tb.ks + off));
+                const bf16x8 c = as<bf16x8>(*(const u32x4 *)((const char *)tb.vs + off));
                 s = mfma32x32x16(a, qf[ks], s);
                 dp = mfma32x32x16(c, df[ks], dp);
             }
@@ -455,9 +366,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    acc[db] = mfma32x32x16(tr_operand((const char *)tb.kt, tr_lane, mm, db), sf[mm], acc[db]);
+                    acc[db] = mfma32x32x16(tr_operand((const char *)tb.ks, lane_x, mm, db), sf[mm], acc[db]);
         }
-        if (j + 1 < n_kt) store(buf[cur ^ 1]);
+        {   // this wave's copies of tile j + 1 done; those of later tiles may fly
+            constexpr int per = KTILE_COPIES / NWV;
+            const int newer = min(j + NRING - 1, n_kt - 1) - (j + 1);
+            if (newer >= 2) wait_vmcnt<2 * per>();
+            else if (newer == 1) wait_vmcnt<per>();
+            else wait_vmcnt<0>();
+        }
         __syncthreads();
     }
 
