@@ -5,14 +5,15 @@
 // the whole pass (Q outer, K/V inner: the loop order "AI Infra 入门…", §3
 // credits to FlashAttention-2). 64-key K and V tiles stream HBM → LDS with
 // global_load_lds_dwordx4 two tiles ahead of use (a ring of four, no register
-// staging; the bulk tiles take one barrier per pair), both row-major with
-// padded rows: K rows take 272 B (16 B pad) so
-// the rows of a score read start 4 banks apart, V rows take 320 B (64 B pad)
-// so the 8 rows × 32 B that one 32-lane phase of a transposed read touches
-// fall on distinct banks (both measured conflict-free). With padding (rather than a swizzle) every LDS read address is a
-// per-lane base plus a compile-time offset. A wave-wide direct load fills
-// 1 KiB of LDS; the lanes that land on pad slots repeat a neighbour's
-// address.
+// staging; the bulk tiles take one barrier per pair), both row-major in
+// unpadded 256-byte rows: 16-byte chunk c of row r sits at chunk
+// c ^ (4·(r & 3) + (r / 4 & 3)), which spreads both the score reads (one
+// chunk of 16 rows per 16-lane ds_read_b128 phase) and the transposed value
+// reads (4 chunks of 4 rows per 32-lane phase) over all 64 banks. A
+// wave-wide direct load fills 1 KiB of LDS, 4 whole rows, each lane fetching
+// the chunk its slot holds. (Padded rows, 272 B for K and 320 B for V, are
+// also conflict-free and give every read a compile-time offset, but take
+// 37 KiB per tile against 32 and measured 1–2 % slower.)
 //
 //   Sᵀ = K·Qᵀ   v_mfma_f32_32x32x16_bf16, keys as MFMA rows, queries as
 //               columns: each lane owns one query's scores, so the row max and
@@ -74,6 +75,9 @@ namespace {
 #ifndef ATTN_PF_PAIR
 #define ATTN_PF_PAIR 1       // bulk tiles two per barrier, ring of 4 tiles
 #endif
+#ifndef ATTN_PF_SWZ
+#define ATTN_PF_SWZ 1        // unpadded 256-byte tile rows with a chunk swizzle (else padded rows)
+#endif
 #ifndef ATTN_PF_BULK
 #define ATTN_PF_BULK 1       // separate loop for the tiles wholly visible to every wave
 #endif
@@ -81,7 +85,8 @@ namespace {
 
 constexpr int NW = ATTN_PF_WAVES, NBUF = ATTN_PF_PAIR ? 4 : ATTN_PF_NBUF;
 constexpr int D = 128, BR = 32 * NW, BC = 64;
-constexpr int KROWB = 272, VROWB = ATTN_PF_VROWB;   // padded LDS row strides (bytes)
+constexpr int KROWB = ATTN_PF_SWZ ? 256 : 272;                 // LDS row strides (bytes)
+constexpr int VROWB = ATTN_PF_SWZ ? 256 : ATTN_PF_VROWB;
 constexpr int KSLOT = KROWB / 16, VSLOT = VROWB / 16;
 constexpr int KTILEB = BC * KROWB;        // 17 KiB
 constexpr int VTILEB = BC * VROWB;        // 18 KiB
@@ -100,8 +105,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 // wave-wide direct load `idx` brings into LDS slot 64·idx + lane (rows of
 // `slots` 16-byte slots, the last slots of a row being padding). Rows past
 // `rows` (the end of the sequence) are clamped to the last valid row.
+// Swizzled rows (ATTN_PF_SWZ): 16-byte chunk c of tile row r sits at chunk
+// c ^ bswz(r). A score read takes one chunk of 16 rows per 16-lane phase of
+// ds_read_b128, a transposed value read 4 chunks of 4 consecutive rows per
+// 32-lane phase of ds_read_b64_tr_b16; the swizzle puts both on all 64 banks.
+__device__ __forceinline__ int bswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 __device__ __forceinline__ uint32_t tile_src(int idx, int lane, int slots, int rows) {
     const int s = 64 * idx + lane;
+    if constexpr (ATTN_PF_SWZ) {  // a copy fills 4 whole rows
+        const int r = s / 16, c = (s % 16) ^ bswz(r);
+        return (uint32_t)(min(r, rows - 1) * (D * 2) + 16 * c);
+    }
     const int r = min(s / slots, rows - 1);
     const int c = min(s % slots, 15);       // pad slots repeat chunk 15
     return (uint32_t)(r * (D * 2) + 16 * c);
@@ -251,7 +265,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 a = *(const u32x4 *)(kb_ + k_lane + kb * 32 * KROWB + 32 * ks);
+                const u32x4 a = ATTN_PF_SWZ
+                    ? *(const u32x4 *)(kb_ + (kb * 32 + col) * 256 + 16 * ((2 * ks + half) ^ bswz(col)))
+                    : *(const u32x4 *)(kb_ + k_lane + kb * 32 * KROWB + 32 * ks);
                 sacc[kb] = mfma32x32x16(as<bf16x8>(a), qf[ks], sacc[kb]);
             }
         // ---- mask (key > query → −inf); lane's keys: kt0 + 32kb + 8(i/4) + 4half + i%4
@@ -329,9 +345,16 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
             if (ATTN_PF_SCHED && mm) __builtin_amdgcn_sched_barrier(0);  // keep each step's reads together
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const char *p1 = vb_ + v_lane + 16 * mm * VROWB + 64 * db;
+                const char *p1 = vb_ + v_lane + 16 * mm * VROWB + 64 * db, *p2 = p1 + 8 * VROWB;
+                if constexpr (ATTN_PF_SWZ) {
+                    // rows 16mm + 4half + e (+ 8): swizzle 4e + half (+ 2)
+                    const int low = 2 * (g & 1) + (cq >> 1);
+                    const char *r0 = vb_ + (16 * mm + 4 * half + e) * 256 + 64 * (db ^ e) + 8 * (cq & 1);
+                    p1 = r0 + 16 * (low ^ half);
+                    p2 = r0 + 8 * 256 + 16 * (low ^ (half + 2));
+                }
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p1);
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p1 + 8 * VROWB));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p2);
                 const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
                 const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
                 oacc[db] = mfma32x32x16(as<bf16x8>(a), pf[mm], oacc[db]);
