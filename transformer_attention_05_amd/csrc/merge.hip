@@ -145,7 +145,9 @@ hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse,
 {
     if (splits > kMaxSplits) return hipErrorInvalidValue;
     const dim3 grid((unsigned)rows), block(128);
-    if (dv == 128)
+    if (dv == 128 && splits <= 8)  // one pass, no clamped duplicate loads
+        merge_kernel<1, 8><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
+    else if (dv == 128)
         merge_kernel<1, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
     else if (dv == 512)
         merge_kernel<4, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
