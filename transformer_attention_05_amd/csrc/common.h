@@ -78,19 +78,6 @@ __device__ __forceinline__ T as(u32x4 v) { return __builtin_bit_cast(T, v); }
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-// HBM → LDS without registers: global_load_lds_dwordx4 copies 16 bytes per
-// lane from `src` to LDS byte lds_block + 16·lane (lds_block is wave-uniform
-// and goes to M0). Written as asm on purpose: the compiler then does not
-// track the copy, and does not put a wait for every copy in flight in front
-// of each later LDS read (it cannot tell which buffer a transposed read
-// touches). The caller orders the copy with s_waitcnt vmcnt(N) and a barrier
-// before any lane reads the block. There is no output register, so nothing
-// is written behind the compiler's back.
-__device__ __forceinline__ void copy_to_lds16(const void *src, const void *lds_block) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_char *)lds_block;
-    asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 

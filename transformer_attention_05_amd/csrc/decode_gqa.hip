@@ -33,7 +33,9 @@
 // the workspace and a second kernel merges the partials through their
 // log-sum-exp (split-K merge, "AI Infra 入门…", §3). No workgroup waits for
 // another; the kernel boundary orders the partial writes before the merge.
-// Slots at or past kv_len are never read.
+// Slots at or past kv_len are never read. The cache loads carry the
+// non-temporal hint: each cached byte is read once, and keeping it out of the
+// way in the caches measured 29.0 → 27.0 µs for the Llama-3-8B call.
 // FP8 cache (OCP E4M3, one byte per element): the same kernel with the K and
 // V bytes converted to bf16 in registers right after they arrive
 // (v_cvt_scalef32_pk_bf16_fp8 with scale 1, exact: every E4M3 value is a
@@ -82,6 +84,13 @@ template <> struct Chunk<true> {
 
 // One wave's chunk of 32 keys from w0 (rows past key_end repeat its last).
 // kb, vb: the (b, hkv) cache rows, kD elements of 2 (bf16) or 1 (E4M3) bytes.
+#ifndef ATTN_GQA_NT
+#define ATTN_GQA_NT 1  // cache loads with the non-temporal hint (every byte is read once)
+#endif
+__device__ __forceinline__ u32x4 ld_cache(const char *p) {
+    if constexpr (ATTN_GQA_NT) return __builtin_nontemporal_load((const u32x4 *)p);
+    else return *(const u32x4 *)p;
+}
 __device__ __forceinline__ void load_chunk(Chunk<false> &c, const char *kb, const char *vb,
                                            int w0, int key_end, int hcol, int quad, int)
 {
@@ -90,12 +99,12 @@ __device__ __forceinline__ void load_chunk(Chunk<false> &c, const char *kb, cons
         const int key = min(w0 + 16 * blk + hcol, key_end - 1);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            c.k[blk][s] = *(const u32x4 *)(kb + 2 * ((size_t)key * kD + 32 * s + 8 * quad));
+            c.k[blk][s] = ld_cache(kb + 2 * ((size_t)key * kD + 32 * s + 8 * quad));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int key = min(w0 + 4 * i + quad, key_end - 1);
-        c.v[i] = *(const u32x4 *)(vb + 2 * ((size_t)key * kD + 8 * hcol));
+        c.v[i] = ld_cache(vb + 2 * ((size_t)key * kD + 8 * hcol));
     }
 }
 __device__ __forceinline__ void load_chunk(Chunk<true> &c, const char *kb, const char *vb,
@@ -106,12 +115,12 @@ __device__ __forceinline__ void load_chunk(Chunk<true> &c, const char *kb, const
         const int key = min(w0 + 16 * blk + hcol, key_end - 1);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            c.k[blk][h] = *(const u32x4 *)(kb + (size_t)key * kD + 32 * quad + 16 * h);
+            c.k[blk][h] = ld_cache(kb + (size_t)key * kD + 32 * quad + 16 * h);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int key = min(w0 + 8 * i + (lane >> 3), key_end - 1);
-        c.v[i] = *(const u32x4 *)(vb + (size_t)key * kD + 16 * (lane & 7));
+        c.v[i] = ld_cache(vb + (size_t)key * kD + 16 * (lane & 7));
     }
 }
 

@@ -41,7 +41,7 @@
 // not average their rounding errors out, so a second product adds
 // Vᵀ·bf16(P − bf16(P)) and the weights enter with about 16 significant bits.
 // Latent tiles (32 rows × 1152 B) move HBM → LDS with global_load_lds_dwordx4
-// (no register staging, copy_to_lds16) into a ring of MNBUF buffers. The low
+// (no register staging, copy_to_lds16_sv / _v) into a ring of MNBUF buffers. The low
 // three bits of each row's 16-byte chunk index are XORed with
 // (row & 7) ^ (row / 16 & 1), which spreads both the score reads
 // (ds_read_b128, 16 rows at one column) and the transposed value reads
@@ -119,12 +119,35 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_v2i32;
 
-// HBM → LDS like copy_to_lds16, addressed as a wave-uniform base plus a
-// per-lane 32-bit byte offset (the scalar-base form of the instruction), so
-// a full tile's copies need no per-lane address arithmetic.
+// HBM → LDS without registers: global_load_lds_dwordx4 copies 16 bytes per
+// lane to LDS byte lds_block + 16·lane (lds_block is wave-uniform and goes
+// to M0). Written as asm on purpose: the compiler then does not track the
+// copy, and does not put a wait for every copy in flight in front of each
+// later LDS read (it cannot tell which buffer a transposed read touches).
+// The caller orders each copy with s_waitcnt vmcnt(N) and a barrier before
+// any lane reads the block; there is no output register. The non-temporal
+// hint (nt) marks the cache bytes as read once (measured: 193 → 189 µs on
+// the 32K workload).
+// copy_to_lds16_sv: addressed as a wave-uniform base plus a per-lane 32-bit
+// byte offset (the scalar-base form of the instruction), so a full tile's
+// copies need no per-lane address arithmetic.
+#ifndef ATTN_MLA_NT
+#define ATTN_MLA_NT 1  // tile copies with the non-temporal hint (every cache byte is read once)
+#endif
 __device__ __forceinline__ void copy_to_lds16_sv(const void *base, uint32_t off, const void *lds_block) {
     const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_char *)lds_block;
-    asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(base), "{m0}"(m0) : "memory");
+    if constexpr (ATTN_MLA_NT)
+        asm volatile("global_load_lds_dwordx4 %0, %1 nt" :: "v"(off), "s"(base), "{m0}"(m0) : "memory");
+    else
+        asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(base), "{m0}"(m0) : "memory");
+}
+// the per-lane-address form, for partial tiles
+__device__ __forceinline__ void copy_to_lds16_v(const void *src, const void *lds_block) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_char *)lds_block;
+    if constexpr (ATTN_MLA_NT)
+        asm volatile("global_load_lds_dwordx4 %0, off nt" :: "v"(src), "{m0}"(m0) : "memory");
+    else
+        asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
 }
 
 // Physical 16-byte chunk holding logical chunk c of tile row r (an involution).
@@ -255,7 +278,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
                 const int pos = 64 * i + lane;
                 const int r = pos / G::CH, pc = pos % G::CH;
                 const int key = min(t0 + r, key_end - 1);
-                copy_to_lds16(cb + (size_t)key * G::ROWB + 16 * swz_t<F8>(r, pc), &tile[buf][1024 * i]);
+                copy_to_lds16_v(cb + (size_t)key * G::ROWB + 16 * swz_t<F8>(r, pc), &tile[buf][1024 * i]);
             }
         }
     };
