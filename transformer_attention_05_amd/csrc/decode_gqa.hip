@@ -36,6 +36,10 @@
 // Slots at or past kv_len are never read. The cache loads carry the
 // non-temporal hint: each cached byte is read once, and keeping it out of the
 // way in the caches measured 29.0 → 27.0 µs for the Llama-3-8B call.
+// When the number of (batch, K/V head) groups is a multiple of 8, the
+// workgroup ids are remapped so that all splits of group g run on XCD g % 8
+// (workgroups are dealt to the 8 XCDs round-robin by id), and the merge puts
+// the group's rows on the same XCD, where the partials were written.
 // FP8 cache (OCP E4M3, one byte per element): the same kernel with the K and
 // V bytes converted to bf16 in registers right after they arrive
 // (v_cvt_scalef32_pk_bf16_fp8 with scale 1, exact: every E4M3 value is a
@@ -84,6 +88,9 @@ template <> struct Chunk<true> {
 
 // One wave's chunk of 32 keys from w0 (rows past key_end repeat its last).
 // kb, vb: the (b, hkv) cache rows, kD elements of 2 (bf16) or 1 (E4M3) bytes.
+#ifndef ATTN_GQA_XCD
+#define ATTN_GQA_XCD 1  // a group's splits, and its merge rows, on one XCD
+#endif
 #ifndef ATTN_GQA_NT
 #define ATTN_GQA_NT 1  // cache loads with the non-temporal hint (every byte is read once)
 #endif
@@ -147,9 +154,20 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     const char *__restrict__ vc, uint16_t *__restrict__ o, float *__restrict__ lse,
     int Hq, int Hkv, int G, int kv_len, int kv_cap, float scale_log2, int splits,
     int split_keys, float *__restrict__ ws_ml, float *__restrict__ ws_part,
-    const int *__restrict__ kv_lens)
+    const int *__restrict__ kv_lens, int xcd_map)
 {
-    const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+    int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+    if (xcd_map) {
+        // workgroups are dealt to the 8 XCDs round-robin by linear id: give
+        // every split of group g the XCD g % 8 (group count a multiple of 8),
+        // so the merge can find a group's partials in one L2
+        const int lin = blockIdx.x + splits * (blockIdx.y + Hkv * blockIdx.z);
+        const int x = lin % 8, k = lin / 8;
+        const int g = 8 * (k / splits) + x;
+        split = k % splits;
+        hkv = g % Hkv;
+        b = g / Hkv;
+    }
     // ragged batch: this sequence's own length, clamped to [0, kv_len]
     if (kv_lens) kv_len = min(max(kv_lens[b], 0), kv_len);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -353,14 +371,15 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
     float *ws_ml = (float *)(w + p.ws_ml);
     float *ws_part = (float *)(w + p.ws_part);
     const dim3 grid(p.splits, Hkv, B), block(256);
+    const int xcd = ATTN_GQA_XCD && (B * Hkv) % 8 == 0;
     auto kern = fp8 ? decode_gqa_kernel<true> : decode_gqa_kernel<false>;
     kern<<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const char *)k, (const char *)v, (uint16_t *)o, lse, Hq,
         Hkv, Hq / Hkv, kv_len, kv_cap, scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part,
-        kv_lens);
+        kv_lens, xcd);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, kD, st);
+    return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, kD, st, xcd ? Hq / Hkv : 0);
 }
 
 }  // namespace attn

@@ -68,7 +68,7 @@ constexpr int kMaxSplits = 128;  // upper bound the planners respect
 // ml [rows][splits] = float4 (m, ℓ, λ, unused) in base 2 (ℓ feeds the LSE,
 // λ normalises O); part [rows][splits][dv] fp32.
 hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse, int rows,
-                        int splits, int dv, hipStream_t s);
+                        int splits, int dv, hipStream_t s, int xcd_group = 0);
 // The merge of the balanced split of a ragged batch (ragged.h): records
 // [slot][row of the batch's Hq heads], slot = worker + sequence, `workers`
 // workers over tiles of `tile` keys of sequences of length kv_lens[b] (at

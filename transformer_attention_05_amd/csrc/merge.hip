@@ -87,10 +87,17 @@ __device__ __forceinline__ void merge_row(const float4 *__restrict__ mr, size_t 
 template <int CPT, int SPT>  // channels per thread (dv / 128), split slots per pass
 __global__ __launch_bounds__(128) void merge_kernel(
     const float *__restrict__ ml, const float *__restrict__ part, uint16_t *__restrict__ o,
-    float *__restrict__ lse, int splits)
+    float *__restrict__ lse, int splits, int xcd_group)
 {
     constexpr int DV = 128 * CPT;
-    const int row = blockIdx.x, t = threadIdx.x;
+    int row = blockIdx.x;
+    if (xcd_group) {
+        // rows g·G .. g·G + G − 1 of group g on XCD g % 8, where the
+        // group's partials were written (blocks go to XCDs by id % 8)
+        const int x = row % 8, k = row / 8;
+        row = (8 * (k / xcd_group) + x) * xcd_group + k % xcd_group;
+    }
+    const int t = threadIdx.x;
     merge_row<CPT, SPT>((const float4 *)(ml + (size_t)row * splits * 4), 1,
                         part + (size_t)row * splits * DV + CPT * t, DV, splits,
                         o + (size_t)row * DV + CPT * t, lse + row, t);
@@ -141,16 +148,16 @@ __global__ __launch_bounds__(128) void merge_ragged_kernel(
 }  // namespace
 
 hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse, int rows,
-                        int splits, int dv, hipStream_t st)
+                        int splits, int dv, hipStream_t st, int xcd_group)
 {
     if (splits > kMaxSplits) return hipErrorInvalidValue;
     const dim3 grid((unsigned)rows), block(128);
     if (dv == 128 && splits <= 8)  // one pass, no clamped duplicate loads
-        merge_kernel<1, 8><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
+        merge_kernel<1, 8><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits, xcd_group);
     else if (dv == 128)
-        merge_kernel<1, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
+        merge_kernel<1, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits, xcd_group);
     else if (dv == 512)
-        merge_kernel<4, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits);
+        merge_kernel<4, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits, xcd_group);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
