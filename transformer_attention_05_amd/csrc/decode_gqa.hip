@@ -86,8 +86,6 @@ template <> struct Chunk<true> {
     u32x4 v[4];     // row 8·i + lane/8, E4M3 bytes d = 16·(lane%8) .. + 15
 };
 
-// One wave's chunk of 32 keys from w0 (rows past key_end repeat its last).
-// kb, vb: the (b, hkv) cache rows, kD elements of 2 (bf16) or 1 (E4M3) bytes.
 #ifndef ATTN_GQA_XCD
 #define ATTN_GQA_XCD 1  // a group's splits, and its merge rows, on one XCD
 #endif
@@ -98,6 +96,9 @@ __device__ __forceinline__ u32x4 ld_cache(const char *p) {
     if constexpr (ATTN_GQA_NT) return __builtin_nontemporal_load((const u32x4 *)p);
     else return *(const u32x4 *)p;
 }
+
+// One wave's chunk of 32 keys from w0 (rows past key_end repeat its last).
+// kb, vb: the (b, hkv) cache rows, kD elements of 2 (bf16) or 1 (E4M3) bytes.
 __device__ __forceinline__ void load_chunk(Chunk<false> &c, const char *kb, const char *vb,
                                            int w0, int key_end, int hcol, int quad, int)
 {
