@@ -33,9 +33,11 @@
 // the workspace and a second kernel merges the partials through their
 // log-sum-exp (split-K merge, "AI Infra 入门…", §3). No workgroup waits for
 // another; the kernel boundary orders the partial writes before the merge.
-// Slots at or past kv_len are never read. The cache loads carry the
-// non-temporal hint: each cached byte is read once, and keeping it out of the
-// way in the caches measured 29.0 → 27.0 µs for the Llama-3-8B call.
+// Slots at or past kv_len are never read. In a uniform call the cache loads
+// carry the non-temporal hint (each cached byte is read once): 29.0 → 27.0 µs
+// for the Llama-3-8B call. A ragged batch, whose workgroups stream ranges of
+// up to half the cache, measured slower with it (119 → 129 µs) and loads
+// with the default policy.
 // When the number of (batch, K/V head) groups is a multiple of 8, the
 // workgroup ids are remapped so that all splits of group g run on XCD g % 8
 // (workgroups are dealt to the 8 XCDs round-robin by id), and the merge puts
@@ -89,16 +91,16 @@ template <> struct Chunk<true> {
 #ifndef ATTN_GQA_XCD
 #define ATTN_GQA_XCD 1  // a group's splits, and its merge rows, on one XCD
 #endif
-#ifndef ATTN_GQA_NT
-#define ATTN_GQA_NT 1  // cache loads with the non-temporal hint (every byte is read once)
-#endif
+// Cache loads, with the non-temporal hint when NT (every byte is read once).
+template <bool NT>
 __device__ __forceinline__ u32x4 ld_cache(const char *p) {
-    if constexpr (ATTN_GQA_NT) return __builtin_nontemporal_load((const u32x4 *)p);
+    if constexpr (NT) return __builtin_nontemporal_load((const u32x4 *)p);
     else return *(const u32x4 *)p;
 }
 
 // One wave's chunk of 32 keys from w0 (rows past key_end repeat its last).
 // kb, vb: the (b, hkv) cache rows, kD elements of 2 (bf16) or 1 (E4M3) bytes.
+template <bool NT>
 __device__ __forceinline__ void load_chunk(Chunk<false> &c, const char *kb, const char *vb,
                                            int w0, int key_end, int hcol, int quad, int)
 {
@@ -107,14 +109,15 @@ __device__ __forceinline__ void load_chunk(Chunk<false> &c, const char *kb, cons
         const int key = min(w0 + 16 * blk + hcol, key_end - 1);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            c.k[blk][s] = ld_cache(kb + 2 * ((size_t)key * kD + 32 * s + 8 * quad));
+            c.k[blk][s] = ld_cache<NT>(kb + 2 * ((size_t)key * kD + 32 * s + 8 * quad));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int key = min(w0 + 4 * i + quad, key_end - 1);
-        c.v[i] = ld_cache(vb + 2 * ((size_t)key * kD + 8 * hcol));
+        c.v[i] = ld_cache<NT>(vb + 2 * ((size_t)key * kD + 8 * hcol));
     }
 }
+template <bool NT>
 __device__ __forceinline__ void load_chunk(Chunk<true> &c, const char *kb, const char *vb,
                                            int w0, int key_end, int hcol, int quad, int lane)
 {
@@ -123,12 +126,12 @@ __device__ __forceinline__ void load_chunk(Chunk<true> &c, const char *kb, const
         const int key = min(w0 + 16 * blk + hcol, key_end - 1);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            c.k[blk][h] = ld_cache(kb + (size_t)key * kD + 32 * quad + 16 * h);
+            c.k[blk][h] = ld_cache<NT>(kb + (size_t)key * kD + 32 * quad + 16 * h);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int key = min(w0 + 8 * i + (lane >> 3), key_end - 1);
-        c.v[i] = ld_cache(vb + (size_t)key * kD + 16 * (lane & 7));
+        c.v[i] = ld_cache<NT>(vb + (size_t)key * kD + 16 * (lane & 7));
     }
 }
 
@@ -149,7 +152,7 @@ __device__ __forceinline__ bf16x8 k_operand(const Chunk<true> &c, int blk, int s
     return as<bf16x8>(u32x4{a[0], a[1], b[0], b[1]});
 }
 
-template <bool FP8>
+template <bool FP8, bool NT>
 __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     const uint16_t *__restrict__ q, const char *__restrict__ kc,
     const char *__restrict__ vc, uint16_t *__restrict__ o, float *__restrict__ lse,
@@ -292,14 +295,14 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     // the E4M3 cache a third buffer, two chunks in flight, measured slower)
     const int first = key_begin + wave * kWaveKeys;
     Chunk<FP8> ca, cb;
-    if (first < key_end) load_chunk(ca, kbase, vbase, first, key_end, hcol, quad, lane);
+    if (first < key_end) load_chunk<NT>(ca, kbase, vbase, first, key_end, hcol, quad, lane);
     for (int w0 = first; w0 < key_end; w0 += 2 * kChunk) {
         const int w1 = w0 + kChunk;
-        if (w1 < key_end) load_chunk(cb, kbase, vbase, w1, key_end, hcol, quad, lane);
+        if (w1 < key_end) load_chunk<NT>(cb, kbase, vbase, w1, key_end, hcol, quad, lane);
         compute(ca, w0);
         if (w1 >= key_end) break;
         const int w2 = w1 + kChunk;
-        if (w2 < key_end) load_chunk(ca, kbase, vbase, w2, key_end, hcol, quad, lane);
+        if (w2 < key_end) load_chunk<NT>(ca, kbase, vbase, w2, key_end, hcol, quad, lane);
         compute(cb, w1);
     }
 
@@ -373,7 +376,10 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
     float *ws_part = (float *)(w + p.ws_part);
     const dim3 grid(p.splits, Hkv, B), block(256);
     const int xcd = ATTN_GQA_XCD && (B * Hkv) % 8 == 0;
-    auto kern = fp8 ? decode_gqa_kernel<true> : decode_gqa_kernel<false>;
+    // the non-temporal hint pays for short per-workgroup ranges (uniform
+    // calls) and costs for the long ones of a ragged batch (measured both ways)
+    auto kern = kv_lens ? (fp8 ? decode_gqa_kernel<true, false> : decode_gqa_kernel<false, false>)
+                        : (fp8 ? decode_gqa_kernel<true, true> : decode_gqa_kernel<false, true>);
     kern<<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const char *)k, (const char *)v, (uint16_t *)o, lse, Hq,
         Hkv, Hq / Hkv, kv_len, kv_cap, scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part,
