@@ -187,7 +187,8 @@ size_t attn_prefill_chunked_workspace_bytes(int B, int Hq, int Nq, int kv_cap,
  * The cache is split into chunks processed by separate workgroups, each
  * producing a partial (O, running max, running sum); a second kernel on the
  * same stream merges the partials through their log-sum-exp. The split
- * depends only on the shape, so results are bitwise reproducible.
+ * depends only on the shape (and the cache type), so results are bitwise
+ * reproducible.
  * D must be 128 and Hq/Hkv at most 16.
  * Errors: NULL pointer → ATTN_ERR_NULL_POINTER; B, Hq, Hkv < 1, Hq % Hkv,
  * kv_len < 1 or kv_len > kv_cap, or a scale that is not finite and positive
@@ -201,7 +202,9 @@ attn_status attn_decode_gqa(const void *q, const void *k_cache,
                             float scale, void *workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace attn_decode_gqa needs for this shape (0 if invalid). */
+/* Bytes of workspace attn_decode_gqa, attn_decode_gqa_fp8 and
+ * attn_decode_gqa_ragged need for this shape (0 if invalid); one size serves
+ * all three (the E4M3 cache is split into more pieces). */
 size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len,
                                        int D);
 

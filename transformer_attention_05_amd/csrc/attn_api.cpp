@@ -68,7 +68,7 @@ attn_status decode_gqa_impl(const char *fn, const void *q, const void *k_cache,
         !aligned4(kv_lens))
         return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned (o, lse, kv_lens: 4)", fn);
     attn::GqaPlan p;
-    attn::gqa_plan(B, Hq, Hkv, kv_len, &p);
+    attn::gqa_plan(B, Hq, Hkv, kv_len, &p, fp8);
     if (!workspace || workspace_bytes < p.ws_total || !aligned16(workspace))
         return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, p.ws_total,
                     workspace ? workspace_bytes : (size_t)0);
@@ -238,9 +238,12 @@ attn_status attn_prefill_causal_backward(const void *q, const void *k, const voi
 
 size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len, int D)
 {
-    attn::GqaPlan p;
-    if (D != 128 || !attn::gqa_plan(B, Hq, Hkv, kv_len, &p)) return 0;
-    return p.ws_total;
+    // one size serves both cache types: the larger of the two plans
+    attn::GqaPlan p, p8;
+    if (D != 128 || !attn::gqa_plan(B, Hq, Hkv, kv_len, &p, false) ||
+        !attn::gqa_plan(B, Hq, Hkv, kv_len, &p8, true))
+        return 0;
+    return p.ws_total > p8.ws_total ? p.ws_total : p8.ws_total;
 }
 
 attn_status attn_decode_gqa(const void *q, const void *k_cache, const void *v_cache, void *o,

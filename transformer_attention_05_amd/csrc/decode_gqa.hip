@@ -60,15 +60,20 @@
 namespace attn {
 namespace {
 
-#ifndef ATTN_GQA_TARGET_GROUPS
-#define ATTN_GQA_TARGET_GROUPS 512  // workgroups per launch the split aims at
+// Workgroups per launch the split aims at: one per CU for a bf16 cache;
+// an E4M3 workgroup moves half the bytes per key, and two per CU keep
+// enough of them in flight (both measured best of 256 / 512 / 1024).
+#ifndef ATTN_GQA_TARGET_BF16
+#define ATTN_GQA_TARGET_BF16 256
+#endif
+#ifndef ATTN_GQA_TARGET_FP8
+#define ATTN_GQA_TARGET_FP8 512
 #endif
 
 constexpr int kD = 128;
 constexpr int kWaves = 4;
 constexpr int kWaveKeys = 32;
 constexpr int kChunk = kWaves * kWaveKeys;  // keys per workgroup step
-constexpr int kTargetGroups = ATTN_GQA_TARGET_GROUPS;
 constexpr int kDB = kD / 16;                // 16-row blocks of Oᵀ
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -345,14 +350,15 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
 
 }  // namespace
 
-bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p)
+bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p, bool fp8)
 {
     if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || kv_len < 1) return false;
     const int G = Hq / Hkv;
     if (G > 16) return false;
     const long groups = (long)B * Hkv;
     const int chunks = (kv_len + kChunk - 1) / kChunk;
-    int want = (int)((kTargetGroups + groups - 1) / groups);
+    const long target = fp8 ? ATTN_GQA_TARGET_FP8 : ATTN_GQA_TARGET_BF16;
+    int want = (int)((target + groups - 1) / groups);
     int s = want < 1 ? 1 : (want < chunks ? want : chunks);
     if (s > kMaxSplits) s = kMaxSplits;
     const int per = (chunks + s - 1) / s;
