@@ -7,8 +7,8 @@
 // Decomposition. Workgroup (split, hkv, b) owns keys
 // [split·split_keys, min(kv_len, (split+1)·split_keys)) of one K/V head and
 // all G = Hq/Hkv query heads that share it, so each K/V byte is loaded once
-// and used G times. The split count aims at two resident workgroups per CU
-// (one round, no tail). Its four waves take 32-key chunks in turn and
+// and used G times. The split count aims at one workgroup per CU for a bf16
+// cache and two for an E4M3 one (one round, no tail). Its four waves take 32-key chunks in turn and
 // software-pipeline them: the K and V loads of a wave's next chunk are in
 // flight while the current chunk is computed.
 //
