@@ -34,6 +34,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // acc + lo + hi of a packed bf16 pair, in fp32 (v_dot2c_f32_bf16 with (1, 1)).
+// Two floats as two fp16 (round to nearest even), lo in the low half.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const f16x2 h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
 __device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);

@@ -67,16 +67,19 @@ hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, v
 // ---- split-K merge through the log-sum-exp (shared by both decodes) -------
 constexpr int kMaxSplits = 128;  // upper bound the planners respect
 // ml [rows][splits] = float4 (m, ℓ, λ, unused) in base 2 (ℓ feeds the LSE,
-// λ normalises O); part [rows][splits][dv] fp32.
+// λ normalises O); part [rows][splits][dv]: fp32 Õ, or (part_f16) fp16 Õ/λ.
+// xcd_group: 0, or the rows per group when group g's partials were written
+// on XCD g % 8 (the merge then reads them there).
 hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse, int rows,
-                        int splits, int dv, hipStream_t s, int xcd_group = 0);
+                        int splits, int dv, hipStream_t s, int xcd_group = 0,
+                        bool part_f16 = false);
 // The merge of the balanced split of a ragged batch (ragged.h): records
 // [slot][row of the batch's Hq heads], slot = worker + sequence, `workers`
 // workers over tiles of `tile` keys of sequences of length kv_lens[b] (at
 // most max_len). A sequence with no key gets O = 0, LSE = −∞.
 hipError_t launch_merge_ragged(const float *ml, const float *part, void *o, float *lse,
                                const int *kv_lens, int B, int Hq, int max_len, int workers,
-                               int tile, int dv, hipStream_t s);
+                               int tile, int dv, hipStream_t s, bool part_f16);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

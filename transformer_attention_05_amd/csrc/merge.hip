@@ -15,7 +15,8 @@
 // the result is deterministic. An empty split (no key: m = −∞, sums 0) gets
 // weight 0; a row whose splits are all empty gets O = 0 and LSE = −∞.
 //
-// Layout: ml[row][split] = (m, ℓ, λ, unused) as float4, part[row][split][dv];
+// Layout: ml[row][split] = (m, ℓ, λ, unused) as float4, part[row][split][dv]
+// (fp32 Õ, or fp16 Õ/λ from the MLA decode, which the merge weighs by λ);
 // for the balanced split of a ragged batch (ragged.h), ml[slot][row] and
 // part[slot][row][dv] with slot = worker + sequence.
 // One 128-thread block per row; each thread reduces dv/128 channels over the
@@ -30,9 +31,10 @@ namespace {
 // Merge `splits` partial records of one row: record s at ml4[s·mstride]
 // (float4) and pr[s·pstride + ...] (dv floats); thread t owns channels
 // CPT·t .. CPT·t + CPT − 1.
-template <int CPT, int SPT>
+// F16: the records hold Õ/λ in fp16 (weighted by λ here) instead of fp32 Õ.
+template <int CPT, int SPT, bool F16 = false>
 __device__ __forceinline__ void merge_row(const float4 *__restrict__ mr, size_t mstride,
-                                          const float *__restrict__ pr, size_t pstride, int splits,
+                                          const void *__restrict__ pr_, size_t pstride, int splits,
                                           uint16_t *__restrict__ orow, float *__restrict__ lse_out,
                                           int t)
 {
@@ -50,8 +52,15 @@ __device__ __forceinline__ void merge_row(const float4 *__restrict__ mr, size_t 
         for (int u = 0; u < SPT; ++u) {
             const int s = min(s0 + u, splits - 1);
             st[u] = mr[(size_t)s * mstride];
+            if constexpr (F16) {
+                const _Float16 *pr = (const _Float16 *)pr_ + (size_t)s * pstride;
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) x[u][c] = pr[(size_t)s * pstride + c];
+                for (int c = 0; c < CPT; ++c) x[u][c] = (float)pr[c];
+            } else {
+                const float *pr = (const float *)pr_ + (size_t)s * pstride;
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) x[u][c] = pr[c];
+            }
         }
         float Mn = M;
 #pragma unroll
@@ -69,8 +78,9 @@ __device__ __forceinline__ void merge_row(const float4 *__restrict__ mr, size_t 
             const float w = s0 + u < splits ? exp2_fast(st[u].x - Mu) : 0.f;
             l = fmaf(w, st[u].y, l);
             lam = fmaf(w, st[u].z, lam);
+            const float wo = F16 ? w * st[u].z : w;  // Õ = λ·(Õ/λ)
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) acc[c] = fmaf(w, x[u][c], acc[c]);
+            for (int c = 0; c < CPT; ++c) acc[c] = fmaf(wo, x[u][c], acc[c]);
         }
         M = Mn;
     }
@@ -84,7 +94,7 @@ __device__ __forceinline__ void merge_row(const float4 *__restrict__ mr, size_t 
     if (t == 0) *lse_out = (M + log2_fast(l)) * kLn2;
 }
 
-template <int CPT, int SPT>  // channels per thread (dv / 128), split slots per pass
+template <int CPT, int SPT, bool F16 = false>  // channels per thread (dv / 128), split slots per pass
 __global__ __launch_bounds__(128) void merge_kernel(
     const float *__restrict__ ml, const float *__restrict__ part, uint16_t *__restrict__ o,
     float *__restrict__ lse, int splits, int xcd_group)
@@ -98,14 +108,15 @@ __global__ __launch_bounds__(128) void merge_kernel(
         row = (8 * (k / xcd_group) + x) * xcd_group + k % xcd_group;
     }
     const int t = threadIdx.x;
-    merge_row<CPT, SPT>((const float4 *)(ml + (size_t)row * splits * 4), 1,
-                        part + (size_t)row * splits * DV + CPT * t, DV, splits,
-                        o + (size_t)row * DV + CPT * t, lse + row, t);
+    const size_t poff = (size_t)row * splits * DV + CPT * t;
+    merge_row<CPT, SPT, F16>((const float4 *)(ml + (size_t)row * splits * 4), 1,
+                             F16 ? (const void *)((const uint16_t *)part + poff) : (const void *)(part + poff),
+                             DV, splits, o + (size_t)row * DV + CPT * t, lse + row, t);
 }
 
 // Ragged batch, balanced split: row (b, h) gathers the records of the
 // workers whose runs overlap sequence b (slots w + b, consecutive).
-template <int CPT, int SPT>
+template <int CPT, int SPT, bool F16 = false>
 __global__ __launch_bounds__(128) void merge_ragged_kernel(
     const float *__restrict__ ml, const float *__restrict__ part, uint16_t *__restrict__ o,
     float *__restrict__ lse, const int *__restrict__ kv_lens, int B, int Hq, int max_len,
@@ -141,14 +152,16 @@ __global__ __launch_bounds__(128) void merge_ragged_kernel(
     const int P_eff = min(workers, T);
     const int w0 = ragged_owner(first, T, P_eff), w1 = ragged_owner(first + n - 1, T, P_eff);
     const size_t slot0 = (size_t)(w0 + b) * Hq + h;
-    merge_row<CPT, SPT>((const float4 *)ml + slot0, (size_t)Hq, part + slot0 * DV + CPT * t,
-                        (size_t)Hq * DV, w1 - w0 + 1, orow, lse + row, t);
+    const size_t poff = slot0 * DV + CPT * t;
+    merge_row<CPT, SPT, F16>((const float4 *)ml + slot0, (size_t)Hq,
+                             F16 ? (const void *)((const uint16_t *)part + poff) : (const void *)(part + poff),
+                             (size_t)Hq * DV, w1 - w0 + 1, orow, lse + row, t);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse, int rows,
-                        int splits, int dv, hipStream_t st, int xcd_group)
+                        int splits, int dv, hipStream_t st, int xcd_group, bool part_f16)
 {
     if (splits > kMaxSplits) return hipErrorInvalidValue;
     const dim3 grid((unsigned)rows), block(128);
@@ -156,6 +169,8 @@ hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse,
         merge_kernel<1, 8><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits, xcd_group);
     else if (dv == 128)
         merge_kernel<1, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits, xcd_group);
+    else if (dv == 512 && part_f16)
+        merge_kernel<4, 16, true><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits, xcd_group);
     else if (dv == 512)
         merge_kernel<4, 16><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, splits, xcd_group);
     else
@@ -165,7 +180,7 @@ hipError_t launch_merge(const float *ml, const float *part, void *o, float *lse,
 
 hipError_t launch_merge_ragged(const float *ml, const float *part, void *o, float *lse,
                                const int *kv_lens, int B, int Hq, int max_len, int workers,
-                               int tile, int dv, hipStream_t st)
+                               int tile, int dv, hipStream_t st, bool part_f16)
 {
     const dim3 grid((unsigned)(B * Hq)), block(128);
     // a row of a ragged batch has few records (its sequence's share of
@@ -173,6 +188,9 @@ hipError_t launch_merge_ragged(const float *ml, const float *part, void *o, floa
     if (dv == 128)
         merge_ragged_kernel<1, 4><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, kv_lens, B,
                                                           Hq, max_len, workers, tile);
+    else if (dv == 512 && part_f16)
+        merge_ragged_kernel<4, 4, true><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, kv_lens,
+                                                                B, Hq, max_len, workers, tile);
     else if (dv == 512)
         merge_ragged_kernel<4, 4><<<grid, block, 0, st>>>(ml, part, (uint16_t *)o, lse, kv_lens, B,
                                                           Hq, max_len, workers, tile);
