@@ -51,21 +51,51 @@ constexpr int BLK = T * NWV;                // keys (dkdv) or queries (dq) per w
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Transposed MFMA A operand (32 rows of d × 16 k) from a swizzled tile whose
-// rows are the k index (256-byte rows, chunk c of row r at
-// c ^ (4·(r & 3) + (r / 4 & 3))). Slot t of lane 16g + 4e + c holds tile
-// row 16·mm + 8·(t/4) + 4·half + t%4 — the layout the Sᵀ/P accumulator
-// registers 8·mm .. 8·mm + 7 match. Rows 16·mm + 4·half + e (and + 8) have
-// swizzle 4·e + half (+ 2), so chunk 4·db + low lands at
-// 4·(db ^ e) + (low ^ (half [+ 2])).
-__device__ __forceinline__ bf16x8 tr_operand(const char *tile, int lane, int mm, int db) {
-    const int half = lane >> 5, g = lane >> 4, e = (lane >> 2) & 3, c = lane & 3;
-    const int low = 2 * (g & 1) + (c >> 1);
-    const int rlo = 16 * mm + 4 * half + e;
-    const char *plo = tile + rlo * 256 + 64 * (db ^ e) + 16 * (low ^ half) + 8 * (c & 1);
-    const char *phi = tile + (rlo + 8) * 256 + 64 * (db ^ e) + 16 * (low ^ (half + 2)) + 8 * (c & 1);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)plo);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)phi);
+__device__ __forceinline__ int bswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+// Reads of a swizzled tile (256-byte rows, chunk c of row r at
+// c ^ bswz(r), tile base 256-byte aligned). A lane's three base addresses
+// are formed once per tile; each read then takes one XOR with a
+// compile-time constant (the field offset of the tile and 4096·mm ride in
+// the instruction's offset):
+//   row read of k-step ks (chunk 2·ks + half of row col): f = bswz(col),
+//     row = col·256 + 16·(half ^ (f & 1)) + 32·(f >> 1), read at row ^ 32·ks;
+//   transposed read (mm, db): lo (or hi = lo ^ (8·256 + 32)) ^ 64·db.
+// The transposed read is an MFMA A operand (32 rows of d × 16 k) from a tile
+// whose rows are the k index. Slot t of lane 16g + 4e + c holds tile row
+// 16·mm + 8·(t/4) + 4·half + t%4, the layout the Sᵀ/P accumulator registers
+// 8·mm .. 8·mm + 7 match. Rows 16·mm + 4·half + e (and + 8) have swizzle
+// 4·e + half (+ 2), so chunk 4·db + low lands at 4·(db ^ e) + (low ^ (half [+ 2])).
+struct SwzLane {
+    uint32_t row, lo, hi;  // LDS byte addresses
+};
+struct SwzOff {
+    uint32_t row, lo, hi;  // the same relative to the tile
+};
+__device__ __forceinline__ SwzOff swz_off(int lane) {
+    const int col = lane & 31, half = lane >> 5, g = lane >> 4, e = (lane >> 2) & 3, c = lane & 3;
+    const int f = bswz(col), low = 2 * (g & 1) + (c >> 1);
+    SwzOff z;
+    z.row = col * 256 + 16 * (half ^ (f & 1)) + 32 * (f >> 1);
+    z.lo = (4 * half + e) * 256 + 64 * e + 16 * (low ^ half) + 8 * (c & 1);
+    z.hi = z.lo ^ (8 * 256 + 32);
+    return z;
+}
+__device__ __forceinline__ SwzLane swz_lane(const void *tile, const SwzOff &o) {
+    const uint32_t base = (uint32_t)(uintptr_t)(const lds_char *)tile;
+    return SwzLane{base + o.row, base + o.lo, base + o.hi};
+}
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+template <int FIELD>
+__device__ __forceinline__ u32x4 row_read(const SwzLane &z, int ks) {
+    return *(lds_u32x4 *)(uintptr_t)((z.row ^ (32 * ks)) + FIELD);
+}
+template <int FIELD>
+__device__ __forceinline__ bf16x8 tr_read(const SwzLane &z, int mm, int db) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(uintptr_t)((z.lo ^ (64 * db)) + FIELD + 16 * 256 * mm));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(uintptr_t)((z.hi ^ (64 * db)) + FIELD + 16 * 256 * mm));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return as<bf16x8>(u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
@@ -115,7 +145,6 @@ struct TileBuf {
 constexpr int NRING = 4;                                    // tiles in LDS
 constexpr int TILE_COPIES = 2 * (T * D * 2 / 1024) + 1;     // 8 + 8 + LSE/D
 constexpr int COPIES_MIN = TILE_COPIES / NWV;               // copies every wave issues per tile
-__device__ __forceinline__ int bswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -190,11 +219,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         if (it + NRING - 1 < n_it) issue_tile(it + NRING - 1, buf[(it + NRING - 1) % NRING]);
         const int q0 = q_first + T * (it % n_qt);
         const TileBuf &tb = buf[it % NRING];
-        // per-lane swizzle inputs, opaque to the compiler inside the loop so
-        // the few XORs are redone per tile rather than kept in registers
+        // the lane's read addresses; the lane index is made opaque so that they
+        // are rebuilt per tile (a few VALU) rather than held in registers
         int lane_x = lane;
         asm volatile("" : "+v"(lane_x));
-        const int col_x = lane_x & 31;
+        const SwzLane z = swz_lane(&tb, swz_off(lane_x));
         if (q0 + T - 1 >= kw0) {  // some query of the tile sees some key of the wave
             // ---- S = Q·Kᵀ and dP = dO·Vᵀ: rows = queries, lane column = key
             f32x16 s, dp;
@@ -202,9 +231,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int off = col_x * 256 + 16 * ((2 * ks + half) ^ bswz(col_x));
-                const bf16x8 a = as<bf16x8>(*(const u32x4 *)((const char *)tb.qs + off));
-                const bf16x8 c = as<bf16x8>(*(const u32x4 *)((const char *)tb.ds + off));
+                const bf16x8 a = as<bf16x8>(row_read<offsetof(TileBuf, qs)>(z, ks));
+                const bf16x8 c = as<bf16x8>(row_read<offsetof(TileBuf, ds)>(z, ks));
                 s = mfma32x32x16(a, kf[ks], s);
                 dp = mfma32x32x16(c, vf[ks], dp);
             }
@@ -235,8 +263,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    dvacc[db] = mfma32x32x16(tr_operand((const char *)tb.ds, lane_x, mm, db), pf[mm], dvacc[db]);
-                    dkacc[db] = mfma32x32x16(tr_operand((const char *)tb.qs, lane_x, mm, db), sf[mm], dkacc[db]);
+                    dvacc[db] = mfma32x32x16(tr_read<offsetof(TileBuf, ds)>(z, mm, db), pf[mm], dvacc[db]);
+                    dkacc[db] = mfma32x32x16(tr_read<offsetof(TileBuf, qs)>(z, mm, db), sf[mm], dkacc[db]);
                 }
         }
         // this wave's copies of tile it + 1 done; those of later tiles may fly
@@ -330,13 +358,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         if (t < n_kt) issue_tile(t, buf[t]);
     wait_vmcnt<0>();
     __syncthreads();
+    const SwzOff zo = swz_off(lane);
     for (int j = 0; j < n_kt; ++j) {
         // into the buffer of tile j − 1, which every wave is done with
         if (j + NRING - 1 < n_kt) issue_tile(j + NRING - 1, buf[(j + NRING - 1) % NRING]);
         const KTileBuf &tb = buf[j % NRING];
-        int lane_x = lane;  // opaque: the swizzle XORs are redone per tile
-        asm volatile("" : "+v"(lane_x));
-        const int col_x = lane_x & 31;
+        const SwzLane z = swz_lane(&tb, zo);
         const int kt0 = T * j;
         if (kt0 <= qw0 + T - 1 && qw0 < N) {
             // ---- Sᵀ = K·Qᵀ, dPᵀ = V·dOᵀ: rows = keys, lane column = query
@@ -345,9 +372,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int off = col_x * 256 + 16 * ((2 * ks + half) ^ bswz(col_x));
-                const bf16x8 a = as<bf16x8>(*(const u32x4 *)((const char *)tb.ks + off));
-                const bf16x8 c = as<bf16x8>(*(const u32x4 *)((const char *)tb.vs + off));
+                const bf16x8 a = as<bf16x8>(row_read<offsetof(KTileBuf, ks)>(z, ks));
+                const bf16x8 c = as<bf16x8>(row_read<offsetof(KTileBuf, vs)>(z, ks));
                 s = mfma32x32x16(a, qf[ks], s);
                 dp = mfma32x32x16(c, df[ks], dp);
             }
@@ -366,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    acc[db] = mfma32x32x16(tr_operand((const char *)tb.ks, lane_x, mm, db), sf[mm], acc[db]);
+                    acc[db] = mfma32x32x16(tr_read<offsetof(KTileBuf, ks)>(z, mm, db), sf[mm], acc[db]);
         }
         {   // this wave's copies of tile j + 1 done; those of later tiles may fly
             constexpr int per = KTILE_COPIES / NWV;
