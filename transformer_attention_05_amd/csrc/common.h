@@ -84,6 +84,7 @@ template <typename T>
 __device__ __forceinline__ T as(u32x4 v) { return __builtin_bit_cast(T, v); }
 
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }

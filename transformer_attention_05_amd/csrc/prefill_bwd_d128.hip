@@ -85,7 +85,6 @@ __device__ __forceinline__ SwzLane swz_lane(const void *tile, const SwzOff &o) {
     const uint32_t base = (uint32_t)(uintptr_t)(const lds_char *)tile;
     return SwzLane{base + o.row, base + o.lo, base + o.hi};
 }
-typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 template <int FIELD>
 __device__ __forceinline__ u32x4 row_read(const SwzLane &z, int ks) {
     return *(lds_u32x4 *)(uintptr_t)((z.row ^ (32 * ks)) + FIELD);
