@@ -86,6 +86,37 @@ __device__ __forceinline__ T as(u32x4 v) { return __builtin_bit_cast(T, v); }
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
+// HBM → LDS without registers: each lane copies 16 (or 4) bytes from src to
+// LDS byte lds_block + 16·lane (+ 4·lane); lds_block is wave-uniform (M0).
+// Written as asm on purpose: the compiler then does not track the copy. When
+// it does (the builtin), it cannot tell which LDS buffer a later read
+// touches, and puts a wait for every copy in flight in front of the first
+// LDS read after a copy and in front of each barrier, which leaves no copy in
+// flight across compute. The caller orders each copy with wait_vmcnt and a
+// barrier before any lane reads the block; there is no output register.
+__device__ __forceinline__ void copy16_to_lds(const void *src, const void *lds_block) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_char *)lds_block;
+    asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const void *src, const void *lds_block) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_char *)lds_block;
+    asm volatile("global_load_lds_dword %0, off" :: "v"(src), "{m0}"(m0) : "memory");
+}
+
+// Uses register fragments here, so that the compiler waits for the loads
+// that produce them at this point. Its own waits do not see the asm copies
+// above; a wait it placed inside a loop for a fragment loaded before the
+// loop would also wait for every copy in flight, each iteration.
+template <int N>
+__device__ __forceinline__ void regs_ready(const bf16x8 (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const u32x4 w = __builtin_bit_cast(u32x4, x[i]);
+        asm volatile("" :: "v"(w));
+    }
+}
+__device__ __forceinline__ void regs_ready(float x) { asm volatile("" :: "v"(x)); }
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 

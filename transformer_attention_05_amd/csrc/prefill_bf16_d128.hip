@@ -99,7 +99,6 @@ constexpr float kLazy = 8.f;  // base-2 headroom before the reference max moves
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Global byte offset, within a K/V tile, of the 16 bytes that lane `lane` of
 // wave-wide direct load `idx` brings into LDS slot 64·idx + lane (rows of
@@ -191,7 +190,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     // Loads 0 .. NW·⌊LOADS/NW⌋ − 1 are spread evenly over the waves; the
     // remaining LOADS % NW go to the first waves.
     auto issue = [&](const char *src, char *dst) {
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
+        copy16_to_lds(src, dst);
     };
     auto load_tile = [&](int j, int buf) {
         const char *kb = Kp + (size_t)j * BC * D * 2, *vb = Vp + (size_t)j * BC * D * 2;
@@ -249,6 +248,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         // the first tile resident: only the loads of later tiles may be outstanding
         if (NBUF == 3 && t_hi - t_lo > 1) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
     }
+    regs_ready(qf);
     __syncthreads();
 
     // One key tile for this wave: Sᵀ, online softmax, Oᵀ update. MASK is set

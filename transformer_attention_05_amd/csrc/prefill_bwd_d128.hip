@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             if (j == TILE_COPIES - 1) {
                 const int r = min(q0 + (lane & 31), N - 1);
                 const float *src = lane < 32 ? lse + qoff + r : dd + qoff + r;
-                __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)t.lse, 4, 0, 0);
+                copy4_to_lds(src, t.lse);
                 continue;
             }
             const bool isd = j >= 8;
@@ -205,13 +205,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             const int r = 4 * i + (lane >> 4), c = (lane & 15) ^ bswz(r);
             const uint16_t *src = (isd ? dout : q) + (qoff + min(q0 + r, N - 1)) * D + 8 * c;
             uint16_t *dst = (isd ? t.ds : t.qs) + 512 * i;
-            __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+            copy16_to_lds(src, dst);
         }
     };
 
     for (int t = 0; t < NRING - 1; ++t)
         if (t < n_it) issue_tile(t, buf[t]);
     wait_vmcnt<0>();
+    regs_ready(kf);
+    regs_ready(vf);
     __syncthreads();
     for (int it = 0; it < n_it; ++it) {
         // into the buffer of tile it − 1, which every wave is done with
@@ -349,13 +351,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             const int r = 4 * ii + (lane >> 4), c = (lane & 15) ^ bswz(r);
             const uint16_t *src = (isv ? v : k) + kvoff + (size_t)min(T * j + r, N - 1) * D + 8 * c;
             uint16_t *dst = (isv ? t.vs : t.ks) + 512 * ii;
-            __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+            copy16_to_lds(src, dst);
         }
     };
 
     for (int t = 0; t < NRING - 1; ++t)
         if (t < n_kt) issue_tile(t, buf[t]);
     wait_vmcnt<0>();
+    regs_ready(qf);
+    regs_ready(df);
+    regs_ready(lse2);
+    regs_ready(dq_d);
     __syncthreads();
     const SwzOff zo = swz_off(lane);
     for (int j = 0; j < n_kt; ++j) {
