@@ -297,17 +297,21 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     };
 
     // ---- software-pipelined chunk loop (ping-pong register buffers; for
-    // the E4M3 cache a third buffer, two chunks in flight, measured slower)
+    // the E4M3 cache a third buffer, two chunks in flight, measured slower).
+    // The next chunk is loaded whether or not it exists (past the end every
+    // lane reads the last key row, a cache hit): with a conditional load the
+    // compiler's wait for the current chunk has to assume the load was not
+    // issued, and then also waits for the next chunk when it was.
     const int first = key_begin + wave * kWaveKeys;
     Chunk<FP8> ca, cb;
     if (first < key_end) load_chunk<NT>(ca, kbase, vbase, first, key_end, hcol, quad, lane);
     for (int w0 = first; w0 < key_end; w0 += 2 * kChunk) {
         const int w1 = w0 + kChunk;
-        if (w1 < key_end) load_chunk<NT>(cb, kbase, vbase, w1, key_end, hcol, quad, lane);
+        load_chunk<NT>(cb, kbase, vbase, w1, key_end, hcol, quad, lane);
         compute(ca, w0);
         if (w1 >= key_end) break;
         const int w2 = w1 + kChunk;
-        if (w2 < key_end) load_chunk<NT>(ca, kbase, vbase, w2, key_end, hcol, quad, lane);
+        load_chunk<NT>(ca, kbase, vbase, w2, key_end, hcol, quad, lane);
         compute(cb, w1);
     }
 
