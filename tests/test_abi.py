@@ -86,7 +86,9 @@ def test_decode_gqa_validation(lib):
 
 
 def test_backward_workspace_query():
-    assert attn.attn_prefill_causal_backward_workspace_bytes(2, 4, 100, 128) == 3328
+    # D and LSE·log2(e) per query row, fp32, rows padded to the 32-row tile:
+    # 2 arrays × (2·4 heads) × 128 rows × 4 B
+    assert attn.attn_prefill_causal_backward_workspace_bytes(2, 4, 100, 128) == 8192
 
 
 def test_decode_gqa_workspace_query():

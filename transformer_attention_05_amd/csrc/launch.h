@@ -40,7 +40,8 @@ size_t prefill_chunked_workspace_bytes(int B, int Hq, int Nq, int kv_cap);
 hipError_t launch_prefill_chunked_d128(const void *q, const void *k, const void *v, void *o,
                                        float *lse, const int *kv_lens, int B, int Hq, int Hkv,
                                        int N, int kv_cap, float scale, void *ws, hipStream_t s);
-// Backward of the causal prefill, d = 128, bf16; ws holds B·Hq·N fp32 (D = dO·O).
+// Backward of the causal prefill, d = 128, bf16; ws holds two fp32 arrays
+// [B·Hq][N rounded up to 32]: D = dO·O and LSE·log₂e (+∞ past the sequence).
 size_t prefill_bwd_workspace_bytes(int B, int Hq, int N);
 hipError_t launch_prefill_bwd_d128(const void *q, const void *k, const void *v, const void *o,
                                    const float *lse, const void *dout, void *dq, void *dk,

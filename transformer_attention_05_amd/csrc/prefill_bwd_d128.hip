@@ -111,14 +111,24 @@ __device__ __forceinline__ void pack_b(const f32x16 &acc, bf16x8 (&out)[2]) {
 }
 
 // ---------------------------------------------------------------- D = dO·O ---
+// Row statistics in the workspace, rows of each (b, head) padded to Np, a
+// multiple of the 32-row tile: dd = D = dO·O and l2 = LSE·log₂e; a padded
+// row gets D = 0 and l2 = +∞, so that its weights 2^(s·scale·log₂e − l2)
+// are 0 without a test in the dK/dV loop.
 __global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t *__restrict__ o,
                                                       const uint16_t *__restrict__ dout,
-                                                      float *__restrict__ dd, long rows)
+                                                      const float *__restrict__ lse,
+                                                      float *__restrict__ dd, float *__restrict__ l2,
+                                                      long rows_p, int N, int Np)
 {
-    const long row = (long)blockIdx.x * 16 + threadIdx.x / 16;
+    const long rp = (long)blockIdx.x * 16 + threadIdx.x / 16;  // padded row
     const int c = threadIdx.x % 16;  // 8 elements each
+    const long bh = rp / Np;
+    const int r = (int)(rp - bh * Np);
+    const long row = bh * N + r;
+    const bool real = rp < rows_p && r < N;
     float acc = 0.f;
-    if (row < rows) {
+    if (real) {
         const u32x4 a = *(const u32x4 *)(o + row * D + 8 * c);
         const u32x4 b = *(const u32x4 *)(dout + row * D + 8 * c);
 #pragma unroll
@@ -127,19 +137,22 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t *__restrict
     }
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
-    if (row < rows && c == 0) dd[row] = acc;
+    if (rp < rows_p && c == 0) {
+        dd[rp] = acc;
+        l2[rp] = real ? lse[row] * kLog2e : INFINITY;
+    }
 }
 
 // ------------------------------------------------------------------- dK, dV ---
 // One 32-row query tile: Q and dO rows of 256 B, unpadded, 16-byte chunk c
-// of row r stored at chunk c ^ bswz(r); then the 32 raw LSE (natural log)
-// and D values. The swizzle spreads both reads over all 64 banks: a row
+// of row r stored at chunk c ^ bswz(r); then the 32 rows' LSE·log₂e and D
+// values (+∞ and 0 for rows past the sequence). The swizzle spreads both reads over all 64 banks: a row
 // read (ds_read_b128) takes one chunk of 16 rows per 16-lane phase, a
 // transposed read (ds_read_b64_tr_b16) 4 chunks of 4 consecutive rows per
 // 32-lane phase. A wave-wide 1 KiB copy fills 4 whole rows.
 struct TileBuf {
     uint16_t qs[T * D], ds[T * D];
-    float lse[T], dd[T];
+    float l2[T], dd[T];
 };
 constexpr int NRING = 4;                                    // tiles in LDS
 constexpr int TILE_COPIES = 2 * (T * D * 2 / 1024) + 1;     // 8 + 8 + LSE/D
@@ -147,8 +160,8 @@ constexpr int COPIES_MIN = TILE_COPIES / NWV;               // copies every wave
 
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dd,
-    uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, int Hq, int Hkv, int N, int n_kblk,
+    const uint16_t *__restrict__ dout, const float *__restrict__ l2, const float *__restrict__ dd,
+    uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, int Hq, int Hkv, int N, int Np, int n_kblk,
     float scale_log2, float scale)
 {
     __shared__ __attribute__((aligned(1024))) TileBuf buf[NRING];
@@ -194,10 +207,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         const int h = hkv * G + it / n_qt, q0 = q_first + T * (it % n_qt);
         const size_t qoff = ((size_t)b * Hq + h) * N;
         for (int j = wave; j < TILE_COPIES; j += NWV) {  // wave-uniform
-            if (j == TILE_COPIES - 1) {
-                const int r = min(q0 + (lane & 31), N - 1);
-                const float *src = lane < 32 ? lse + qoff + r : dd + qoff + r;
-                copy4_to_lds(src, t.lse);
+            if (j == TILE_COPIES - 1) {  // padded rows: q0 + 31 < Np
+                const size_t r = ((size_t)b * Hq + h) * Np + q0 + (lane & 31);
+                copy4_to_lds(lane < 32 ? l2 + r : dd + r, t.l2);
                 continue;
             }
             const bool isd = j >= 8;
@@ -239,19 +251,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             }
             // ---- P = 2^(s·scale·log2 e − LSE₂), dS = P ∘ (dP − D); query rows
             // 8·(i/4) + 4·half + i%4 (their LSE and D come as float4 runs)
-            const bool edge = q0 < kw0 + T - 1 || q0 + T > N;  // masked keys or padded queries
+            // (padded query rows: l2 = +∞ gives P = 0, D = 0 gives dS = 0).
+            // Causal mask key > query, i.e. t > 8·(i/4) + i%4 with
+            // t = key − q0 − 4·half: it can hold only in the diagonal tile
+            // (q0 = kw0); later tiles have t < 0.
+            const int t = key - q0 - 4 * half;
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi) {
-                const int r0 = 8 * gi + 4 * half;
-                const float4 L4 = *(const float4 *)&tb.lse[r0];  // natural log: to base 2 here
-                const float Lr[4] = {L4.x * kLog2e, L4.y * kLog2e, L4.z * kLog2e, L4.w * kLog2e};
-                const float4 D4 = *(const float4 *)&tb.dd[r0];
+                const float4 L4 = *(const float4 *)&tb.l2[8 * gi + 4 * half];
+                const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+                const float4 D4 = *(const float4 *)&tb.dd[8 * gi + 4 * half];
                 const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int i = 4 * gi + j, qi = q0 + r0 + j;
+                    const int i = 4 * gi + j;
                     float p = exp2_fast(fmaf(s[i], scale_log2, -Lr[j]));
-                    if (edge && (key > qi || qi >= N)) p = 0.f;
+                    if (t > 8 * gi + j) p = 0.f;
                     s[i] = p;
                     dp[i] = p * (dp[i] - Dr[j]);
                 }
@@ -306,7 +321,7 @@ static_assert(KTILE_COPIES % NWV == 0, "every wave issues the same copies per ti
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const uint16_t *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ dd,
-    uint16_t *__restrict__ dq, int Hq, int Hkv, int N, int n_qblk, float scale_log2, float scale)
+    uint16_t *__restrict__ dq, int Hq, int Hkv, int N, int Np, int n_qblk, float scale_log2, float scale)
 {
     __shared__ __attribute__((aligned(1024))) KTileBuf buf[NRING];
 
@@ -331,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
     }
     const float lse2 = lse[(size_t)bhq * N + min(qrow, N - 1)] * kLog2e;
-    const float dq_d = dd[(size_t)bhq * N + min(qrow, N - 1)];
+    const float dq_d = dd[(size_t)bhq * Np + min(qrow, N - 1)];
     f32x16 acc[DB];  // dQᵀ: rows d, column = query
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -382,14 +397,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 s = mfma32x32x16(a, qf[ks], s);
                 dp = mfma32x32x16(c, df[ks], dp);
             }
-            const bool diag = kt0 + T - 1 > qw0;  // keys after some query of the wave
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kj = kt0 + 8 * (i / 4) + 4 * half + (i % 4);
-                float p = exp2_fast(fmaf(s[i], scale_log2, -lse2));
-                if (diag && kj > qrow) p = 0.f;
-                dp[i] = p * (dp[i] - dq_d);
+            for (int i = 0; i < 16; ++i) s[i] = exp2_fast(fmaf(s[i], scale_log2, -lse2));
+            if (kt0 + T - 1 > qw0) {  // keys after some query of the wave (wave-uniform)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (kt0 + 8 * (i / 4) + 4 * half + (i % 4) > qrow) s[i] = 0.f;
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dp[i] = s[i] * (dp[i] - dq_d);
             bf16x8 sf[2];
             pack_b(dp, sf);
             // ---- dQᵀ += Kᵀ·dSᵀ (k = the tile's keys)
@@ -424,9 +440,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 }  // namespace
 
+// dd then l2, each [B·Hq][Np] fp32 (Np = N rounded up to the 32-row tile)
+static size_t bwd_rows_padded(int B, int Hq, int N) { return (size_t)B * Hq * ((N + T - 1) / T * T); }
 size_t prefill_bwd_workspace_bytes(int B, int Hq, int N)
 {
-    return align_up(sizeof(float) * (size_t)B * Hq * N, 256);
+    return align_up(2 * sizeof(float) * bwd_rows_padded(B, Hq, N), 256);
 }
 
 hipError_t launch_prefill_bwd_d128(const void *q, const void *k, const void *v, const void *o,
@@ -434,22 +452,23 @@ hipError_t launch_prefill_bwd_d128(const void *q, const void *k, const void *v, 
                                    void *dv, int B, int Hq, int Hkv, int N, float scale,
                                    void *ws, hipStream_t st)
 {
-    float *dd = (float *)ws;
-    const long rows = (long)B * Hq * N;
-    bwd_dot_kernel<<<dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st>>>(
-        (const uint16_t *)o, (const uint16_t *)dout, dd, rows);
+    const int Np = (N + T - 1) / T * T;
+    const long rows_p = (long)bwd_rows_padded(B, Hq, N);
+    float *dd = (float *)ws, *l2 = dd + rows_p;
+    bwd_dot_kernel<<<dim3((unsigned)((rows_p + 15) / 16)), dim3(256), 0, st>>>(
+        (const uint16_t *)o, (const uint16_t *)dout, lse, dd, l2, rows_p, N, Np);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const float sl2 = scale * kLog2e;
     const int n_blk = (N + BLK - 1) / BLK;
     bwd_dkdv_kernel<<<dim3((unsigned)(n_blk * B * Hkv)), dim3(256), 0, st>>>(
-        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse,
-        dd, (uint16_t *)dk, (uint16_t *)dv, Hq, Hkv, N, n_blk, sl2, scale);
+        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, l2,
+        dd, (uint16_t *)dk, (uint16_t *)dv, Hq, Hkv, N, Np, n_blk, sl2, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     bwd_dq_kernel<<<dim3((unsigned)(n_blk * B * Hq)), dim3(256), 0, st>>>(
         (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse,
-        dd, (uint16_t *)dq, Hq, Hkv, N, n_blk, sl2, scale);
+        dd, (uint16_t *)dq, Hq, Hkv, N, Np, n_blk, sl2, scale);
     return hipGetLastError();
 }
 
