@@ -304,10 +304,10 @@ def summarize_counters(fetch_db: str, write_db: str) -> dict:
         "dispatches": {"fetch": nf, "write": nw},
         "hbm_bytes_per_call": round(total),
         "algorithmic_bytes_per_call": 134349824,
-        "commands": ["rocprofv3 --pmc FETCH_SIZE -d gpurun_out/fetch -o fetch -- python3 -u bench.py --counters",
-                     "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/write -o write -- python3 -u bench.py --counters",
-                     "python3 bench.py --summarize-counters gpurun_out/fetch/fetch_results.db "
-                     "gpurun_out/write/write_results.db"],
+        "commands": ["rocprofv3 --pmc FETCH_SIZE -d prof/fetch -o fetch -- python3 -u bench.py --counters",
+                     "rocprofv3 --pmc WRITE_SIZE -d prof/write -o write -- python3 -u bench.py --counters",
+                     "python3 bench.py --summarize-counters prof/fetch/fetch_results.db "
+                     "prof/write/write_results.db"],
     }
 
 
