@@ -60,14 +60,14 @@
 namespace attn {
 namespace {
 
-// Workgroups per launch the split aims at: one per CU for a bf16 cache;
-// an E4M3 workgroup moves half the bytes per key, and two per CU keep
-// enough of them in flight (both measured best of 256 / 512 / 1024).
+// Workgroups per launch the split aims at: one per CU, for a bf16 and for
+// an E4M3 cache (both measured best of 256 / 512 / 1024 once the next
+// chunk's loads stay in flight during compute).
 #ifndef ATTN_GQA_TARGET_BF16
 #define ATTN_GQA_TARGET_BF16 256
 #endif
 #ifndef ATTN_GQA_TARGET_FP8
-#define ATTN_GQA_TARGET_FP8 512
+#define ATTN_GQA_TARGET_FP8 256
 #endif
 
 constexpr int kD = 128;
