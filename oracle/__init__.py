@@ -58,13 +58,16 @@ def _load():
             lib.oracle_decode_mla.argtypes = [dp, dp, i, i, i, i, i, i, d, dp, dp, i]
             lib.oracle_prefill_causal_backward.argtypes = [dp, dp, dp, dp, i, i, i, i, i, d,
                                                            dp, dp, dp, i]
+            lib.oracle_prefill_causal_backward_rows.argtypes = [dp, dp, dp, dp, i, i, i, i, i, d,
+                                                                ip, i, ip, i, dp, dp, dp, i]
             lib.oracle_prefill_chunked.argtypes = [dp, dp, dp, i, i, i, i, ip, i, i, d, ip, i,
                                                    dp, dp, i]
             lib.oracle_decode_gqa_ragged.argtypes = [dp, dp, dp, i, i, i, ip, i, i, d, dp, dp, i]
             lib.oracle_decode_mla_ragged.argtypes = [dp, dp, i, i, ip, i, i, i, d, dp, dp, i]
             for f in (lib.oracle_prefill_causal, lib.oracle_decode_gqa, lib.oracle_decode_mla,
                       lib.oracle_prefill_chunked, lib.oracle_decode_gqa_ragged,
-                      lib.oracle_decode_mla_ragged, lib.oracle_prefill_causal_backward):
+                      lib.oracle_decode_mla_ragged, lib.oracle_prefill_causal_backward,
+                      lib.oracle_prefill_causal_backward_rows):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -269,4 +272,29 @@ def prefill_causal_backward(q, k, v, dout, scale, threads=None):
         _ptr(dq), _ptr(dk), _ptr(dv), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_prefill_causal_backward rejected its arguments")
+    return dq, dk, dv
+
+
+def prefill_causal_backward_rows(q, k, v, dout, scale, rows=None, keys=None, threads=None):
+    """The gradients of prefill_causal_backward at chosen query rows (dq) and
+    chosen keys (dk, dv), with the work spread over rows and keys so a long
+    sequence is affordable. Default: every row and every key.
+
+    Returns (dq [B,Hq,R,D], dk [B,Hkv,K,D], dv [B,Hkv,K,D]) in float64."""
+    q = np.asarray(q)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, D) and v.shape == k.shape and dout.shape == q.shape
+    rows = np.arange(N, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    keys = np.arange(N, dtype=np.int32) if keys is None else np.ascontiguousarray(keys, dtype=np.int32)
+    q64, k64, v64, d64 = widen(q), widen(k), widen(v), widen(dout)
+    dq = np.empty((B, Hq, rows.shape[0], D))
+    dk = np.empty((B, Hkv, keys.shape[0], D))
+    dv = np.empty((B, Hkv, keys.shape[0], D))
+    rc = _load().oracle_prefill_causal_backward_rows(
+        _ptr(q64), _ptr(k64), _ptr(v64), _ptr(d64), B, Hq, Hkv, N, D, float(scale),
+        _iptr(rows), rows.shape[0], _iptr(keys), keys.shape[0], _ptr(dq), _ptr(dk), _ptr(dv),
+        threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_prefill_causal_backward_rows rejected its arguments")
     return dq, dk, dv

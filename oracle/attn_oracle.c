@@ -472,3 +472,154 @@ int oracle_decode_mla_ragged(const double *q, const double *ckv, int B, int Hq,
     mla_ctx c = {q, ckv, B, Hq, 0, kv_cap, Dqk, Dv, kv_lens, scale, o, lse};
     return run_units(mla_unit, &c, (long)B * Hq, kv_cap, threads);
 }
+
+/* ------------------------- causal prefill backward, selected rows / keys --- */
+/* The same gradients as oracle_prefill_causal_backward, evaluated for chosen
+ * query rows (dQ) and chosen keys (dK, dV) with the work spread over rows,
+ * so one (b, K/V head) group of a long sequence takes seconds, not minutes.
+ * It follows the definition in three passes:
+ *   1. every row i: the forward weights P_i (the same attend_row as the
+ *      prefill, with the causal mask row), its LSE_i, and
+ *      Dsum_i = Σ_j P_ij · dP_ij with dP_ij = dO_i · V_j;
+ *   2. each chosen row: dS_ij = P_ij (dP_ij − Dsum_i), dQ_i = scale Σ_j dS_ij K_j;
+ *   3. each chosen key j, for every row i the mask leaves it visible to
+ *      (i >= j), in every query head of its group: P_ij = exp(s_ij − LSE_i)
+ *      (the softmax written through the log-sum-exp, [p1] §3), dS_ij as above,
+ *      dV_j = Σ P_ij dO_i, dK_j = scale Σ dS_ij Q_i.
+ * Per-row quantities are fixed before pass 2 and 3 read them, and every sum
+ * runs in ascending index order inside one unit, so the thread count does not
+ * change the result. */
+typedef struct {
+    const double *q, *k, *v, *dout;
+    int B, Hq, Hkv, N, D;
+    double scale;
+    const int *rows, *keys;
+    int n_rows, n_keys;
+    double *lse, *dsum; /* [B][Hq][N] */
+    double *dq;         /* [B][Hq][n_rows][D] */
+    double *dk, *dv;    /* [B][Hkv][n_keys][D] */
+} bwd_rows_ctx;
+
+static double dot_d(const double *a, const double *b, int D)
+{
+    double acc = 0.0;
+    for (int t = 0; t < D; ++t)
+        acc += a[t] * b[t];
+    return acc;
+}
+
+/* scratch: s[N], p[N], o[D], mask[N] bytes */
+static void bwd_rows_stats(bwd_rows_ctx *c, int b, int hq, int i, double *scratch, double *lse_out,
+                           double *dsum_out, double *p)
+{
+    const int N = c->N, D = c->D, hkv = hq / (c->Hq / c->Hkv);
+    double *s = scratch, *o = scratch + 2L * N;
+    unsigned char *mask = (unsigned char *)(o + D);
+    const double *Q = c->q + ((long)b * c->Hq + hq) * (long)N * D;
+    const double *dO = c->dout + ((long)b * c->Hq + hq) * (long)N * D;
+    const double *K = c->k + ((long)b * c->Hkv + hkv) * (long)N * D;
+    const double *V = c->v + ((long)b * c->Hkv + hkv) * (long)N * D;
+    for (int j = 0; j < N; ++j)
+        mask[j] = (unsigned char)(j > i);
+    attend_row(Q + (long)i * D, K, D, D, V, D, D, N, mask, c->scale, s, o, lse_out, p);
+    double acc = 0.0;
+    for (int j = 0; j < N; ++j)
+        if (!mask[j])
+            acc += p[j] * dot_d(dO + (long)i * D, V + (long)j * D, D);
+    *dsum_out = acc;
+}
+
+static void bwd_rows_pass1(void *vctx, long unit, double *scratch)
+{
+    bwd_rows_ctx *c = (bwd_rows_ctx *)vctx;
+    const int i = (int)(unit % c->N), bh = (int)(unit / c->N);
+    bwd_rows_stats(c, bh / c->Hq, bh % c->Hq, i, scratch, c->lse + unit, c->dsum + unit,
+                   scratch + c->N);
+}
+
+static void bwd_rows_pass2(void *vctx, long unit, double *scratch)
+{
+    bwd_rows_ctx *c = (bwd_rows_ctx *)vctx;
+    const int N = c->N, D = c->D;
+    const int r = (int)(unit % c->n_rows), bh = (int)(unit / c->n_rows);
+    const int b = bh / c->Hq, hq = bh % c->Hq, hkv = hq / (c->Hq / c->Hkv), i = c->rows[r];
+    double *p = scratch + N, lse_i, dsum_i;
+    bwd_rows_stats(c, b, hq, i, scratch, &lse_i, &dsum_i, p);
+    const double *dO = c->dout + ((long)b * c->Hq + hq) * (long)N * D;
+    const double *K = c->k + ((long)b * c->Hkv + hkv) * (long)N * D;
+    const double *V = c->v + ((long)b * c->Hkv + hkv) * (long)N * D;
+    const double Di = c->dsum[(long)bh * N + i];
+    double *dq = c->dq + ((long)bh * c->n_rows + r) * D;
+    for (int t = 0; t < D; ++t)
+        dq[t] = 0.0;
+    for (int j = 0; j <= i; ++j) {
+        const double ds = p[j] * (dot_d(dO + (long)i * D, V + (long)j * D, D) - Di);
+        for (int t = 0; t < D; ++t)
+            dq[t] += ds * K[(long)j * D + t];
+    }
+    for (int t = 0; t < D; ++t)
+        dq[t] *= c->scale;
+}
+
+static void bwd_rows_pass3(void *vctx, long unit, double *scratch)
+{
+    (void)scratch;
+    bwd_rows_ctx *c = (bwd_rows_ctx *)vctx;
+    const int N = c->N, D = c->D, G = c->Hq / c->Hkv;
+    const int u = (int)(unit % c->n_keys), bk = (int)(unit / c->n_keys);
+    const int b = bk / c->Hkv, hkv = bk % c->Hkv, j = c->keys[u];
+    const double *K = c->k + ((long)b * c->Hkv + hkv) * (long)N * D + (long)j * D;
+    const double *V = c->v + ((long)b * c->Hkv + hkv) * (long)N * D + (long)j * D;
+    double *dk = c->dk + ((long)bk * c->n_keys + u) * D;
+    double *dv = c->dv + ((long)bk * c->n_keys + u) * D;
+    for (int t = 0; t < D; ++t)
+        dk[t] = dv[t] = 0.0;
+    for (int g = 0; g < G; ++g) {
+        const long bh = (long)b * c->Hq + hkv * G + g;
+        const double *Q = c->q + bh * N * D, *dO = c->dout + bh * N * D;
+        for (int i = 0; i < N; ++i) {
+            if (j > i) /* the causal mask: key j is in row i's future */
+                continue;
+            const double s = c->scale * dot_d(Q + (long)i * D, K, D);
+            const double p = exp(s - c->lse[bh * N + i]);
+            const double ds = p * (dot_d(dO + (long)i * D, V, D) - c->dsum[bh * N + i]);
+            for (int t = 0; t < D; ++t) {
+                dv[t] += p * dO[(long)i * D + t];
+                dk[t] += c->scale * ds * Q[(long)i * D + t];
+            }
+        }
+    }
+}
+
+/* q, dout: [B][Hq][N][D]; k, v: [B][Hkv][N][D]; rows: n_rows query indices,
+ * keys: n_keys key indices, each in [0, N).
+ * dq: [B][Hq][n_rows][D]; dk, dv: [B][Hkv][n_keys][D]. */
+int oracle_prefill_causal_backward_rows(const double *q, const double *k, const double *v,
+                                        const double *dout, int B, int Hq, int Hkv, int N, int D,
+                                        double scale, const int *rows, int n_rows, const int *keys,
+                                        int n_keys, double *dq, double *dk, double *dv,
+                                        int threads)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1 || Hq % Hkv || n_rows < 0 || n_keys < 0)
+        return -1;
+    for (int r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= N)
+            return -1;
+    for (int u = 0; u < n_keys; ++u)
+        if (keys[u] < 0 || keys[u] >= N)
+            return -1;
+    double *stats = (double *)malloc(sizeof(double) * 2 * (size_t)B * Hq * N);
+    if (!stats)
+        return -1;
+    bwd_rows_ctx c = {q, k, v, dout, B, Hq, Hkv, N, D, scale, rows, keys, n_rows, n_keys,
+                      stats, stats + (size_t)B * Hq * N, dq, dk, dv};
+    /* scratch: s[N], p[N], o[D], and N mask bytes */
+    const int scratch = 2 * N + D + (N + 7) / 8 + 1;
+    int rc = run_units(bwd_rows_pass1, &c, (long)B * Hq * N, scratch, threads);
+    if (rc == 0 && n_rows > 0)
+        rc = run_units(bwd_rows_pass2, &c, (long)B * Hq * n_rows, scratch, threads);
+    if (rc == 0 && n_keys > 0)
+        rc = run_units(bwd_rows_pass3, &c, (long)B * Hkv * n_keys, 1, threads);
+    free(stats);
+    return rc;
+}

@@ -63,3 +63,18 @@ def check_f32(o, o_ref, lse, lse_ref, what=""):
     assert err.mean() <= 1e-5, "%s: mean abs error %g" % (what, err.mean())
     assert lrel.max() <= 1e-4, "%s: LSE rel error %g" % (what, lrel.max())
     return dict(max_abs=float(err.max()), mean_abs=float(err.mean()), lse_rel=float(lrel.max()))
+
+
+def check_bf16_channels(o, o_ref, lse, lse_ref, values, what=""):
+    """The comparison rule applied channel by channel in units of that
+    channel's values: O and O_ref are divided by g_c = 2^⌊log2 max_j |v_jc|⌋
+    (a power of two, exact in float64), then check_bf16 applies. Each output
+    channel is a convex combination of the values of that channel, so its
+    error scales with their magnitude; this keeps the gate meaningful when
+    channels span many decades (an un-balanced latent cache). `values`: the
+    stored value rows, any leading shape, channels last."""
+    v = np.abs(np.asarray(values, dtype=np.float64))
+    vmax = v.reshape(-1, v.shape[-1]).max(axis=0)
+    g = 2.0 ** np.floor(np.log2(np.maximum(vmax, 2.0 ** -126)))
+    return check_bf16(np.asarray(o, np.float64) / g, np.asarray(o_ref, np.float64) / g,
+                      lse, lse_ref, what)

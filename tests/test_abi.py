@@ -227,3 +227,47 @@ def test_last_error_is_thread_local(lib):
     t.join()
     assert seen == [""]
     assert "NULL" in attn.last_error()
+
+
+# ----------------------------------------------- Python binding checks (CPU) ---
+def test_binding_requires_scale():
+    """Every entry point takes the score scale from the caller; the binding
+    infers none (no 1/√D, no MLA head width)."""
+    import inspect
+    for name in ("attn_prefill_causal", "attn_prefill_causal_backward", "attn_decode_gqa",
+                 "attn_decode_gqa_fp8", "attn_decode_gqa_ragged", "attn_decode_mla_absorbed",
+                 "attn_decode_mla_fp8", "attn_decode_mla_ragged", "attn_prefill_chunked"):
+        prm = inspect.signature(getattr(attn, name)).parameters["scale"]
+        assert prm.default is inspect.Parameter.empty, name
+    with pytest.raises(TypeError):
+        attn._scale(None)
+    assert attn._scale(0.125) == 0.125
+
+
+def test_binding_tensor_checks():
+    """The checks every caller-supplied tensor passes before a library call:
+    dtype, number of dimensions, exact shape (an out=, lse= or gradient of the
+    wrong shape would be written past its end), contiguity, device. CPU
+    tensors stand in for GPU ones here (the GPU requirement itself is
+    checked too)."""
+    import torch
+    t = torch.empty(2, 3, 4, dtype=torch.bfloat16)
+    cpu = torch.device("cpu")
+    attn._check_tensor(t, "x", torch.bfloat16, shape=(2, 3, 4), device=cpu, cuda=False)
+    with pytest.raises(TypeError, match="GPU"):
+        attn._check_tensor(t, "x", torch.bfloat16)
+    with pytest.raises(TypeError, match="float32"):
+        attn._check_tensor(t, "x", torch.float32, cuda=False)
+    with pytest.raises(ValueError, match="3-d"):
+        attn._check_tensor(t, "x", torch.bfloat16, ndim=4, cuda=False)
+    with pytest.raises(ValueError, match="shape"):
+        attn._check_tensor(t, "out", torch.bfloat16, shape=(2, 3, 5), cuda=False)
+    with pytest.raises(ValueError, match="contiguous"):
+        attn._check_tensor(t.transpose(0, 1), "x", torch.bfloat16, cuda=False)
+    with pytest.raises(ValueError, match="on"):
+        attn._check_tensor(t, "x", torch.bfloat16, device=torch.device("meta"), cuda=False)
+    with pytest.raises(TypeError):
+        attn._check_tensor(t.numpy, "x", torch.bfloat16, cuda=False)
+    # E4M3 tensors are passed on as their bytes
+    f8 = torch.zeros(4, dtype=torch.float8_e4m3fn)
+    assert attn._fp8_bytes(f8).dtype == torch.uint8

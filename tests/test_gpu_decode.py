@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from parity import check_bf16, dev_bf16, host
+from parity import check_bf16, check_bf16_channels, dev_bf16, host
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +118,44 @@ def test_decode_mla_32k_workload_sampled_batches(gpu):
     bs = [0, w.B - 1]
     o_ref, lse_ref = oracle.decode_mla_absorbed(w.q[bs], w.ckv[bs], w.kv_len, w.Dv, w.scale)
     check_bf16(host(o[bs]), o_ref, host(lse[bs]), lse_ref, "decode_mla_absorbed_32k")
+
+
+def test_decode_mla_raw_latent_32k_sampled_batches(gpu):
+    """The MLA workload's shape (B=16, 128 heads, 32768 latent rows of 576)
+    with the absorbed query and latent stored raw, without the channel scale:
+    query channels of magnitude 1e-4..1e2, latent channels the reciprocals
+    (up to ~4e4). fp32 accumulation is what keeps the scores right here
+    ("MLA 矩阵乘法吸收的数值稳定性治理", §二.2, §五). Two batches against the
+    oracle, channel by channel in units of each channel's values."""
+    w = workloads.make("decode_mla_absorbed_32k", balance=False)
+    o, lse = _mla(gpu, w)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    bs = [0, w.B - 1]
+    o_ref, lse_ref = oracle.decode_mla_absorbed(w.q[bs], w.ckv[bs], w.kv_len, w.Dv, w.scale)
+    vals = oracle.widen(w.ckv[bs][:, :w.kv_len, :w.Dv])
+    check_bf16_channels(host(o[bs]), o_ref, host(lse[bs]), lse_ref, vals, "mla raw latent 32k")
+
+
+@pytest.mark.parametrize("B,Hq,kv_len", [(1, 128, 4096), (2, 64, 700), (3, 32, 1)])
+def test_decode_mla_values_beyond_fp16_range(gpu, B, Hq, kv_len):
+    """Latent channels of magnitude 1e5..1e6 (raw storage, query channels
+    1e-6..1e-5): the values exceed fp16's largest finite 65504, which bf16
+    holds. Split partials, the merge and the single-split path all keep
+    them (a 16-bit float partial would give Inf), and the output is rounded
+    once. Uniform and ragged calls."""
+    w = workloads.gen_decode_mla(B, Hq, kv_len, kv_cap=kv_len + 3, seed=kv_len + Hq,
+                                 balance=False, mag_lo=1e-6, mag_hi=1e-5)
+    vals = oracle.widen(w.ckv[:, :kv_len, :w.Dv])
+    assert np.abs(vals).max() > 65504
+    o_ref, lse_ref = oracle.decode_mla_absorbed(w.q, w.ckv, kv_len, w.Dv, w.scale)
+    q, c = dev_bf16(w.q), dev_bf16(w.ckv)
+    o, lse = gpu.attn_decode_mla_absorbed(q, c, kv_len, w.Dv, w.scale)
+    lens = torch.full((B,), kv_len, dtype=torch.int32, device="cuda")
+    o2, lse2 = gpu.attn_decode_mla_ragged(q, c, lens, kv_len, w.Dv, w.scale)
+    torch.cuda.synchronize()
+    assert np.abs(host(o)).max() > 65504
+    check_bf16_channels(host(o), o_ref, host(lse), lse_ref, vals, "mla |v| > 65504 %s" % ((B, Hq, kv_len),))
+    check_bf16_channels(host(o2), o_ref, host(lse2), lse_ref, vals, "ragged mla |v| > 65504")
 
 
 @pytest.mark.parametrize("kv_len", [512, 513])

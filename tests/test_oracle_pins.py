@@ -566,3 +566,41 @@ def test_backward_closed_forms():
     for hkv in range(Hkv):
         want = sum(p[0, h, N - 1, N - 1] * dout[0, h, N - 1] for h in (2 * hkv, 2 * hkv + 1))
         np.testing.assert_allclose(dv[0, hkv, N - 1], want, rtol=1e-14, atol=1e-15)
+
+
+def test_backward_rows_equals_backward():
+    """The row- and key-parallel backward (used for long sequences) gives the
+    gradients of the serial one, which the three pins above fix: all rows and
+    keys, and chosen subsets in any order, across GQA groups and ragged N."""
+    for (B, Hq, Hkv, N, D, seed) in ((1, 4, 2, 9, 6, 1), (2, 6, 3, 40, 16, 2), (1, 2, 1, 1, 8, 3)):
+        w = workloads.gen_prefill(B, Hq, Hkv, N, D, dtype="bf16", seed=seed)
+        dout = workloads.gen_upstream_grad((B, Hq, N, D), seed=seed + 10)
+        dq, dk, dv = oracle.prefill_causal_backward(w.q, w.k, w.v, dout, w.scale)
+        rq, rk, rv = oracle.prefill_causal_backward_rows(w.q, w.k, w.v, dout, w.scale, threads=3)
+        for a, b in ((rq, dq), (rk, dk), (rv, dv)):
+            np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+        rows, keys = [N - 1, 0, N // 2], [N // 3, N - 1]
+        sq, sk, sv = oracle.prefill_causal_backward_rows(w.q, w.k, w.v, dout, w.scale, rows=rows,
+                                                         keys=keys)
+        np.testing.assert_array_equal(sq, rq[:, :, rows])
+        np.testing.assert_array_equal(sk, rk[:, :, keys])
+        np.testing.assert_array_equal(sv, rv[:, :, keys])
+
+
+def test_bf16_widening_every_bit_pattern():
+    """oracle.widen reads bfloat16 storage: every one of the 65,536 bit
+    patterns widens to the value torch's bfloat16 → float64 conversion
+    gives (the upper half of an IEEE binary32 word: sign, 8 exponent bits,
+    7 mantissa bits), NaN patterns to NaN, ±0 and ±inf kept."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.widen(bits)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    # spot values fixed by the format itself
+    assert got[0x3F80] == 1.0 and got[0xBF80] == -1.0 and got[0x4049] == 3.140625
+    assert got[0x0001] == 2.0 ** -133 and got[0x7F7F] == (2 - 2 ** -7) * 2.0 ** 127
+    assert np.isinf(got[0x7F80]) and got[0xFF80] < 0 and np.isnan(got[0x7FC0])

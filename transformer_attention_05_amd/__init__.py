@@ -12,14 +12,17 @@ no fallback: if libattn.so is missing or fails to load, every call raises.
     o, lse = attn_decode_gqa_ragged(q, k_cache, v_cache, kv_lens, max_kv_len, scale)
     o, lse = attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, 512, scale)
     o, lse = attn_decode_gqa_fp8(q, k_fp8, v_fp8, kv_len, scale)   # E4M3 caches (uint8)
-    o, lse = attn_decode_mla_fp8(q, ckv_fp8, kv_len)                 # E4M3 latent cache
+    o, lse = attn_decode_mla_fp8(q, ckv_fp8, kv_len, 512, scale)   # E4M3 latent cache
     dq, dk, dv = attn_prefill_causal_backward(q, k, v, o, lse, dout, scale)
 (kv_lens: an int32 GPU tensor of per-sequence lengths, read by the kernels.)
+The score scale is always an argument: the binding never infers 1/√D.
+Every caller-supplied tensor (inputs, out=, lse=, gradients, workspace,
+kv_lens) is checked for dtype, shape, contiguity and device against q before
+the library is called.
 """
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 import threading
 
@@ -103,13 +106,47 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, name, dtype, ndim):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+def _check_tensor(t, name, dtype, shape=None, ndim=None, device=None, cuda=True):
+    """Raise unless t is a contiguous tensor of `dtype` with the given shape
+    (or number of dimensions), on `device` (when given) and on a GPU (when
+    `cuda`). A tensor the kernels would read or write past its end, or one on
+    another device than the stream's, never reaches the library."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if cuda and not t.is_cuda:
         raise TypeError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, the call runs on %s" % (name, t.device, device))
     if t.dtype != dtype:
         raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
-    if t.dim() != ndim or not t.is_contiguous():
-        raise ValueError("%s must be a contiguous %d-d tensor" % (name, ndim))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must be a %d-d tensor (got %d-d)" % (name, ndim, t.dim()))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _fp8_bytes(t):
+    """E4M3 codes as uint8: torch.float8_e4m3fn tensors are viewed as bytes."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    return t
+
+
+def _scale(scale) -> float:
+    """The score scale is always the caller's: nothing here infers 1/√D."""
+    if scale is None:
+        raise TypeError("scale is required (the caller passes it; it is never inferred)")
+    return float(scale)
+
+
+def _out(t, name, dtype, shape, device):
+    """The caller's output tensor, checked, or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _check_tensor(t, name, dtype, shape=shape, device=device)
+    return t
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
@@ -129,57 +166,60 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return ws
 
 
-def attn_prefill_causal(q, k, v, scale=None, out=None, lse=None):
+def _ws(lib_bytes, ws, device, name="ws"):
+    if ws is None:
+        return workspace(lib_bytes, device)
+    _check_tensor(ws, name, torch.uint8, ndim=1, device=device)
+    return ws
+
+
+def attn_prefill_causal(q, k, v, scale, out=None, lse=None):
     """Causal prefill. q [B,Hq,N,D], k/v [B,Hkv,N,D] (bf16 or fp32, same
     dtype). Returns (o [B,Hq,N,D] same dtype, lse [B,Hq,N] fp32)."""
     lib = load()
-    dtype = q.dtype
+    dtype = q.dtype if isinstance(q, torch.Tensor) else None
     if dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("q must be bfloat16 or float32")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, name, dtype, 4)
+        raise TypeError("q must be a bfloat16 or float32 tensor")
+    _check_tensor(q, "q", dtype, ndim=4)
+    dev = q.device
     B, Hq, N, D = q.shape
+    _check_tensor(k, "k", dtype, ndim=4, device=dev)
     Hkv = k.shape[1]
-    if k.shape != (B, Hkv, N, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [B, Hkv, N, D] matching q")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, "out", dtype, 4)
-    _need(l, "lse", torch.float32, 3)
+    _check_tensor(k, "k", dtype, shape=(B, Hkv, N, D), device=dev)
+    _check_tensor(v, "v", dtype, shape=(B, Hkv, N, D), device=dev)
+    sc = _scale(scale)
+    o = _out(out, "out", dtype, (B, Hq, N, D), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq, N), dev)
     st = lib.attn_prefill_causal(ATTN_BF16 if dtype == torch.bfloat16 else ATTN_FP32,
                                  _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
-                                 B, Hq, Hkv, N, D, float(scale), _stream(q.device))
+                                 B, Hq, Hkv, N, D, sc, _stream(dev))
     _check(st, lib)
     return o, l
 
 
-def attn_prefill_causal_backward(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None,
+def attn_prefill_causal_backward(q, k, v, o, lse, dout, scale, dq=None, dk=None, dv=None,
                                  ws=None):
     """Backward of attn_prefill_causal (bf16, D = 128). q, o, dout [B,Hq,N,D];
     k, v [B,Hkv,N,D]; lse [B,Hq,N] fp32 from the forward. Returns (dq, dk, dv)."""
     lib = load()
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        _need(t, name, torch.bfloat16, 4)
+    _check_tensor(q, "q", torch.bfloat16, ndim=4)
+    dev = q.device
     B, Hq, N, D = q.shape
+    _check_tensor(k, "k", torch.bfloat16, ndim=4, device=dev)
     Hkv = k.shape[1]
-    if k.shape != (B, Hkv, N, D) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("shapes must be q/o/dout [B,Hq,N,D], k/v [B,Hkv,N,D]")
-    _need(lse, "lse", torch.float32, 3)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _need(t, name, torch.bfloat16, 4)
-    need = lib.attn_prefill_causal_backward_workspace_bytes(B, Hq, N, D)
-    w = workspace(need, q.device) if ws is None else ws
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(t, name, torch.bfloat16, shape=(B, Hkv, N, D), device=dev)
+    for name, t in (("o", o), ("dout", dout)):
+        _check_tensor(t, name, torch.bfloat16, shape=(B, Hq, N, D), device=dev)
+    _check_tensor(lse, "lse", torch.float32, shape=(B, Hq, N), device=dev)
+    sc = _scale(scale)
+    dq = _out(dq, "dq", torch.bfloat16, (B, Hq, N, D), dev)
+    dk = _out(dk, "dk", torch.bfloat16, (B, Hkv, N, D), dev)
+    dv = _out(dv, "dv", torch.bfloat16, (B, Hkv, N, D), dev)
+    w = _ws(lib.attn_prefill_causal_backward_workspace_bytes(B, Hq, N, D), ws, dev)
     st = lib.attn_prefill_causal_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                                          _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, D,
-                                          float(scale), _ptr(w), w.numel() * w.element_size(),
-                                          _stream(q.device))
+                                          _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, D, sc,
+                                          _ptr(w), w.numel(), _stream(dev))
     _check(st, lib)
     return dq, dk, dv
 
@@ -192,57 +232,48 @@ def attn_prefill_causal_backward_workspace_bytes(B, Hq, N, D=128) -> int:
     return int(load().attn_prefill_causal_backward_workspace_bytes(B, Hq, N, D))
 
 
-def attn_decode_gqa(q, k_cache, v_cache, kv_len, scale=None, out=None, lse=None, ws=None):
+def _gqa_args(q, k_cache, v_cache, cache_dtype):
+    """Shapes of a GQA decode call, every input checked against q."""
+    _check_tensor(q, "q", torch.bfloat16, ndim=3)
+    dev = q.device
+    B, Hq, D = q.shape
+    _check_tensor(k_cache, "k_cache", cache_dtype, ndim=4, device=dev)
+    _, Hkv, kv_cap, _ = k_cache.shape
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(t, name, cache_dtype, shape=(B, Hkv, kv_cap, D), device=dev)
+    return dev, B, Hq, Hkv, kv_cap, D
+
+
+def attn_decode_gqa(q, k_cache, v_cache, kv_len, scale, out=None, lse=None, ws=None):
     """Single-query GQA decode. q [B,Hq,D] bf16; caches [B,Hkv,kv_cap,D] bf16
     filled to kv_len. Returns (o [B,Hq,D] bf16, lse [B,Hq] fp32)."""
     lib = load()
-    _need(q, "q", torch.bfloat16, 3)
-    _need(k_cache, "k_cache", torch.bfloat16, 4)
-    _need(v_cache, "v_cache", torch.bfloat16, 4)
-    B, Hq, D = q.shape
-    _, Hkv, kv_cap, _ = k_cache.shape
-    if k_cache.shape != (B, Hkv, kv_cap, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("caches must be [B, Hkv, kv_cap, D] matching q")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, "out", torch.bfloat16, 3)
-    _need(l, "lse", torch.float32, 2)
-    need = lib.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, int(kv_len), D)
-    w = workspace(need, q.device) if ws is None else ws
+    dev, B, Hq, Hkv, kv_cap, D = _gqa_args(q, k_cache, v_cache, torch.bfloat16)
+    sc = _scale(scale)
+    o = _out(out, "out", torch.bfloat16, (B, Hq, D), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq), dev)
+    w = _ws(lib.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, int(kv_len), D), ws, dev)
     st = lib.attn_decode_gqa(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
-                             B, Hq, Hkv, int(kv_len), kv_cap, D, float(scale),
-                             _ptr(w), w.numel() * w.element_size(), _stream(q.device))
+                             B, Hq, Hkv, int(kv_len), kv_cap, D, sc,
+                             _ptr(w), w.numel(), _stream(dev))
     _check(st, lib)
     return o, l
 
 
-def attn_decode_gqa_fp8(q, k_cache, v_cache, kv_len, scale=None, out=None, lse=None, ws=None):
+def attn_decode_gqa_fp8(q, k_cache, v_cache, kv_len, scale, out=None, lse=None, ws=None):
     """GQA decode over an FP8 E4M3 cache. q [B,Hq,D] bf16; caches
     [B,Hkv,kv_cap,D] torch.uint8 (E4M3 codes) or torch.float8_e4m3fn, filled
     to kv_len. Returns (o [B,Hq,D] bf16, lse [B,Hq] fp32)."""
     lib = load()
-    _need(q, "q", torch.bfloat16, 3)
-    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        if t.dtype == torch.float8_e4m3fn:
-            t = t.view(torch.uint8)
-        _need(t, name, torch.uint8, 4)
-    B, Hq, D = q.shape
-    _, Hkv, kv_cap, _ = k_cache.shape
-    if k_cache.shape != (B, Hkv, kv_cap, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("caches must be [B, Hkv, kv_cap, D] matching q")
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, "out", torch.bfloat16, 3)
-    _need(l, "lse", torch.float32, 2)
-    need = lib.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, int(kv_len), D)
-    w = workspace(need, q.device) if ws is None else ws
+    k_cache, v_cache = _fp8_bytes(k_cache), _fp8_bytes(v_cache)
+    dev, B, Hq, Hkv, kv_cap, D = _gqa_args(q, k_cache, v_cache, torch.uint8)
+    sc = _scale(scale)
+    o = _out(out, "out", torch.bfloat16, (B, Hq, D), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq), dev)
+    w = _ws(lib.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, int(kv_len), D), ws, dev)
     st = lib.attn_decode_gqa_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
-                                 B, Hq, Hkv, int(kv_len), kv_cap, D, float(scale),
-                                 _ptr(w), w.numel() * w.element_size(), _stream(q.device))
+                                 B, Hq, Hkv, int(kv_len), kv_cap, D, sc,
+                                 _ptr(w), w.numel(), _stream(dev))
     _check(st, lib)
     return o, l
 
@@ -255,153 +286,118 @@ def attn_decode_mla_ragged_workspace_bytes(B, Hq, max_kv_len, Dqk=576, Dv=512) -
     return int(load().attn_decode_mla_ragged_workspace_bytes(B, Hq, max_kv_len, Dqk, Dv))
 
 
-def attn_decode_mla_absorbed(q, ckv, kv_len, dv=512, scale=None, out=None, lse=None, ws=None):
+def _mla_args(q, ckv, cache_dtype):
+    _check_tensor(q, "q", torch.bfloat16, ndim=3)
+    dev = q.device
+    B, Hq, Dqk = q.shape
+    _check_tensor(ckv, "ckv", cache_dtype, ndim=3, device=dev)
+    kv_cap = ckv.shape[1]
+    _check_tensor(ckv, "ckv", cache_dtype, shape=(B, kv_cap, Dqk), device=dev)
+    return dev, B, Hq, Dqk, kv_cap
+
+
+def attn_decode_mla_absorbed(q, ckv, kv_len, dv, scale, out=None, lse=None, ws=None):
     """Absorbed MLA decode. q [B,Hq,Dqk] bf16 (absorbed, channel-balanced
     query | rope), ckv [B,kv_cap,Dqk] bf16 (balanced latent | rope). Value =
     first dv channels of each cached row. Returns (o [B,Hq,dv] bf16, lse)."""
     lib = load()
-    _need(q, "q", torch.bfloat16, 3)
-    _need(ckv, "ckv", torch.bfloat16, 3)
-    B, Hq, Dqk = q.shape
-    kv_cap = ckv.shape[1]
-    if ckv.shape != (B, kv_cap, Dqk):
-        raise ValueError("ckv must be [B, kv_cap, Dqk] matching q")
-    if scale is None:
-        scale = 1.0 / math.sqrt(128 + 64)
-    o = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
-    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, "out", torch.bfloat16, 3)
-    _need(l, "lse", torch.float32, 2)
-    need = lib.attn_decode_mla_workspace_bytes(B, Hq, int(kv_len), Dqk, dv)
-    w = workspace(need, q.device) if ws is None else ws
+    dev, B, Hq, Dqk, kv_cap = _mla_args(q, ckv, torch.bfloat16)
+    dv, sc = int(dv), _scale(scale)
+    o = _out(out, "out", torch.bfloat16, (B, Hq, dv), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq), dev)
+    w = _ws(lib.attn_decode_mla_workspace_bytes(B, Hq, int(kv_len), Dqk, dv), ws, dev)
     st = lib.attn_decode_mla_absorbed(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), B, Hq, int(kv_len),
-                                      kv_cap, Dqk, dv, float(scale), _ptr(w),
-                                      w.numel() * w.element_size(), _stream(q.device))
+                                      kv_cap, Dqk, dv, sc, _ptr(w), w.numel(), _stream(dev))
     _check(st, lib)
     return o, l
 
 
-def attn_decode_mla_fp8(q, ckv, kv_len, dv=512, scale=None, out=None, lse=None, ws=None):
+def attn_decode_mla_fp8(q, ckv, kv_len, dv, scale, out=None, lse=None, ws=None):
     """Absorbed MLA decode over an FP8 E4M3 latent cache. q [B,Hq,Dqk] bf16
     (absorbed, channel-balanced query | rope); ckv [B,kv_cap,Dqk]
     torch.uint8 (E4M3 codes of the balanced latent | rope) or
     torch.float8_e4m3fn. Returns (o [B,Hq,dv] bf16, lse [B,Hq] fp32)."""
     lib = load()
-    _need(q, "q", torch.bfloat16, 3)
-    _need(ckv.view(torch.uint8) if ckv.dtype == torch.float8_e4m3fn else ckv, "ckv", torch.uint8, 3)
-    B, Hq, Dqk = q.shape
-    kv_cap = ckv.shape[1]
-    if ckv.shape != (B, kv_cap, Dqk):
-        raise ValueError("ckv must be [B, kv_cap, Dqk] matching q")
-    if scale is None:
-        scale = 1.0 / math.sqrt(128 + 64)
-    o = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
-    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, "out", torch.bfloat16, 3)
-    _need(l, "lse", torch.float32, 2)
-    need = lib.attn_decode_mla_workspace_bytes(B, Hq, int(kv_len), Dqk, dv)
-    w = workspace(need, q.device) if ws is None else ws
+    ckv = _fp8_bytes(ckv)
+    dev, B, Hq, Dqk, kv_cap = _mla_args(q, ckv, torch.uint8)
+    dv, sc = int(dv), _scale(scale)
+    o = _out(out, "out", torch.bfloat16, (B, Hq, dv), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq), dev)
+    w = _ws(lib.attn_decode_mla_workspace_bytes(B, Hq, int(kv_len), Dqk, dv), ws, dev)
     st = lib.attn_decode_mla_fp8(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), B, Hq, int(kv_len), kv_cap,
-                                 Dqk, dv, float(scale), _ptr(w), w.numel() * w.element_size(),
-                                 _stream(q.device))
+                                 Dqk, dv, sc, _ptr(w), w.numel(), _stream(dev))
     _check(st, lib)
     return o, l
 
 
-def _need_lens(kv_lens, B):
-    _need(kv_lens, "kv_lens", torch.int32, 1)
-    if kv_lens.shape[0] != B:
-        raise ValueError("kv_lens must hold one length per sequence")
+def _need_lens(kv_lens, B, device):
+    _check_tensor(kv_lens, "kv_lens", torch.int32, shape=(B,), device=device)
 
 
 def attn_prefill_chunked_workspace_bytes(B, Hq, Nq, kv_cap, D=128) -> int:
     return int(load().attn_prefill_chunked_workspace_bytes(B, Hq, Nq, kv_cap, D))
 
 
-def attn_prefill_chunked(q, k_cache, v_cache, kv_lens, scale=None, out=None, lse=None, ws=None):
+def attn_prefill_chunked(q, k_cache, v_cache, kv_lens, scale, out=None, lse=None, ws=None):
     """Chunked prefill against a cache. q [B,Hq,Nq,D] bf16; caches
     [B,Hkv,kv_cap,D] bf16 filled to kv_lens[b] (int32 GPU tensor [B], each
     in [Nq, kv_cap]), the last Nq slots being the chunk's own tokens.
     Returns (o [B,Hq,Nq,D] bf16, lse [B,Hq,Nq] fp32)."""
     lib = load()
-    _need(q, "q", torch.bfloat16, 4)
-    _need(k_cache, "k_cache", torch.bfloat16, 4)
-    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _check_tensor(q, "q", torch.bfloat16, ndim=4)
+    dev = q.device
     B, Hq, Nq, D = q.shape
+    _check_tensor(k_cache, "k_cache", torch.bfloat16, ndim=4, device=dev)
     _, Hkv, kv_cap, _ = k_cache.shape
-    if k_cache.shape != (B, Hkv, kv_cap, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("caches must be [B, Hkv, kv_cap, D] matching q")
-    _need_lens(kv_lens, B)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, "out", torch.bfloat16, 4)
-    _need(l, "lse", torch.float32, 3)
-    need = lib.attn_prefill_chunked_workspace_bytes(B, Hq, Nq, kv_cap, D)
-    w = workspace(need, q.device) if ws is None else ws
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_tensor(t, name, torch.bfloat16, shape=(B, Hkv, kv_cap, D), device=dev)
+    _need_lens(kv_lens, B, dev)
+    sc = _scale(scale)
+    o = _out(out, "out", torch.bfloat16, (B, Hq, Nq, D), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq, Nq), dev)
+    w = _ws(lib.attn_prefill_chunked_workspace_bytes(B, Hq, Nq, kv_cap, D), ws, dev)
     st = lib.attn_prefill_chunked(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
-                                  _ptr(kv_lens), B, Hq, Hkv, Nq, kv_cap, D, float(scale),
-                                  _ptr(w), w.numel() * w.element_size(), _stream(q.device))
+                                  _ptr(kv_lens), B, Hq, Hkv, Nq, kv_cap, D, sc,
+                                  _ptr(w), w.numel(), _stream(dev))
     _check(st, lib)
     return o, l
 
 
-def attn_decode_gqa_ragged(q, k_cache, v_cache, kv_lens, max_kv_len, scale=None, out=None,
+def attn_decode_gqa_ragged(q, k_cache, v_cache, kv_lens, max_kv_len, scale, out=None,
                            lse=None, ws=None):
     """GQA decode of a ragged batch: sequence b's caches are filled to
     kv_lens[b] (int32 GPU tensor [B], each at most max_kv_len). Returns
     (o [B,Hq,D] bf16, lse [B,Hq] fp32); a sequence of length 0 gets O = 0,
     LSE = -inf."""
     lib = load()
-    _need(q, "q", torch.bfloat16, 3)
-    _need(k_cache, "k_cache", torch.bfloat16, 4)
-    _need(v_cache, "v_cache", torch.bfloat16, 4)
-    B, Hq, D = q.shape
-    _, Hkv, kv_cap, _ = k_cache.shape
-    if k_cache.shape != (B, Hkv, kv_cap, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("caches must be [B, Hkv, kv_cap, D] matching q")
-    _need_lens(kv_lens, B)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, "out", torch.bfloat16, 3)
-    _need(l, "lse", torch.float32, 2)
-    need = lib.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, int(max_kv_len), D)
-    w = workspace(need, q.device) if ws is None else ws
+    dev, B, Hq, Hkv, kv_cap, D = _gqa_args(q, k_cache, v_cache, torch.bfloat16)
+    _need_lens(kv_lens, B, dev)
+    sc = _scale(scale)
+    o = _out(out, "out", torch.bfloat16, (B, Hq, D), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq), dev)
+    w = _ws(lib.attn_decode_gqa_workspace_bytes(B, Hq, Hkv, int(max_kv_len), D), ws, dev)
     st = lib.attn_decode_gqa_ragged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
-                                    _ptr(kv_lens), B, Hq, Hkv, int(max_kv_len), kv_cap, D,
-                                    float(scale), _ptr(w), w.numel() * w.element_size(),
-                                    _stream(q.device))
+                                    _ptr(kv_lens), B, Hq, Hkv, int(max_kv_len), kv_cap, D, sc,
+                                    _ptr(w), w.numel(), _stream(dev))
     _check(st, lib)
     return o, l
 
 
-def attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, dv=512, scale=None, out=None, lse=None,
+def attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, dv, scale, out=None, lse=None,
                            ws=None):
     """Absorbed MLA decode of a ragged batch: sequence b's latent cache is
     filled to kv_lens[b] (int32 GPU tensor [B], each at most max_kv_len).
     Returns (o [B,Hq,dv] bf16, lse [B,Hq] fp32)."""
     lib = load()
-    _need(q, "q", torch.bfloat16, 3)
-    _need(ckv, "ckv", torch.bfloat16, 3)
-    B, Hq, Dqk = q.shape
-    kv_cap = ckv.shape[1]
-    if ckv.shape != (B, kv_cap, Dqk):
-        raise ValueError("ckv must be [B, kv_cap, Dqk] matching q")
-    _need_lens(kv_lens, B)
-    if scale is None:
-        scale = 1.0 / math.sqrt(128 + 64)
-    o = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
-    l = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _need(o, "out", torch.bfloat16, 3)
-    _need(l, "lse", torch.float32, 2)
-    need = lib.attn_decode_mla_ragged_workspace_bytes(B, Hq, int(max_kv_len), Dqk, dv)
-    w = workspace(need, q.device) if ws is None else ws
+    dev, B, Hq, Dqk, kv_cap = _mla_args(q, ckv, torch.bfloat16)
+    _need_lens(kv_lens, B, dev)
+    dv, sc = int(dv), _scale(scale)
+    o = _out(out, "out", torch.bfloat16, (B, Hq, dv), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq), dev)
+    w = _ws(lib.attn_decode_mla_ragged_workspace_bytes(B, Hq, int(max_kv_len), Dqk, dv), ws, dev)
     st = lib.attn_decode_mla_ragged(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), _ptr(kv_lens), B, Hq,
-                                    int(max_kv_len), kv_cap, Dqk, dv, float(scale), _ptr(w),
-                                    w.numel() * w.element_size(), _stream(q.device))
+                                    int(max_kv_len), kv_cap, Dqk, dv, sc, _ptr(w),
+                                    w.numel(), _stream(dev))
     _check(st, lib)
     return o, l
 

@@ -533,28 +533,15 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     auto rec = [&](int h) __attribute__((always_inline)) {
         return SK ? (size_t)split * Hq + h : ((size_t)b * Hq + h) * splits + split;
     };
-    // the partial output is stored normalised, Õ/λ (bounded by the values),
-    // in fp16: 11 significant bits, half the bytes of fp32 Õ; every wave
-    // needs λ of every head, passed through LDS as in the one-split case
-    __syncthreads();  // every wave is done with the last tile's factors
-    if (own && quad == 0) {
-        hinfo[0][hcol][wave] = l_o;
-        *(float4 *)(ws_ml + 4 * rec(head)) = make_float4(m_ref, l_e, l_o, 0.f);
-    }
-    __syncthreads();
-    uint16_t *part = (uint16_t *)ws_part;
+    // the partial output Õ is stored in fp32, as accumulated: the merge
+    // rounds the output once, and any value bf16 can hold fits
+    if (own && quad == 0) *(float4 *)(ws_ml + 4 * rec(head)) = make_float4(m_ref, l_e, l_o, 0.f);
 #pragma unroll
     for (int hb = 0; hb < MHB; ++hb) {
         if (hb >= nhb) break;
-        const float lam = hinfo[0][hcol][hb];
-        const float inv = lam > 0.f ? 1.f / lam : 0.f;  // no key here: Õ = 0
-        uint16_t *prow = part + rec(hg * MH + 16 * hb + hcol) * MV + MDW * wave + 4 * quad;
+        float *prow = ws_part + rec(hg * MH + 16 * hb + hcol) * MV + MDW * wave + 4 * quad;
 #pragma unroll
-        for (int db = 0; db < MDBW; ++db) {
-            const u32x2 w = {pack_f16x2(oacc[db][hb][0] * inv, oacc[db][hb][1] * inv),
-                             pack_f16x2(oacc[db][hb][2] * inv, oacc[db][hb][3] * inv)};
-            __builtin_nontemporal_store(w, (u32x2 *)(prow + 16 * db));
-        }
+        for (int db = 0; db < MDBW; ++db) __builtin_nontemporal_store(oacc[db][hb], (f32x4 *)(prow + 16 * db));
     }
 }
 
@@ -576,7 +563,7 @@ bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p)
     const size_t rows = (size_t)B * Hq;
     p->ws_ml = 0;
     p->ws_part = align_up(sizeof(float) * 4 * rows * s, 256);
-    p->ws_total = s == 1 ? 256 : p->ws_part + align_up(sizeof(uint16_t) * MV * rows * s, 256);
+    p->ws_total = s == 1 ? 256 : p->ws_part + align_up(sizeof(float) * MV * rows * s, 256);
     return true;
 }
 
@@ -596,7 +583,7 @@ bool mla_ragged_plan(int B, int Hq, int max_len, MlaPlan *p)
     const size_t recs = (size_t)(P + B) * Hq;        // slots w + b, all heads
     p->ws_ml = 0;
     p->ws_part = align_up(sizeof(float) * 4 * recs, 256);
-    p->ws_total = p->ws_part + align_up(sizeof(uint16_t) * MV * recs, 256);
+    p->ws_total = p->ws_part + align_up(sizeof(float) * MV * recs, 256);
     return true;
 }
 
@@ -625,7 +612,7 @@ static hipError_t launch_decode_mla_t(const MlaPlan &p, const void *q, const voi
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         return launch_merge_ragged(ws_ml, ws_part, o, lse, kv_lens, B, Hq, kv_len, p.splits, MBC,
-                                   MV, st, true);
+                                   MV, st);
         }
     }
     const dim3 grid(p.splits, hgs, B);
@@ -637,7 +624,7 @@ static hipError_t launch_decode_mla_t(const MlaPlan &p, const void *q, const voi
         scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part, nullptr, B);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, MV, st, 0, true);
+    return launch_merge(ws_ml, ws_part, o, lse, B * Hq, p.splits, MV, st);
 }
 
 hipError_t launch_decode_mla(const MlaPlan &p, const void *q, const void *ckv, void *o,

@@ -167,8 +167,8 @@ class DecodeMLA:
     FP8 E4M3 codes.
 
     Each row is [latent (Dv) | rope (Dqk-Dv)]. The latent part is stored
-    channel-balanced: q holds q̃·S⁻¹ and ckv holds S·c, S = diag(s).
-    V is the latent part of ckv (its first Dv channels).
+    channel-balanced (q holds q̃·S⁻¹ and ckv holds S·c, S = diag(s)) or raw
+    (s = 1). V is the latent part of ckv (its first Dv channels).
     """
     B: int
     Hq: int
@@ -179,9 +179,10 @@ class DecodeMLA:
     scale: float
     q: np.ndarray
     ckv: np.ndarray
-    s: np.ndarray = field(default=None)   # channel scale, [Dv] float64
+    s: np.ndarray = field(default=None)   # channel scale S applied before storage, [Dv] float64
     kv_lens: np.ndarray | None = None     # [B] int32 per-sequence lengths (ragged batch)
     cache_dtype: str = "bf16"             # "bf16" (uint16 bits) or "fp8" (E4M3 uint8 codes)
+    mags: np.ndarray = field(default=None)  # true channel magnitudes of the raw q̃, [Dv]
 
 
 def ragged_lengths(B, lo, hi, seed) -> np.ndarray:
@@ -305,17 +306,25 @@ def gen_prefill_chunked(B, Hq, Hkv, Nq, kv_lens, D=128, kv_cap=None, seed=0, sca
 
 def gen_decode_mla(B, Hq, kv_len=None, Dqk=576, Dv=512, kv_cap=None, seed=0,
                    scale=None, mag_lo=1e-4, mag_hi=1e2, poison_tail=True,
-                   kv_lens=None, cache_dtype="bf16") -> DecodeMLA:
-    """Absorbed-MLA decode inputs, channel-balanced before storage.
+                   kv_lens=None, cache_dtype="bf16", balance=True, calib_rows=128) -> DecodeMLA:
+    """Absorbed-MLA decode inputs.
 
-    s_k = 10^U(log10 mag_lo, log10 mag_hi) per latent channel. The model-side
-    absorbed query is q̃ = q_u ⊙ s and the latent is c = c_u ⊘ s (so logits
-    stay O(1)); what is stored is bf16(q̃ ⊙ s⁻¹) and bf16(s ⊙ c). The rope
-    channels (Dqk - Dv of them) are N(0,1) and not scaled. Default scale is
-    1/√192 (128 no-rope + 64 rope dims of the pre-absorption head).
-    With kv_lens (a ragged batch) sequence b is filled to kv_lens[b] and
-    kv_len is the longest. cache_dtype "fp8" stores the cache as OCP E4M3
-    codes of the same balanced rows S·c (round to nearest even; the
+    Channel magnitudes: m_k = 10^U(log10 mag_lo, log10 mag_hi) per latent
+    channel. The model-side absorbed query is q̃ = q_u ⊙ m and the latent is
+    c = c_u ⊘ m (so logits stay O(1)), q_u, c_u ~ N(0,1). The rope channels
+    (Dqk - Dv of them) are N(0,1) and not scaled.
+
+    balance=True: a static channel scale S = diag(s) is applied before
+    storage, q̃ ⊙ s⁻¹ and s ⊙ c. S is estimated offline, as the root mean
+    square of each channel over `calib_rows` seeded calibration draws of that
+    channel (magnitude m_k), so it tracks the true magnitudes only up to
+    sampling error and some imbalance stays in storage. balance=False stores
+    the raw q̃ and c (channels from mag_lo to mag_hi and their reciprocals).
+
+    The default scale is 1/√192 (128 no-rope + 64 rope dims of the
+    pre-absorption head). With kv_lens (a ragged batch) sequence b is filled
+    to kv_lens[b] and kv_len is the longest. cache_dtype "fp8" stores the
+    cache as OCP E4M3 codes of the same rows (round to nearest even; the
     balanced values lie far inside E4M3's range), the query staying bf16.
     """
     if cache_dtype not in ("bf16", "fp8"):
@@ -331,9 +340,14 @@ def gen_decode_mla(B, Hq, kv_len=None, Dqk=576, Dv=512, kv_cap=None, seed=0,
     rq, rc, rs = _rng(seed, 3)
     if scale is None:
         scale = 1.0 / math.sqrt(128 + 64)
-    s = 10.0 ** rs.uniform(math.log10(mag_lo), math.log10(mag_hi), size=Dv)
+    mags = 10.0 ** rs.uniform(math.log10(mag_lo), math.log10(mag_hi), size=Dv)
+    if balance:
+        calib = rs.standard_normal((calib_rows, Dv)) * mags
+        s = np.sqrt(np.mean(calib * calib, axis=0))
+    else:
+        s = np.ones(Dv)
     qn = _normal(rq, (B, Hq, Dqk)).astype(np.float64)
-    q_tilde = qn[..., :Dv] * s                      # raw absorbed query
+    q_tilde = qn[..., :Dv] * mags                   # raw absorbed query
     qn[..., :Dv] = q_tilde / s                      # q̃·S⁻¹
     q = round_to_bf16_bits(qn)
     elt, nan = (np.uint8, E4M3_NAN_BITS) if fp8 else (np.uint16, BF16_NAN_BITS)
@@ -341,12 +355,12 @@ def gen_decode_mla(B, Hq, kv_len=None, Dqk=576, Dv=512, kv_cap=None, seed=0,
     for b in range(B):                              # per batch to bound memory
         n = int(lens[b])
         cn = _normal(rc, (n, Dqk)).astype(np.float64)
-        c_raw = cn[:, :Dv] / s                      # raw latent
+        c_raw = cn[:, :Dv] / mags                   # raw latent
         cn[:, :Dv] = s * c_raw                      # S·c
         ckv[b, :n] = round_to_e4m3_bits(cn) if fp8 else round_to_bf16_bits(cn)
         ckv[b, n:] = nan if poison_tail else elt(0)
     return DecodeMLA(B, Hq, kv_len, kv_cap, Dqk, Dv, float(scale), q, ckv, s,
-                     lens if kv_lens is not None else None, cache_dtype)
+                     lens if kv_lens is not None else None, cache_dtype, mags)
 
 
 # --------------------------------------------------------- named workloads ---
