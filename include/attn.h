@@ -209,6 +209,27 @@ size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len,
                                        int D);
 
 /*
+ * GQA decode that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Same
+ * arguments, kernels, results (bit for bit) and errors as attn_decode_gqa,
+ * without the workspace pair: the split partials go to a static device
+ * array of 2 MiB inside the library (one per GPU, held until the process
+ * ends; its device address is looked up on the first call on each device).
+ * That covers every shape whose partials need at most 2 MiB — among them
+ * any group size up to 4, and the Llama-3-8B decode (B = 8, 32/8 heads,
+ * 4096 keys: 0.5 MiB); a shape needing more returns ATTN_ERR_WORKSPACE,
+ * launches nothing and must use attn_decode_gqa. Nothing in the array has
+ * to start at any value. All calls on one GPU share the array and it keeps
+ * the last call's contents: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ */
+attn_status attn_decode_gqa_noalloc(const void *q, const void *k_cache,
+                                    const void *v_cache, void *o, float *lse, int B,
+                                    int Hq, int Hkv, int kv_len, int kv_cap, int D,
+                                    float scale, hipStream_t stream);
+
+/*
  * GQA decode over an FP8 K/V cache: as attn_decode_gqa, but k_cache and
  * v_cache hold OCP FP8 E4M3 codes, one byte per element ([B, Hkv, kv_cap, D]
  * bytes; sign, 4-bit exponent with bias 7, 3-bit mantissa, largest finite

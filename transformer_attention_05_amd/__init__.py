@@ -7,6 +7,7 @@ no fallback: if libattn.so is missing or fails to load, every call raises.
 
     o, lse = attn_prefill_causal(q, k, v, scale)                  # [B,H,N,D]
     o, lse = attn_decode_gqa(q, k_cache, v_cache, kv_len, scale)  # q [B,Hq,D]
+    o, lse = attn_decode_gqa_noalloc(q, k_cache, v_cache, kv_len, scale)  # no workspace
     o, lse = attn_decode_mla_absorbed(q, ckv, kv_len, 512, scale) # q [B,Hq,576]
     o, lse = attn_prefill_chunked(q, k_cache, v_cache, kv_lens, scale)  # q [B,Hq,Nq,D]
     o, lse = attn_decode_gqa_ragged(q, k_cache, v_cache, kv_lens, max_kv_len, scale)
@@ -60,6 +61,7 @@ def load() -> ctypes.CDLL:
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.attn_prefill_causal.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.attn_decode_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        lib.attn_decode_gqa_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
         lib.attn_decode_mla_absorbed.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_gqa_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_mla_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
@@ -79,7 +81,8 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_gqa_workspace_bytes.restype = sz
         lib.attn_decode_mla_workspace_bytes.restype = sz
         lib.attn_decode_mla_ragged_workspace_bytes.restype = sz
-        for fn in (lib.attn_prefill_causal, lib.attn_decode_gqa, lib.attn_decode_mla_absorbed,
+        for fn in (lib.attn_prefill_causal, lib.attn_decode_gqa, lib.attn_decode_gqa_noalloc,
+                   lib.attn_decode_mla_absorbed,
                    lib.attn_prefill_chunked, lib.attn_decode_gqa_ragged, lib.attn_decode_gqa_fp8,
                    lib.attn_prefill_causal_backward,
                    lib.attn_decode_mla_ragged, lib.attn_decode_mla_fp8):
@@ -256,6 +259,22 @@ def attn_decode_gqa(q, k_cache, v_cache, kv_len, scale, out=None, lse=None, ws=N
     st = lib.attn_decode_gqa(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
                              B, Hq, Hkv, int(kv_len), kv_cap, D, sc,
                              _ptr(w), w.numel(), _stream(dev))
+    _check(st, lib)
+    return o, l
+
+
+def attn_decode_gqa_noalloc(q, k_cache, v_cache, kv_len, scale, out=None, lse=None):
+    """attn_decode_gqa without a workspace: the library keeps the split
+    partials in its own static device scratch and allocates nothing (pass
+    out= and lse= to allocate nothing here either). Calls that may overlap
+    on one GPU race on that scratch. Returns (o [B,Hq,D] bf16, lse [B,Hq])."""
+    lib = load()
+    dev, B, Hq, Hkv, kv_cap, D = _gqa_args(q, k_cache, v_cache, torch.bfloat16)
+    sc = _scale(scale)
+    o = _out(out, "out", torch.bfloat16, (B, Hq, D), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq), dev)
+    st = lib.attn_decode_gqa_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(l),
+                                     B, Hq, Hkv, int(kv_len), kv_cap, D, sc, _stream(dev))
     _check(st, lib)
     return o, l
 

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "launch.h"
 
@@ -46,7 +48,7 @@ attn_status decode_gqa_impl(const char *fn, const void *q, const void *k_cache,
                             const void *v_cache, void *o, float *lse, const int *kv_lens,
                             int B, int Hq, int Hkv, int kv_len, int kv_cap, int D, float scale,
                             void *workspace, size_t workspace_bytes, hipStream_t stream,
-                            bool fp8 = false)
+                            bool fp8 = false, bool fixed_scratch = false)
 {
     const char *len_name = kv_lens ? "max_kv_len" : "kv_len";
     if (B < 1 || Hq < 1 || Hkv < 1 || D < 1)
@@ -69,12 +71,51 @@ attn_status decode_gqa_impl(const char *fn, const void *q, const void *k_cache,
         return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned (o, lse, kv_lens: 4)", fn);
     attn::GqaPlan p;
     attn::gqa_plan(B, Hq, Hkv, kv_len, &p, fp8);
+    if (fixed_scratch && p.ws_total > workspace_bytes)
+        return fail(ATTN_ERR_WORKSPACE,
+                    "%s: this shape needs %zu bytes of scratch; the library's static scratch holds "
+                    "%zu (use attn_decode_gqa with a caller workspace)", fn, p.ws_total,
+                    workspace_bytes);
     if (!workspace || workspace_bytes < p.ws_total || !aligned16(workspace))
         return fail(ATTN_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, p.ws_total,
                     workspace ? workspace_bytes : (size_t)0);
     return from_hip(attn::launch_decode_gqa(p, q, k_cache, v_cache, o, lse, B, Hq, Hkv, kv_len,
                                             kv_cap, scale, workspace, stream, kv_lens, fp8),
                     fn);
+}
+
+// Scratch of attn_decode_gqa_noalloc: the split partials between the split
+// kernel and the merge kernel live in this fixed device array instead of a
+// caller workspace, so the call allocates nothing. Each device holds its own
+// copy until the process ends. On the host the name `scratch` is only a
+// stand-in for the symbol: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+constexpr size_t kScratchBytes = 2u << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+attn_status scratch_of_current_device(const char *fn, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e, fn);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn, dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return from_hip(e, fn);
+        if (!ptr) return fail(ATTN_ERR_HIP, "%s: no device address for the static scratch", fn);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ATTN_OK;
 }
 
 attn_status decode_mla_impl(const char *fn, const void *q, const void *ckv, void *o, float *lse,
@@ -255,6 +296,20 @@ attn_status attn_decode_gqa(const void *q, const void *k_cache, const void *v_ca
         return fail(ATTN_ERR_NULL_POINTER, "attn_decode_gqa: NULL tensor pointer");
     return decode_gqa_impl("attn_decode_gqa", q, k_cache, v_cache, o, lse, nullptr, B, Hq, Hkv,
                            kv_len, kv_cap, D, scale, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_gqa_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                    void *o, float *lse, int B, int Hq, int Hkv, int kv_len,
+                                    int kv_cap, int D, float scale, hipStream_t stream)
+{
+    const char *fn = "attn_decode_gqa_noalloc";
+    if (!q || !k_cache || !v_cache || !o || !lse)
+        return fail(ATTN_ERR_NULL_POINTER, "%s: NULL tensor pointer", fn);
+    void *ws = nullptr;
+    const attn_status st = scratch_of_current_device(fn, &ws);
+    if (st != ATTN_OK) return st;
+    return decode_gqa_impl(fn, q, k_cache, v_cache, o, lse, nullptr, B, Hq, Hkv, kv_len, kv_cap, D,
+                           scale, ws, kScratchBytes, stream, false, true);
 }
 
 attn_status attn_decode_gqa_fp8(const void *q, const void *k_cache, const void *v_cache,
