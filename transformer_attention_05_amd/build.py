@@ -2,7 +2,8 @@
 
     python -m transformer_attention_05_amd.build
 
-Every source is compiled for gfx950 only, with packed-fp32 instruction
+libattn_probes.so (the hardware-ceiling probes bench.py --ceilings runs) is
+built beside it. Every source is compiled for gfx950 only, with packed-fp32 instruction
 selection disabled (-Xclang -target-feature -Xclang -packed-fp32-ops: the
 host pass warns that it does not know the feature, which is harmless).
 Objects go to _build/, the library to the package directory.
@@ -19,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+PROBE_LIB = os.path.join(PKG, "libattn_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_api.cpp", "decode_gqa.hip", "prefill_bf16.hip", "prefill_f32.hip",
@@ -50,6 +52,11 @@ def build(verbose: bool = False) -> str:
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                    check=True)
     os.replace(tmp, LIB)
+    # the measurement probes (bench.py --ceilings) are a library of their own
+    pobj = _compile("probes.hip", verbose)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", pobj, "-o", tmp], check=True)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -1,0 +1,109 @@
+// Hardware ceilings the measurements of the attention kernels are read
+// against (libattn_probes.so, used by bench.py --ceilings; not part of the
+// attention library's C ABI):
+//   * attn_probe_stream_read: a plain streaming read of a device buffer, 16
+//     bytes per lane per load, several loads in flight per lane, over a grid
+//     of the caller's size. Its best rate over a few grid sizes is the read
+//     bandwidth a decode kernel can hope for on this GPU (the 8 TB/s HBM
+//     figure is the interface peak; a read-only kernel reaches less).
+//   * attn_probe_valu: per-wave timing (shader clock) of long runs of
+//     independent v_exp_f32 (the transcendental unit the online softmax's
+//     2^x uses), of fp32 FMAs, and of a software 2^x built from FMAs
+//     (range reduction x = n + f with n = rint(x), a degree-6 polynomial
+//     for 2^f on [−½, ½], n added to the exponent), each with eight independent chains
+//     per lane and enough waves per SIMD to fill the issue slots.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int UNROLL>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restrict__ src, size_t n16,
+                                                          uint32_t *__restrict__ sink)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (UNROLL - 1) * stride < n16; i += UNROLL * stride) {
+        u32x4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = src[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; almost never stores
+}
+
+// 2^x from FMAs: x = n + f with n = rint(x), f in [−½, ½]; 2^f by a degree-6
+// Taylor polynomial of e^(f·ln2) in Horner form (relative error < 2^-22 on
+// [−½, ½]); the exponent n is added to the result's exponent bits.
+__device__ __forceinline__ float exp2_poly(float x)
+{
+    x = fminf(fmaxf(x, -126.f), 126.f);
+    const float n = __builtin_rintf(x);
+    const float f = x - n;
+    float p = 1.5403530e-4f;            // ln2^6 / 720
+    p = fmaf(p, f, 1.3333558e-3f);      // ln2^5 / 120
+    p = fmaf(p, f, 9.6181291e-3f);      // ln2^4 / 24
+    p = fmaf(p, f, 5.5504109e-2f);      // ln2^3 / 6
+    p = fmaf(p, f, 2.4022651e-1f);      // ln2^2 / 2
+    p = fmaf(p, f, 6.9314718e-1f);      // ln2
+    p = fmaf(p, f, 1.0f);
+    return __int_as_float(__float_as_int(p) + ((int)n << 23));
+}
+
+template <int KIND>  // 0: v_exp_f32, 1: fma, 2: exp2_poly
+__global__ __launch_bounds__(256) void valu_kernel(float *__restrict__ out, unsigned long long *__restrict__ cyc,
+                                                   int iters)
+{
+    float x[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = -1.0f - 0.01f * (float)(threadIdx.x & 63) - 0.1f * (float)c;
+    const unsigned long long t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if (KIND == 0) x[c] = __builtin_amdgcn_exp2f(x[c]);
+            else if (KIND == 1) x[c] = fmaf(x[c], 0.999f, -0.5f);
+            else x[c] = exp2_poly(x[c]);
+        }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s += x[c];
+    const unsigned long long t1 = __builtin_readcyclecounter();
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+    if ((threadIdx.x & 63) == 0) cyc[(size_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = t1 - t0;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads nbytes (a multiple of 16) from src with `blocks` workgroups of 256
+// threads, four 16-byte loads in flight per lane. Returns a hipError_t code.
+int attn_probe_stream_read(const void *src, size_t nbytes, int blocks, void *sink, hipStream_t st)
+{
+    stream_read_kernel<4><<<blocks, 256, 0, st>>>((const u32x4 *)src, nbytes / 16, (uint32_t *)sink);
+    return (int)hipGetLastError();
+}
+
+// kind 0: v_exp_f32, 1: fp32 FMA, 2: 2^x from FMAs. Each lane runs eight
+// independent chains of `iters` steps; cyc[w] receives wave w's shader-clock
+// cycles (blocks × 4 waves); out holds one float per thread.
+int attn_probe_valu(int kind, int blocks, int iters, float *out, unsigned long long *cyc, hipStream_t st)
+{
+    if (kind == 0) valu_kernel<0><<<blocks, 256, 0, st>>>(out, cyc, iters);
+    else if (kind == 1) valu_kernel<1><<<blocks, 256, 0, st>>>(out, cyc, iters);
+    else if (kind == 2) valu_kernel<2><<<blocks, 256, 0, st>>>(out, cyc, iters);
+    else return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"
