@@ -256,15 +256,26 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     // 64 i + l = (row r, physical chunk pc), and come from row r, logical
     // chunk swz(r, pc). The byte offsets within a full tile are fixed.
     // (each offset is below 2^16: two per register)
-    uint32_t voffp[(G::LOADS_HI + 1) / 2] = {};
-#pragma unroll
-    for (int j = 0; j < G::LOADS_HI; ++j) {
-        const int pos = 64 * (wave + MW * j) + lane;
+    // The copies every wave makes (j < LOADS_LO) keep their offsets packed in
+    // registers; the one extra copy of the first LOADS % MW waves computes its
+    // offset when issued, from a lane index made there (held across the loop,
+    // that offset was spilled, and the reload's wait also waited for every
+    // tile copy in flight).
+    auto voff_of = [&](int j, int ln) __attribute__((always_inline)) {
+        const int pos = 64 * (wave + MW * j) + ln;
         const int r = min(pos / G::CH, MBC - 1), pc = pos % G::CH;
-        voffp[j / 2] |= (uint32_t)(r * G::ROWB + 16 * swz_t<F8>(r, pc)) << (16 * (j & 1));
-    }
+        return (uint32_t)(r * G::ROWB + 16 * swz_t<F8>(r, pc));
+    };
+    uint32_t voffp[(G::LOADS_LO + 1) / 2] = {};
+#pragma unroll
+    for (int j = 0; j < G::LOADS_LO; ++j) voffp[j / 2] |= voff_of(j, lane) << (16 * (j & 1));
     static_assert(G::TILEB <= 65536, "tile offsets fit 16 bits");
-    auto voff = [&](int j) __attribute__((always_inline)) { return (voffp[j / 2] >> (16 * (j & 1))) & 0xffffu; };
+    auto voff = [&](int j) __attribute__((always_inline)) {
+        if (j < G::LOADS_LO) return (voffp[j / 2] >> (16 * (j & 1))) & 0xffffu;
+        int ln;  // the lane index, recomputed here (v_mbcnt) rather than kept live
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        return voff_of(j, ln);
+    };
     // Ragged batches: made opaque once per tile, so the unpacked offsets are
     // rebuilt (a shift and a mask each) rather than held in registers. There
     // they spilled, and each reload's wait also waited for every tile copy in
@@ -273,7 +284,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     auto voff_refresh = [&]() __attribute__((always_inline)) {
         if constexpr (SK) {
 #pragma unroll
-            for (int i = 0; i < (G::LOADS_HI + 1) / 2; ++i) asm volatile("" : "+v"(voffp[i]));
+            for (int i = 0; i < (G::LOADS_LO + 1) / 2; ++i) asm volatile("" : "+v"(voffp[i]));
         }
     };
     // Rows past the split's end repeat its last row (their scores are masked).
@@ -326,11 +337,31 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
             // (bf16: one 16-byte chunk; E4M3: 8 bytes, widened at the MFMA)
             const char *row0 = tb + hcol * G::ROWB, *row1 = row0 + 16 * G::ROWB;
             using Raw = std::conditional_t<F8, u32x2, u32x4>;
-            auto ld = [&](const char *rowp, int r, int ks) __attribute__((always_inline)) {
-                if constexpr (F8)
-                    return *(const u32x2 *)(rowp + 16 * swz8(r, 2 * ks + (quad >> 1)) + 8 * (quad & 1));
-                else
-                    return *(const u32x4 *)(rowp + 16 * swz(r, 4 * ks + quad));
+            // The swizzled chunk of k-step ks follows one per-lane pattern for
+            // even ks and one for odd ks, each moving by a fixed amount every
+            // two steps: (ks odd ? po : pe) + STEP2·(ks / 2) is the chunk
+            // swz(r, 4ks + quad) (swz8(r, 2ks + quad / 2) for E4M3), so the
+            // addresses are two registers per row and immediate offsets.
+            constexpr int STEP2 = F8 ? 64 : 128;
+            auto ptrs = [&](const char *rowp, int r, const char *&pe, const char *&po)
+                __attribute__((always_inline)) {
+                if constexpr (F8) {
+                    const int x = (quad >> 1) ^ ((r >> 2) & 1) ^ ((((r >> 3) ^ (r >> 4)) & 1) << 1);
+                    pe = rowp + 16 * x + 8 * (quad & 1);
+                    po = rowp + 16 * (x ^ 2) + 8 * (quad & 1);
+                } else {
+                    const int y = quad ^ (r & 7) ^ ((r >> 4) & 1);
+                    pe = rowp + 16 * y;
+                    po = rowp + 16 * (y ^ 4);
+                }
+            };
+            const char *pe0, *po0, *pe1, *po1;
+            ptrs(row0, hcol, pe0, po0);
+            ptrs(row1, 16 + hcol, pe1, po1);
+            auto ld = [&](int half, int ks) __attribute__((always_inline)) {
+                const char *p = (ks & 1 ? (half ? po1 : po0) : (half ? pe1 : pe0)) + STEP2 * (ks >> 1);
+                if constexpr (F8) return *(const u32x2 *)p;
+                else return *(const u32x4 *)p;
             };
             auto opnd = [&](Raw a) __attribute__((always_inline)) {
                 if constexpr (F8) return as<bf16x8>(e4m3x8_to_bf16(a));
@@ -338,7 +369,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
             };
             if (cbase) voff_refresh();
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-            Raw a0 = ld(row0, hcol, 0), a1 = ld(row1, 16 + hcol, 0);
+            Raw a0 = ld(0, 0), a1 = ld(1, 0);
 #pragma unroll
             for (int ks = 0; ks < MKS; ++ks) {
                 constexpr int kEvery = (MKS + G::LOADS_HI - 1) / G::LOADS_HI;  // score steps per copy
@@ -350,8 +381,8 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
                 Raw n0 = a0, n1 = a1;
                 u32x4 qn;
                 if (ks + 1 < MKS) {
-                    n0 = ld(row0, hcol, ks + 1);
-                    n1 = ld(row1, 16 + hcol, ks + 1);
+                    n0 = ld(0, ks + 1);
+                    n1 = ld(1, ks + 1);
                 }
                 if (ks >= MKR) qn = q_lds[ks - MKR][wave][lane];
                 const bf16x8 qk = ks < MKR ? qf[ks < MKR ? ks : 0] : as<bf16x8>(qn);
