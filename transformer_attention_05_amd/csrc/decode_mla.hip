@@ -30,6 +30,12 @@
 // lane), but each wave now reads only its 64 channels: transposed reads run
 // at half the rate of ds_read_b128 and were the busiest LDS traffic when
 // every wave read all 512 channels for its own heads.
+// Schedule. For uniform batches without the residual product the loop is
+// software-pipelined over tiles: step t scores tile t + 1, then runs the
+// P·V MFMAs of tile t with the softmax of tile t + 1 in five stages between
+// the head blocks' MFMAs (independent work, so the VALU overlaps the matrix
+// cores), one barrier per step. The other kernels score, barrier, multiply
+// and barrier again per tile.
 // Softmax. Base 2, against a reference max m that moves only when a score
 // exceeds it by more than kLazy (so the weights 2^(s − m) stay ≤ 2^kLazy and
 // the output is rescaled rarely); the rescale factor of each head goes to
@@ -208,9 +214,14 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     float *__restrict__ ws_part, const int *__restrict__ kv_lens, int B)
 {
     using G = MGeo<F8>;
+    // PIPE: the software-pipelined schedule (uniform batches without the
+    // residual product); its weights and factors are double-buffered
+    constexpr bool PIPE = LOM == 0 && !SK;
+    constexpr int NPB = PIPE ? 2 : 1;
+    static_assert(MNBUF * G::TILEB + NPB * MHB * 1024 + (LOM ? MHB : 1) * 1024 + NPB * MH * 4 +
+                      MKQ * MW * 1024 <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) char tile[MNBUF][G::TILEB];
     // weights in B-operand order and per-head α (then λ)
-    constexpr int NPB = 1;
     __shared__ __attribute__((aligned(16))) u32x4 p_hi[NPB][MHB][64];
     __shared__ __attribute__((aligned(16))) u32x4 p_lo[LOM ? MHB : 1][64];
     __shared__ __attribute__((aligned(16))) float hinfo[NPB][16][MHB];
@@ -326,14 +337,14 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     const int ve = (lane >> 2) & 3, vc = lane & 3;
     const int vr1 = 4 * quad + ve, vr2 = 16 + 4 * quad + ve;
 
-    // ---- scores of this wave's 16 heads, online softmax, weights to LDS.
-    // PARTIAL: the tile runs past the split's end (its last keys are masked).
-    // cbase (if set): the next full tile's copies into buffer cbuf are issued
-    // between the score steps instead of in one burst
-    auto scores = [&](const char *tb, int t0, int pb, const char *cbase, int cbuf,
-                      auto partial_tag) __attribute__((always_inline)) {
+    // ---- scores of this wave's 16 heads: raw q·c into sc (the scale is
+    // applied in the exponent). PARTIAL: the tile runs past the split's end
+    // (its last keys are masked). cbase (if set): the next full tile's
+    // copies into buffer cbuf are issued between the score steps instead of
+    // in one burst
+    auto score_mfma = [&](const char *tb, int t0, float (&sc)[8], const char *cbase, int cbuf,
+                          auto partial_tag) __attribute__((always_inline)) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
-        float sc[8];  // raw scores q·c (the scale is applied in the exponent)
         {
             // the two 16-key halves of the tile as two independent MFMA chains,
             // the operands of step ks + 1 requested before the MFMAs of step ks
@@ -412,45 +423,72 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
                 if (PARTIAL && t0 + 16 + 4 * quad + i >= key_end) sc[4 + i] = -INFINITY;
             }
         }
-        float mx = sc[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));  // finite: each tile has a key < key_end
-        mx *= scale_log2;                  // scale > 0: the max commutes with it
-        float alpha = 1.f;
-        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kLazy)) {
-            const float m_new = mx > m_ref + kLazy ? mx : m_ref;
-            alpha = exp2_fast(m_ref - m_new);  // first tile: 2^-inf = 0
-            l_e *= alpha;
-            l_o *= alpha;
-            m_ref = m_new;
-        }
-        u32x4 phi, plo;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float p0 = exp2_fast(fmaf(sc[2 * u], scale_log2, -m_ref));
-            const float p1 = exp2_fast(fmaf(sc[2 * u + 1], scale_log2, -m_ref));
-            l_e += p0 + p1;
-            const uint32_t h = pack_bf16x2(p0, p1);
-            phi[u] = h;
-            l_o = sum_bf16x2(h, l_o);
-            if (LOM != 0 && lo_on) {
-                // the residual p − bf16(p) is exact in fp32
-                const uint32_t w = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
-                plo[u] = w;
-                l_o = sum_bf16x2(w, l_o);
-            }
-        }
-        // B operand of head block `wave`: slots 0..3 ↔ keys 4·quad + e,
-        // slots 4..7 ↔ keys 16 + 4·quad + e (the Sᵀ rows this lane holds)
-        p_hi[pb][wave][lane] = phi;
-        if (LOM != 0 && lo_on) p_lo[wave][lane] = plo;
-        if (quad == 0) hinfo[pb][hcol][wave] = alpha;
     };
 
-    // ---- Oᵀ += Vᵀ Pᵀ over this wave's 64 channels and every head block
-    auto values = [&](const char *tb, int pb) __attribute__((always_inline)) {
+    // ---- online softmax of the tile's scores, weights and factors to LDS
+    // buffer pb, in five stages (the pipelined schedule runs P·V MFMAs of
+    // the previous tile between them): 0 the tile max, 1 the reference
+    // update, 2 and 3 the weights of the two 16-key halves, 4 the stores.
+    // The reference moves only when a score exceeds it by more than kLazy;
+    // lanes whose reference stays get α = 2^0 = 1 exactly.
+    float sm_mx = 0.f, sm_alpha = 1.f;
+    u32x4 sm_phi = {}, sm_plo = {};
+    auto softmax_stage = [&](const float (&sc)[8], int pb, int stage) __attribute__((always_inline)) {
+        if (stage == 0) {
+            float mx = sc[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));  // finite: each tile has a key < key_end
+            sm_mx = mx * scale_log2;           // scale > 0: the max commutes with it
+        } else if (stage == 1) {
+            const bool mv = sm_mx > m_ref + kLazy;
+            const float m_new = mv ? sm_mx : m_ref;
+            sm_alpha = mv ? exp2_fast(m_ref - m_new) : 1.f;  // first tile: 2^-inf = 0
+            l_e *= sm_alpha;
+            l_o *= sm_alpha;
+            m_ref = m_new;
+        } else if (stage == 2 || stage == 3) {
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const int u = 2 * (stage - 2) + v;
+                const float p0 = exp2_fast(fmaf(sc[2 * u], scale_log2, -m_ref));
+                const float p1 = exp2_fast(fmaf(sc[2 * u + 1], scale_log2, -m_ref));
+                l_e += p0 + p1;
+                const uint32_t h = pack_bf16x2(p0, p1);
+                sm_phi[u] = h;
+                l_o = sum_bf16x2(h, l_o);
+                if (LOM != 0 && lo_on) {
+                    // the residual p − bf16(p) is exact in fp32
+                    const uint32_t w = pack_bf16x2(p0 - bf16lo(h), p1 - bf16hi(h));
+                    sm_plo[u] = w;
+                    l_o = sum_bf16x2(w, l_o);
+                }
+            }
+        } else {
+            // B operand of head block `wave`: slots 0..3 ↔ keys 4·quad + e,
+            // slots 4..7 ↔ keys 16 + 4·quad + e (the Sᵀ rows this lane holds)
+            p_hi[pb][wave][lane] = sm_phi;
+            if (LOM != 0 && lo_on) p_lo[wave][lane] = sm_plo;
+            // (the four lanes of a head hold the same α: all store it, with no
+            // branch around the store)
+            hinfo[pb][hcol][wave] = sm_alpha;
+        }
+    };
+    auto scores = [&](const char *tb, int t0, int pb, const char *cbase, int cbuf,
+                      auto partial_tag) __attribute__((always_inline)) {
+        float sc[8];
+        score_mfma(tb, t0, sc, cbase, cbuf, partial_tag);
+#pragma unroll
+        for (int st = 0; st < 5; ++st) softmax_stage(sc, pb, st);
+    };
+
+    // ---- Oᵀ += Vᵀ Pᵀ over this wave's 64 channels and every head block.
+    // With sm set (wave-uniform), the softmax stages of the next tile's
+    // scores scn (into weight buffer pbn) run between the head blocks' MFMAs:
+    // they do not depend on them, so the VALU work overlaps the matrix cores.
+    auto values = [&](const char *tb, int pb, const float (&scn)[8], int pbn, bool sm)
+        __attribute__((always_inline)) {
         // rescale first: the new weights are relative to the moved references
         {
             const f32x4 a0 = *(const f32x4 *)&hinfo[pb][hcol][0], a1 = *(const f32x4 *)&hinfo[pb][hcol][4];
@@ -515,6 +553,10 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
                     for (int db = 0; db < MDBW; ++db) oacc[db][hb] = mfma16x16x32(as<bf16x8>(va[db]), bl, oacc[db][hb]);
                 }
             }
+            if (hb < 5 && sm) {
+                softmax_stage(scn, pbn, hb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -525,29 +567,73 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
             else scores(tb, t0, pb, cbase, cbuf, std::false_type{});
         }
     };
-    // Tile t lives in buffer t % MNBUF. Step t waits for tile t, then refills
-    // the buffer of tile t − 1 with tile t + MNBUF − 1. The second barrier of
-    // a step publishes the weights; the first barrier of the next step keeps
-    // them until every wave has used them. (A one-barrier variant with
-    // double-buffered weights measured slower: a wave's scores then compete
-    // for LDS with the other waves' P·V.)
+    float sc_none[8] = {};  // (no softmax between the P·V MFMAs)
+    if constexpr (PIPE) {
+        // Software-pipelined over tiles. Step t: wait for tile t + 1, one
+        // barrier, then the score MFMAs of tile t + 1, then the P·V MFMAs of
+        // tile t with the softmax of tile t + 1 run between them, its
+        // weights going to buffer (t + 1) & 1. Tile t lives in buffer
+        // t % MNBUF and is read in steps t − 1 and t, so the buffer of tile
+        // t − 1 takes tile t + 2 from step t on (its copies spread over the
+        // score steps). The barrier of step t publishes tile t + 1 and the
+        // weights of tile t, and keeps the buffers step t reuses until every
+        // wave has left step t − 1.
+        float sc[8] = {};
+        auto score_tile = [&](int u, const char *cbase, int cbuf) __attribute__((always_inline)) {
+            const int u0 = key_begin + u * MBC;
+            if (u0 + MBC > key_end) score_mfma(tile[u % MNBUF], u0, sc, cbase, cbuf, std::true_type{});
+            else score_mfma(tile[u % MNBUF], u0, sc, cbase, cbuf, std::false_type{});
+        };
+        if (n_t > 0) load_tile(key_begin, 0);
+        if (n_t > 1) load_tile(key_begin + MBC, 1);
+        if (n_t > 0) {
+            wait_tile<F8>(min(1, n_t - 1), hi_wave);
+            __syncthreads();  // tile 0 visible
+            if (own) {
+                score_tile(0, nullptr, 0);
 #pragma unroll
-    for (int p = 0; p < MNBUF - 1; ++p)
-        if (p < n_t) load_tile(key_begin + p * MBC, p);
-    for (int t = 0; t < n_t; ++t) {
-        const int t0 = key_begin + t * MBC;
-        wait_tile<F8>(min(MNBUF - 2, n_t - 1 - t), hi_wave);
-        __syncthreads();  // tile t visible; tile t − 1 and the last weights no longer read
-        // refill: a full next tile is copied from inside the score steps of
-        // the waves that score; a partial one (clamped rows), or the copies of
-        // a wave without score heads, in one go
-        const int tn = t0 + (MNBUF - 1) * MBC, bn = (t + MNBUF - 1) % MNBUF;
-        const bool refill = t + MNBUF - 1 < n_t, spread = refill && own && tn + MBC <= key_end;
-        if (refill && !spread) load_tile(tn, bn);
-        const char *tb = tile[t % MNBUF];
-        do_scores(tb, t0, 0, spread ? cb + (size_t)tn * G::ROWB : nullptr, bn);
-        __syncthreads();  // weights and rescale factors of every head visible
-        values(tb, 0);
+                for (int st = 0; st < 5; ++st) softmax_stage(sc, 0, st);
+            }
+        }
+        for (int t = 0; t < n_t; ++t) {
+            const bool next = t + 1 < n_t;
+            if (next) wait_tile<F8>(0, hi_wave);
+            __syncthreads();  // tile t + 1 and the weights of tile t visible
+            const int tn = key_begin + (t + 2) * MBC, bn = (t + 2) % MNBUF;
+            const bool refill = t + 2 < n_t, spread = refill && own && next && tn + MBC <= key_end;
+            if (refill && !spread) load_tile(tn, bn);
+            if (next && own) score_tile(t + 1, spread ? cb + (size_t)tn * G::ROWB : nullptr, bn);
+            // (waves without score heads run the stages on zeros; their
+            // weights and factors are never read)
+            // (one call with a flag: two calls, with and without the
+            // softmax, made the register allocator spill)
+            values(tile[t % MNBUF], t & 1, sc, (t + 1) & 1, next);
+        }
+    } else {
+        // Tile t lives in buffer t % MNBUF. Step t waits for tile t, then refills
+        // the buffer of tile t − 1 with tile t + MNBUF − 1. The second barrier of
+        // a step publishes the weights; the first barrier of the next step keeps
+        // them until every wave has used them. (A one-barrier variant with
+        // double-buffered weights measured slower: a wave's scores then compete
+        // for LDS with the other waves' P·V.)
+    #pragma unroll
+        for (int p = 0; p < MNBUF - 1; ++p)
+            if (p < n_t) load_tile(key_begin + p * MBC, p);
+        for (int t = 0; t < n_t; ++t) {
+            const int t0 = key_begin + t * MBC;
+            wait_tile<F8>(min(MNBUF - 2, n_t - 1 - t), hi_wave);
+            __syncthreads();  // tile t visible; tile t − 1 and the last weights no longer read
+            // refill: a full next tile is copied from inside the score steps of
+            // the waves that score; a partial one (clamped rows), or the copies of
+            // a wave without score heads, in one go
+            const int tn = t0 + (MNBUF - 1) * MBC, bn = (t + MNBUF - 1) % MNBUF;
+            const bool refill = t + MNBUF - 1 < n_t, spread = refill && own && tn + MBC <= key_end;
+            if (refill && !spread) load_tile(tn, bn);
+            const char *tb = tile[t % MNBUF];
+            do_scores(tb, t0, 0, spread ? cb + (size_t)tn * G::ROWB : nullptr, bn);
+            __syncthreads();  // weights and rescale factors of every head visible
+            values(tb, 0, sc_none, 0, false);
+        }
     }
 
     // ---- epilogue: per-head sums over the head's four lanes
