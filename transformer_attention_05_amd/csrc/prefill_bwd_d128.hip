@@ -167,8 +167,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(1024))) TileBuf buf[NRING];
 
     const int G = Hq / Hkv;
-    // heaviest first: key block 0 sees every query
-    const int kblk = blockIdx.x % n_kblk, bh = blockIdx.x / n_kblk;
+    // Heaviest first (key block 0 sees every query). When the (b, K/V head)
+    // groups are a multiple of 8, all key blocks of a group run on one XCD
+    // (workgroups are dealt to the 8 XCDs round-robin by id): they read the
+    // same Q and dO tiles, and walk them in the same order (below), so the
+    // tiles come from that XCD's L2 rather than from HBM once per block.
+    int kblk, bh;
+    {
+        const int groups = (int)gridDim.x / n_kblk, lin = blockIdx.x;
+        if (groups % 8 == 0) {
+            const int x = lin % 8, kk = lin / 8, per = groups / 8;
+            kblk = kk / per;
+            bh = 8 * (kk % per) + x;
+        } else {
+            kblk = lin % n_kblk;
+            bh = lin / n_kblk;
+        }
+    }
     const int b = bh / Hkv, hkv = bh % Hkv;
     const int k0 = kblk * BLK;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -199,12 +214,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const int q_first = (k0 / T) * T;                   // first tile with a query >= k0
     const int n_qt = (N - q_first + T - 1) / T;         // query tiles per head
     const int n_it = G * n_qt;
+    // item it: the query heads of the group innermost, the tiles from the
+    // last one down to the diagonal, so every key block of the group starts
+    // on the same tiles and they walk them together
+    auto item_h = [&](int it) __attribute__((always_inline)) { return hkv * G + it % G; };
+    auto item_q0 = [&](int it) __attribute__((always_inline)) { return q_first + T * (n_qt - 1 - it / G); };
     // copy j of a tile (wave w issues j = w, w + 4, ...): 0..7 Q rows
     // 4j .. 4j + 3, 8..15 dO rows, 16 LSE (lanes 0..31) and D (32..63).
     // Lane l lands at row 4j + l/16, physical chunk l % 16, so it reads
     // logical chunk (l % 16) ^ bswz(row).
     auto issue_tile = [&](int it, TileBuf &t) __attribute__((always_inline)) {
-        const int h = hkv * G + it / n_qt, q0 = q_first + T * (it % n_qt);
+        const int h = item_h(it), q0 = item_q0(it);
         const size_t qoff = ((size_t)b * Hq + h) * N;
         for (int j = wave; j < TILE_COPIES; j += NWV) {  // wave-uniform
             if (j == TILE_COPIES - 1) {  // padded rows: q0 + 31 < Np
@@ -230,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     for (int it = 0; it < n_it; ++it) {
         // into the buffer of tile it − 1, which every wave is done with
         if (it + NRING - 1 < n_it) issue_tile(it + NRING - 1, buf[(it + NRING - 1) % NRING]);
-        const int q0 = q_first + T * (it % n_qt);
+        const int q0 = item_q0(it);
         const TileBuf &tb = buf[it % NRING];
         // the lane's read addresses; the lane index is made opaque so that they
         // are rebuilt per tile (a few VALU) rather than held in registers
@@ -325,8 +345,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 {
     __shared__ __attribute__((aligned(1024))) KTileBuf buf[NRING];
 
-    // heaviest first: the last query block sees every key
-    const int qblk = n_qblk - 1 - (int)(blockIdx.x % n_qblk), bhq = blockIdx.x / n_qblk;
+    // Heaviest first (the last query block sees every key). When the (b,
+    // K/V head) groups are a multiple of 8, every query block of every query
+    // head of a group runs on one XCD: they all walk the group's K and V
+    // tiles from the first one up, so the tiles come from that XCD's L2.
+    int qblk, bhq;
+    {
+        const int G = Hq / Hkv, groups = (int)gridDim.x / (n_qblk * G), lin = blockIdx.x;
+        if (groups % 8 == 0) {
+            const int x = lin % 8, kk = lin / 8, per = groups / 8;
+            const int rem = kk % (per * G), gr = 8 * (rem / G) + x;
+            qblk = n_qblk - 1 - kk / (per * G);
+            bhq = (gr / Hkv) * Hq + (gr % Hkv) * G + rem % G;
+        } else {
+            qblk = n_qblk - 1 - lin % n_qblk;
+            bhq = lin / n_qblk;
+        }
+    }
     const int b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv);
     const int q0 = qblk * BLK;
     const int tid = threadIdx.x, lane = tid & 63;
