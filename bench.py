@@ -178,7 +178,8 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev, plain=False
         q = _upload_bf16(torch, w.q, dev)
         c = torch.from_numpy(w.ckv).to(dev) if fp8 else _upload_bf16(torch, w.ckv, dev)
         if ragged:
-            nbytes = workloads.decode_mla_ragged_bytes(w.Hq, w.kv_lens, w.Dqk, w.Dv)
+            nbytes = workloads.decode_mla_ragged_bytes(w.Hq, w.kv_lens, w.Dqk, w.Dv,
+                                                       kv_elt=1 if fp8 else 2)
         else:
             nbytes = workloads.decode_mla_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv,
                                                 kv_elt=1 if fp8 else 2)
@@ -189,8 +190,9 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev, plain=False
         ws_fn = attn.attn_decode_mla_ragged_workspace_bytes if ragged else attn.attn_decode_mla_workspace_bytes
         ws = torch.empty(ws_fn(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv), dtype=torch.uint8, device=dev)
         if ragged:
-            calls = [lambda s=s: attn.attn_decode_mla_ragged(s[0], s[1], lens, w.kv_len, w.Dv,
-                                                             w.scale, out=o, lse=lse, ws=ws)
+            fn = attn.attn_decode_mla_ragged_fp8 if fp8 else attn.attn_decode_mla_ragged
+            calls = [lambda s=s: fn(s[0], s[1], lens, w.kv_len, w.Dv, w.scale, out=o, lse=lse,
+                                    ws=ws)
                      for s in sets]
         elif fp8:
             calls = [lambda s=s: attn.attn_decode_mla_fp8(s[0], s[1], w.kv_len, w.Dv, w.scale,
@@ -374,7 +376,8 @@ def _work_bytes(workloads, name, w):
                                           kv_elt=1 if w.cache_dtype == "fp8" else 2)
     if kind == "decode_mla":
         if ragged:
-            return workloads.decode_mla_ragged_bytes(w.Hq, w.kv_lens, w.Dqk, w.Dv)
+            return workloads.decode_mla_ragged_bytes(w.Hq, w.kv_lens, w.Dqk, w.Dv,
+                                                     kv_elt=1 if w.cache_dtype == "fp8" else 2)
         return workloads.decode_mla_bytes(w.B, w.Hq, w.kv_len, w.Dqk, w.Dv,
                                           kv_elt=1 if w.cache_dtype == "fp8" else 2)
     return None

@@ -343,6 +343,25 @@ attn_status attn_decode_mla_ragged(const void *q, const void *ckv, void *o,
                                    void *workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/*
+ * Absorbed MLA decode of a ragged batch over an FP8 latent cache: the
+ * ragged batch of attn_decode_mla_ragged (kv_lens, max_kv_len, the balanced
+ * split over all sequences' tiles) with the E4M3 latent cache of
+ * attn_decode_mla_fp8 ([B, kv_cap, Dqk] bytes of the channel-balanced
+ * latent S·c, "MLA 矩阵乘法吸收的数值稳定性治理", §二.1; each value enters the
+ * products exactly as bf16, every product accumulates in fp32, §五). Given
+ * a bf16 copy of the same cached values, the result is bit for bit that of
+ * attn_decode_mla_ragged. Workspace: attn_decode_mla_ragged_workspace_bytes().
+ * Errors as for attn_decode_mla_ragged.
+ */
+attn_status attn_decode_mla_ragged_fp8(const void *q, const void *ckv,
+                                       void *o, float *lse,
+                                       const int *kv_lens, int B, int Hq,
+                                       int max_kv_len, int kv_cap, int Dqk,
+                                       int Dv, float scale, void *workspace,
+                                       size_t workspace_bytes,
+                                       hipStream_t stream);
+
 /* Bytes of workspace attn_decode_mla_ragged needs (0 if invalid). */
 size_t attn_decode_mla_ragged_workspace_bytes(int B, int Hq, int max_kv_len,
                                               int Dqk, int Dv);

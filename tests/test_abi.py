@@ -29,7 +29,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -161,6 +161,21 @@ def test_decode_mla_fp8_validation(lib):
     for s in BAD_SCALES:
         assert f(scale=s) == SHAPE
     assert "attn_decode_mla_fp8" in attn.last_error()
+
+
+def test_decode_mla_ragged_fp8_validation(lib):
+    f = lambda **kw: lib.attn_decode_mla_ragged_fp8(*[kw.get(n, d) for n, d in (
+        ("q", P), ("c", P), ("o", P), ("lse", P), ("lens", P), ("B", 2), ("Hq", 128),
+        ("max_len", 1000), ("kv_cap", 1024), ("Dqk", 576), ("Dv", 512), ("scale", 0.07),
+        ("ws", P), ("ws_bytes", 1 << 30), ("st", None))])
+    assert f(lens=None) == NULLP and f(c=None) == NULLP
+    assert f(max_len=1025) == SHAPE and f(max_len=0) == SHAPE
+    assert f(Dqk=192, Dv=128) == UNSUP and f(Hq=20) == UNSUP
+    assert f(c=P + 8) == UNSUP and f(lens=P + 2) == UNSUP   # misaligned cache, lengths
+    assert f(ws_bytes=attn.attn_decode_mla_ragged_workspace_bytes(2, 128, 1000) - 1) == WS
+    for s in BAD_SCALES:
+        assert f(scale=s) == SHAPE
+    assert "attn_decode_mla_ragged_fp8" in attn.last_error()
 
 
 def _chunked(lib, q=P, k=P, v=P, o=P, lse=P, lens=P, B=2, Hq=8, Hkv=2, Nq=100, kv_cap=512,

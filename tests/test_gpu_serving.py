@@ -177,6 +177,46 @@ def test_decode_mla_ragged_32k_workload_sampled_heads(gpu):
     check_bf16(host(o[:, hs]), o_ref, host(lse[:, hs]), lse_ref, "decode_mla_ragged_32k")
 
 
+# ------------------------------------------------------- ragged MLA, E4M3 cache ---
+def _dev_u8(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+
+@pytest.mark.parametrize("Hq,lens,max_len,kv_cap", [
+    (16, [0, 1, 100, 512, 513, 2000], 2000, 2000),   # short rows take the residual product
+    (128, [3, 40, 600], 600, 640),
+    (32, [0, 200, 512], 512, 520),                   # every row short
+    (144, [70, 1], 100, 100),                        # a partial head group
+    (16, [int(x) for x in workloads.ragged_lengths(70, 0, 700, 7)], 700, 700)])  # > 64 sequences
+def test_decode_mla_ragged_fp8_matches_oracle(gpu, Hq, lens, max_len, kv_cap):
+    """Ragged batch over an E4M3 latent cache (balanced rows S·c, the NaN
+    code past each length): the oracle reads the same codes."""
+    B = len(lens)
+    w = workloads.gen_decode_mla(B, Hq, kv_cap=kv_cap, kv_lens=lens, seed=3 * B + Hq,
+                                 cache_dtype="fp8")
+    o, lse = gpu.attn_decode_mla_ragged_fp8(dev_bf16(w.q), _dev_u8(w.ckv), _lens(lens), max_len,
+                                            w.Dv, w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_mla_ragged(w.q, w.ckv, w.kv_lens, w.Dv, w.scale)
+    _check_ragged(o, lse, o_ref, lse_ref, lens, "mla ragged fp8 %s" % (lens,))
+
+
+def test_decode_mla_ragged_fp8_equals_bf16_copy(gpu):
+    """The E4M3 ragged decode gives the same bits as the bf16 ragged decode
+    over a bf16 copy of the cached values (every E4M3 value is a bf16 value,
+    and both feed the same operands to the same products in the same
+    order), for a batch that mixes empty, short and long sequences."""
+    lens = [0, 7, 300, 513, 2500, 4096, 1]
+    w = workloads.gen_decode_mla(len(lens), 128, kv_cap=4096, kv_lens=lens, seed=71,
+                                 cache_dtype="fp8")
+    q, kl = dev_bf16(w.q), _lens(lens)
+    o8, l8 = gpu.attn_decode_mla_ragged_fp8(q, _dev_u8(w.ckv), kl, 4096, w.Dv, w.scale)
+    c16 = _dev_u8(w.ckv).view(torch.float8_e4m3fn).to(torch.bfloat16)
+    o16, l16 = gpu.attn_decode_mla_ragged(q, c16, kl, 4096, w.Dv, w.scale)
+    torch.cuda.synchronize()
+    assert _same(o8, o16) and _same(l8, l16)
+
+
 # ------------------------------------------------------- one graph, new lengths ---
 def test_graph_replays_follow_new_lengths(gpu):
     """The lengths are read by the kernels at run time: a graph captured once

@@ -14,6 +14,7 @@ no fallback: if libattn.so is missing or fails to load, every call raises.
     o, lse = attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, 512, scale)
     o, lse = attn_decode_gqa_fp8(q, k_fp8, v_fp8, kv_len, scale)   # E4M3 caches (uint8)
     o, lse = attn_decode_mla_fp8(q, ckv_fp8, kv_len, 512, scale)   # E4M3 latent cache
+    o, lse = attn_decode_mla_ragged_fp8(q, ckv_fp8, kv_lens, max_kv_len, 512, scale)
     dq, dk, dv = attn_prefill_causal_backward(q, k, v, o, lse, dout, scale)
 (kv_lens: an int32 GPU tensor of per-sequence lengths, read by the kernels.)
 The score scale is always an argument: the binding never infers 1/√D.
@@ -75,6 +76,7 @@ def load() -> ctypes.CDLL:
         lib.attn_decode_gqa_ragged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz,
                                                vp]
         lib.attn_decode_mla_ragged.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+        lib.attn_decode_mla_ragged_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
         lib.attn_decode_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.attn_decode_mla_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.attn_decode_mla_ragged_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -85,7 +87,8 @@ def load() -> ctypes.CDLL:
                    lib.attn_decode_mla_absorbed,
                    lib.attn_prefill_chunked, lib.attn_decode_gqa_ragged, lib.attn_decode_gqa_fp8,
                    lib.attn_prefill_causal_backward,
-                   lib.attn_decode_mla_ragged, lib.attn_decode_mla_fp8):
+                   lib.attn_decode_mla_ragged, lib.attn_decode_mla_fp8,
+                   lib.attn_decode_mla_ragged_fp8):
             fn.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [i]
         lib.attn_status_string.restype = ctypes.c_char_p
@@ -417,6 +420,27 @@ def attn_decode_mla_ragged(q, ckv, kv_lens, max_kv_len, dv, scale, out=None, lse
     st = lib.attn_decode_mla_ragged(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), _ptr(kv_lens), B, Hq,
                                     int(max_kv_len), kv_cap, Dqk, dv, sc, _ptr(w),
                                     w.numel(), _stream(dev))
+    _check(st, lib)
+    return o, l
+
+
+def attn_decode_mla_ragged_fp8(q, ckv, kv_lens, max_kv_len, dv, scale, out=None, lse=None,
+                               ws=None):
+    """Absorbed MLA decode of a ragged batch over an FP8 E4M3 latent cache:
+    ckv [B,kv_cap,Dqk] torch.uint8 (E4M3 codes of the balanced latent | rope)
+    or torch.float8_e4m3fn, filled to kv_lens[b] (int32 GPU tensor [B], each
+    at most max_kv_len). Returns (o [B,Hq,dv] bf16, lse [B,Hq] fp32)."""
+    lib = load()
+    ckv = _fp8_bytes(ckv)
+    dev, B, Hq, Dqk, kv_cap = _mla_args(q, ckv, torch.uint8)
+    _need_lens(kv_lens, B, dev)
+    dv, sc = int(dv), _scale(scale)
+    o = _out(out, "out", torch.bfloat16, (B, Hq, dv), dev)
+    l = _out(lse, "lse", torch.float32, (B, Hq), dev)
+    w = _ws(lib.attn_decode_mla_ragged_workspace_bytes(B, Hq, int(max_kv_len), Dqk, dv), ws, dev)
+    st = lib.attn_decode_mla_ragged_fp8(_ptr(q), _ptr(ckv), _ptr(o), _ptr(l), _ptr(kv_lens), B, Hq,
+                                        int(max_kv_len), kv_cap, Dqk, dv, sc, _ptr(w),
+                                        w.numel(), _stream(dev))
     _check(st, lib)
     return o, l
 

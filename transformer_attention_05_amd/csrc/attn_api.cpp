@@ -380,4 +380,16 @@ attn_status attn_decode_mla_ragged(const void *q, const void *ckv, void *o, floa
                            kv_cap, Dqk, Dv, scale, workspace, workspace_bytes, stream);
 }
 
+attn_status attn_decode_mla_ragged_fp8(const void *q, const void *ckv, void *o, float *lse,
+                                       const int *kv_lens, int B, int Hq, int max_kv_len,
+                                       int kv_cap, int Dqk, int Dv, float scale, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream)
+{
+    if (!q || !ckv || !o || !lse || !kv_lens)
+        return fail(ATTN_ERR_NULL_POINTER, "attn_decode_mla_ragged_fp8: NULL tensor pointer");
+    return decode_mla_impl("attn_decode_mla_ragged_fp8", q, ckv, o, lse, kv_lens, B, Hq,
+                           max_kv_len, kv_cap, Dqk, Dv, scale, workspace, workspace_bytes, stream,
+                           true);
+}
+
 }  // extern "C"

@@ -736,8 +736,6 @@ static hipError_t launch_decode_mla_t(const MlaPlan &p, const void *q, const voi
     if (kv_lens) {
         // ragged: balanced split over the tiles of all sequences (kv_len is
         // the longest); short sequences switch the residual product on
-        if constexpr (F8) return hipErrorNotSupported;  // no E4M3 ragged entry point
-        else {
         const dim3 grid(p.splits + B, hgs, 1);  // one workgroup per slot (piece)
         auto kern = kv_len <= kLoMaxKeys
                         ? (full ? decode_mla_kernel<1, true, true, F8> : decode_mla_kernel<1, false, true, F8>)
@@ -749,7 +747,6 @@ static hipError_t launch_decode_mla_t(const MlaPlan &p, const void *q, const voi
         if (e != hipSuccess) return e;
         return launch_merge_ragged(ws_ml, ws_part, o, lse, kv_lens, B, Hq, kv_len, p.splits, MBC,
                                    MV, st);
-        }
     }
     const dim3 grid(p.splits, hgs, B);
     auto kern = kv_len <= kLoMaxKeys

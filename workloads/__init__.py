@@ -405,6 +405,11 @@ WORKLOADS = {
     "decode_mla_ragged_32k": dict(
         kind="decode_mla", B=16, Hq=128, kv_lens=("ragged", 1024, 32768, 1108),
         kv_cap=32768, Dqk=576, Dv=512, seed=1008, scale=1.0 / math.sqrt(128 + 64)),
+    # the same ragged batch over an E4M3 latent cache
+    "decode_mla_ragged_fp8_32k": dict(
+        kind="decode_mla", B=16, Hq=128, kv_lens=("ragged", 1024, 32768, 1108),
+        kv_cap=32768, Dqk=576, Dv=512, seed=1008, scale=1.0 / math.sqrt(128 + 64),
+        cache_dtype="fp8"),
 }
 
 
@@ -478,11 +483,12 @@ def decode_gqa_ragged_bytes(Hq, Hkv, kv_lens, D, elt=2):
     return int(elt * (2 * Hkv * int(lens.sum()) * D + 2 * B * Hq * D) + 4 * B * Hq)
 
 
-def decode_mla_ragged_bytes(Hq, kv_lens, Dqk, Dv, elt=2):
-    """As decode_mla_bytes with per-sequence filled lengths."""
+def decode_mla_ragged_bytes(Hq, kv_lens, Dqk, Dv, kv_elt=2):
+    """As decode_mla_bytes with per-sequence filled lengths (kv_elt bytes per
+    cached element: 2 for bf16, 1 for E4M3; q and O are bf16)."""
     lens = np.asarray(kv_lens, dtype=np.int64).reshape(-1)
     B = lens.shape[0]
-    return int(elt * (int(lens.sum()) * Dqk + B * Hq * Dqk + B * Hq * Dv) + 4 * B * Hq)
+    return int(kv_elt * int(lens.sum()) * Dqk + 2 * (B * Hq * Dqk + B * Hq * Dv) + 4 * B * Hq)
 
 
 def prefill_backward_flops(B, Hq, N, D):
