@@ -101,7 +101,9 @@ def _mla(gpu, w):
 
 @pytest.mark.parametrize("B,Hq,kv_len,kv_cap", [
     (1, 16, 1, 32), (4, 128, 2, 8), (2, 64, 3, 3), (2, 16, 31, 64), (1, 128, 33, 40),
-    (2, 32, 1000, 1024), (1, 128, 5000, 5000), (1, 144, 70, 100)])
+    (2, 32, 1000, 1024), (1, 128, 5000, 5000), (1, 144, 70, 100),
+    (260, 16, 545, 560),   # one split per sequence (no merge), pipelined loop, partial tile
+    (2, 256, 600, 608)])   # two head groups, one tile per split
 def test_decode_mla_matches_oracle(gpu, B, Hq, kv_len, kv_cap):
     w = workloads.gen_decode_mla(B, Hq, kv_len, kv_cap=kv_cap, seed=kv_len + Hq)
     o, lse = _mla(gpu, w)
@@ -233,7 +235,7 @@ def test_decode_gqa_fp8_workload_equals_bf16_copy_of_its_values(gpu):
 @pytest.mark.parametrize("B,Hq,kv_len,kv_cap", [
     (1, 16, 1, 32), (4, 128, 2, 8), (2, 64, 3, 3), (2, 16, 31, 64), (1, 128, 33, 40),
     (2, 64, 512, 520), (2, 64, 513, 520), (2, 32, 1000, 1024), (1, 128, 5000, 5000),
-    (1, 144, 70, 100)])
+    (1, 144, 70, 100), (260, 16, 545, 560)])
 def test_decode_mla_fp8_matches_oracle(gpu, B, Hq, kv_len, kv_cap):
     """E4M3 latent cache (balanced rows S·c, the NaN code past kv_len):
     partial tiles, 16..144 heads (partial head groups), one and many splits,

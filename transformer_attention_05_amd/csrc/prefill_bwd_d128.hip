@@ -214,17 +214,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const int q_first = (k0 / T) * T;                   // first tile with a query >= k0
     const int n_qt = (N - q_first + T - 1) / T;         // query tiles per head
     const int n_it = G * n_qt;
-    // item it: the query heads of the group innermost, the tiles from the
-    // last one down to the diagonal, so every key block of the group starts
-    // on the same tiles and they walk them together
-    auto item_h = [&](int it) __attribute__((always_inline)) { return hkv * G + it % G; };
-    auto item_q0 = [&](int it) __attribute__((always_inline)) { return q_first + T * (n_qt - 1 - it / G); };
+    // Items: the query heads of the group innermost, the tiles from the last
+    // one down to the diagonal, so every key block of the group starts on
+    // the same tiles and they walk them together. Item it is head
+    // hkv·G + it % G, tile n_qt − 1 − it / G; the copy and compute cursors
+    // step through them without a division.
+    struct Cursor {
+        int hh, tt;
+    };
+    auto advance = [&](Cursor &c) __attribute__((always_inline)) {
+        if (++c.hh == G) {
+            c.hh = 0;
+            --c.tt;
+        }
+    };
     // copy j of a tile (wave w issues j = w, w + 4, ...): 0..7 Q rows
     // 4j .. 4j + 3, 8..15 dO rows, 16 LSE (lanes 0..31) and D (32..63).
     // Lane l lands at row 4j + l/16, physical chunk l % 16, so it reads
     // logical chunk (l % 16) ^ bswz(row).
-    auto issue_tile = [&](int it, TileBuf &t) __attribute__((always_inline)) {
-        const int h = item_h(it), q0 = item_q0(it);
+    auto issue_tile = [&](const Cursor &c, TileBuf &t) __attribute__((always_inline)) {
+        const int h = hkv * G + c.hh, q0 = q_first + T * c.tt;
         const size_t qoff = ((size_t)b * Hq + h) * N;
         for (int j = wave; j < TILE_COPIES; j += NWV) {  // wave-uniform
             if (j == TILE_COPIES - 1) {  // padded rows: q0 + 31 < Np
@@ -241,16 +250,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         }
     };
 
+    Cursor cp = {0, n_qt - 1}, cc = {0, n_qt - 1};  // next item to copy, to compute
     for (int t = 0; t < NRING - 1; ++t)
-        if (t < n_it) issue_tile(t, buf[t]);
+        if (t < n_it) {
+            issue_tile(cp, buf[t]);
+            advance(cp);
+        }
     wait_vmcnt<0>();
     regs_ready(kf);
     regs_ready(vf);
     __syncthreads();
     for (int it = 0; it < n_it; ++it) {
         // into the buffer of tile it − 1, which every wave is done with
-        if (it + NRING - 1 < n_it) issue_tile(it + NRING - 1, buf[(it + NRING - 1) % NRING]);
-        const int q0 = item_q0(it);
+        if (it + NRING - 1 < n_it) {
+            issue_tile(cp, buf[(it + NRING - 1) % NRING]);
+            advance(cp);
+        }
+        const int q0 = q_first + T * cc.tt;
+        advance(cc);
         const TileBuf &tb = buf[it % NRING];
         // the lane's read addresses; the lane index is made opaque so that they
         // are rebuilt per tile (a few VALU) rather than held in registers
