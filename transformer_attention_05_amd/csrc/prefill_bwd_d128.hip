@@ -40,6 +40,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace attn {
 namespace {
 
@@ -260,7 +262,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     regs_ready(kf);
     regs_ready(vf);
     __syncthreads();
-    for (int it = 0; it < n_it; ++it) {
+    // One item: copy ahead, then S, dP, P, dS and the dV, dK products. DIAG:
+    // the item may lie on or before a wave's diagonal (the block's first
+    // NWV query tiles), so waves whose keys it does not see skip it and
+    // the causal mask applies; the tiles after those are visible to every
+    // wave in full and take neither test.
+    auto step = [&](int it, auto diag_tag) __attribute__((always_inline)) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
         // into the buffer of tile it − 1, which every wave is done with
         if (it + NRING - 1 < n_it) {
             issue_tile(cp, buf[(it + NRING - 1) % NRING]);
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         int lane_x = lane;
         asm volatile("" : "+v"(lane_x));
         const SwzLane z = swz_lane(&tb, swz_off(lane_x));
-        if (q0 + T - 1 >= kw0) {  // some query of the tile sees some key of the wave
+        if (!DIAG || q0 + T - 1 >= kw0) {  // some query of the tile sees some key of the wave
             // ---- S = Q·Kᵀ and dP = dO·Vᵀ: rows = queries, lane column = key
             f32x16 s, dp;
 #pragma unroll
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
                 for (int j = 0; j < 4; ++j) {
                     const int i = 4 * gi + j;
                     float p = exp2_fast(fmaf(s[i], scale_log2, -Lr[j]));
-                    if (t > 8 * gi + j) p = 0.f;
+                    if (DIAG && t > 8 * gi + j) p = 0.f;
                     s[i] = p;
                     dp[i] = p * (dp[i] - Dr[j]);
                 }
@@ -328,7 +336,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             else wait_vmcnt<0>();
         }
         __syncthreads();
-    }
+    };
+    const int n_bulk = max(0, n_qt - NWV) * G;  // items on tiles q0 >= k0 + BLK
+    int it = 0;
+    for (; it < n_bulk; ++it) step(it, std::false_type{});
+    for (; it < n_it; ++it) step(it, std::true_type{});
 
     // ---- epilogue: dK = scale·(dKᵀ)ᵀ, dV; lane writes column `key`, rows d
     if (key < N) {
