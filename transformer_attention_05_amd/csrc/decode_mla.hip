@@ -689,7 +689,10 @@ bool mla_plan(int B, int Hq, int kv_len, MlaPlan *p)
     const long hgs = (Hq + MH - 1) / MH;
     const int tiles = (kv_len + MBC - 1) / MBC;
     const long groups = (long)B * hgs;
-    int want = (int)((kTargetGroups + groups - 1) / groups);
+    // one workgroup per CU: at most kTargetGroups workgroups, so that none
+    // waits for a second round (rounding the split count up would leave a
+    // few workgroups running alone after the rest)
+    int want = (int)(kTargetGroups / groups);
     int s = want < 1 ? 1 : (want < tiles ? want : tiles);
     if (s > kMaxSplits) s = kMaxSplits;
     const int per = (tiles + s - 1) / s;
@@ -711,7 +714,7 @@ bool mla_ragged_plan(int B, int Hq, int max_len, MlaPlan *p)
     // workers per head group: the P + B pieces (one workgroup each, one
     // workgroup per CU) should all run at once, or the last pieces, each
     // nearly a whole run, would start only when the first ones end
-    long P = (kTargetGroups + hgs - 1) / hgs - B;
+    long P = kTargetGroups / hgs - B;
     if (P < 16) P = 16;
     if (P > tiles_max) P = tiles_max;
     p->splits = (int)P;
