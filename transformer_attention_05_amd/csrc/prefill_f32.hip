@@ -15,6 +15,21 @@ namespace {
 
 constexpr int TR = 16, TC = 16;
 
+// This lane's share of K/V tile rows kt0 .. kt0 + TC − 1 (rows past N repeat
+// row N − 1) into registers.
+template <int D, int NL>
+__device__ __forceinline__ void fetch_kv_tile(f32x4 (&kr)[NL], f32x4 (&vr)[NL], const float *Kp,
+                                              const float *Vp, int kt0, int N, int lane)
+{
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+        const int idx = lane + 64 * t, row = idx / (D / 4), c4 = idx % (D / 4);
+        const int src = min(kt0 + row, N - 1);
+        kr[t] = *(const f32x4 *)(Kp + (size_t)src * D + 4 * c4);
+        vr[t] = *(const f32x4 *)(Vp + (size_t)src * D + 4 * c4);
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
@@ -38,10 +53,20 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
     const int lane = threadIdx.x, r = lane >> 2, sub = lane & 3;
     const int qrow = q0 + r;
 
-    for (int idx = lane; idx < TR * D / 4; idx += 64) {
-        const int row = idx / (D / 4), c4 = idx % (D / 4);
-        const int src = min(q0 + row, N - 1);
-        *(float4 *)&q_lds[row][4 * c4] = *(const float4 *)(Qp + (size_t)src * D + 4 * c4);
+    {
+        // all of the tile's loads first, then the stores: one round trip
+        constexpr int NQ = TR * D / 4 / 64;
+        f32x4 qr[NQ];
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+            const int idx = lane + 64 * t, row = idx / (D / 4), c4 = idx % (D / 4);
+            qr[t] = *(const f32x4 *)(Qp + (size_t)min(q0 + row, N - 1) * D + 4 * c4);
+        }
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+            const int idx = lane + 64 * t, row = idx / (D / 4), c4 = idx % (D / 4);
+            *(f32x4 *)&q_lds[row][4 * c4] = qr[t];
+        }
     }
 
     float oacc[DQ];
@@ -50,15 +75,30 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
     float m_run = -INFINITY, l_run = 0.f;
     const int n_kt = min(N - 1, q0 + TR - 1) / TC + 1;
 
+    // A tile's K/V loads (and the Q tile's) are all issued before its LDS
+    // stores: one round trip per tile instead of one per slice of rows. For
+    // d = 64 the K/V loads also run one tile ahead, in flight while the tile
+    // before is computed (rows past N repeat row N − 1, so the load after
+    // the last tile needs no condition); for d = 128 the 64 extra registers
+    // cost more than that overlap gives. Measured together: 12.2 → 10.0 µs
+    // for 2 heads × 64 queries (d = 64), 124.8 → 101.1 µs for 8 heads × 777
+    // (d = 64), 301.9 → 246.5 µs for 8 heads × 1024 (d = 128; 451 µs with
+    // the tile ahead).
+    constexpr bool AHEAD = D <= 64;
+    constexpr int NL = TC * D / 4 / 64;  // float4 of K (and of V) per lane per tile
+    f32x4 kr[NL], vr[NL];
+    if constexpr (AHEAD) fetch_kv_tile<D, NL>(kr, vr, Kp, Vp, 0, N, lane);
     for (int j = 0; j < n_kt; ++j) {
         const int kt0 = j * TC;
         __syncthreads();  // previous tile fully consumed
-        for (int idx = lane; idx < TC * D / 4; idx += 64) {
-            const int row = idx / (D / 4), c4 = idx % (D / 4);
-            const int src = min(kt0 + row, N - 1);
-            *(float4 *)&k_lds[row][4 * c4] = *(const float4 *)(Kp + (size_t)src * D + 4 * c4);
-            *(float4 *)&v_lds[row][4 * c4] = *(const float4 *)(Vp + (size_t)src * D + 4 * c4);
+        if constexpr (!AHEAD) fetch_kv_tile<D, NL>(kr, vr, Kp, Vp, kt0, N, lane);
+#pragma unroll
+        for (int t = 0; t < NL; ++t) {
+            const int idx = lane + 64 * t, row = idx / (D / 4), c4 = idx % (D / 4);
+            *(f32x4 *)&k_lds[row][4 * c4] = kr[t];
+            *(f32x4 *)&v_lds[row][4 * c4] = vr[t];
         }
+        if constexpr (AHEAD) fetch_kv_tile<D, NL>(kr, vr, Kp, Vp, kt0 + TC, N, lane);
         __syncthreads();
         // scores for keys kt0 + 4·sub + c
         float s[4];
