@@ -70,7 +70,7 @@ attn_status decode_gqa_impl(const char *fn, const void *q, const void *k_cache,
         !aligned4(kv_lens))
         return fail(ATTN_ERR_UNSUPPORTED, "%s: tensors must be 16-byte aligned (o, lse, kv_lens: 4)", fn);
     attn::GqaPlan p;
-    attn::gqa_plan(B, Hq, Hkv, kv_len, &p, fp8);
+    attn::gqa_plan(B, Hq, Hkv, kv_len, &p, fp8, kv_lens != nullptr);
     if (fixed_scratch && p.ws_total > workspace_bytes)
         return fail(ATTN_ERR_WORKSPACE,
                     "%s: this shape needs %zu bytes of scratch; the library's static scratch holds "
@@ -279,12 +279,14 @@ attn_status attn_prefill_causal_backward(const void *q, const void *k, const voi
 
 size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len, int D)
 {
-    // one size serves both cache types: the larger of the two plans
-    attn::GqaPlan p, p8;
+    // one size serves both cache types and ragged batches: the largest plan
+    attn::GqaPlan p, p8, pr;
     if (D != 128 || !attn::gqa_plan(B, Hq, Hkv, kv_len, &p, false) ||
-        !attn::gqa_plan(B, Hq, Hkv, kv_len, &p8, true))
+        !attn::gqa_plan(B, Hq, Hkv, kv_len, &p8, true) ||
+        !attn::gqa_plan(B, Hq, Hkv, kv_len, &pr, false, true))
         return 0;
-    return p.ws_total > p8.ws_total ? p.ws_total : p8.ws_total;
+    size_t m = p.ws_total > p8.ws_total ? p.ws_total : p8.ws_total;
+    return m > pr.ws_total ? m : pr.ws_total;
 }
 
 attn_status attn_decode_gqa(const void *q, const void *k_cache, const void *v_cache, void *o,

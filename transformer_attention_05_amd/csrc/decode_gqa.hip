@@ -33,11 +33,11 @@
 // the workspace and a second kernel merges the partials through their
 // log-sum-exp (split-K merge, "AI Infra 入门…", §3). No workgroup waits for
 // another; the kernel boundary orders the partial writes before the merge.
-// Slots at or past kv_len are never read. In a uniform call the cache loads
-// carry the non-temporal hint (each cached byte is read once): 29.0 → 27.0 µs
-// for the Llama-3-8B call. A ragged batch, whose workgroups stream ranges of
-// up to half the cache, measured slower with it (119 → 129 µs) and loads
-// with the default policy.
+// Slots at or past kv_len are never read. The cache loads carry the
+// non-temporal hint (each cached byte is read once): 29.0 → 27.0 µs for the
+// Llama-3-8B call. A ragged batch is cut into pieces of at most 768 keys
+// (below), so its workgroups' ranges are short too; the hint measured
+// slower only while each of them streamed a whole sequence (119 → 129 µs).
 // When the number of (batch, K/V head) groups is a multiple of 8, the
 // workgroup ids are remapped so that all splits of group g run on XCD g % 8
 // (workgroups are dealt to the 8 XCDs round-robin by id), and the merge puts
@@ -69,6 +69,14 @@ namespace {
 #ifndef ATTN_GQA_TARGET_FP8
 #define ATTN_GQA_TARGET_FP8 256
 #endif
+// Ragged batches: the host knows only the longest length, and a split sized
+// for it leaves the shorter sequences' workgroups idle. Their keys are cut
+// into pieces of at most this many keys (the uniform split when that is
+// finer), so many short workgroups are dealt out as CUs free up. Measured on
+// 32 sequences of 263–7764 keys (8 K/V heads): one split per (b, K/V head)
+// 117.2 µs; pieces of 768 keys (11 splits) 103.2 µs, of 512 keys 107.4 µs,
+// of about 1000 keys 113.6 µs, of about 320 keys 112.9 µs.
+constexpr int kRaggedSplitKeys = 768;
 
 constexpr int kD = 128;
 constexpr int kWaves = 4;
@@ -354,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
 
 }  // namespace
 
-bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p, bool fp8)
+bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p, bool fp8, bool ragged)
 {
     if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv || kv_len < 1) return false;
     const int G = Hq / Hkv;
@@ -363,6 +371,7 @@ bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p, bool fp8)
     const int chunks = (kv_len + kChunk - 1) / kChunk;
     const long target = fp8 ? ATTN_GQA_TARGET_FP8 : ATTN_GQA_TARGET_BF16;
     int want = (int)((target + groups - 1) / groups);
+    if (ragged) want = max(want, (kv_len + kRaggedSplitKeys - 1) / kRaggedSplitKeys);
     int s = want < 1 ? 1 : (want < chunks ? want : chunks);
     if (s > kMaxSplits) s = kMaxSplits;
     const int per = (chunks + s - 1) / s;
@@ -386,10 +395,9 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
     float *ws_part = (float *)(w + p.ws_part);
     const dim3 grid(p.splits, Hkv, B), block(256);
     const int xcd = ATTN_GQA_XCD && (B * Hkv) % 8 == 0;
-    // the non-temporal hint pays for short per-workgroup ranges (uniform
-    // calls) and costs for the long ones of a ragged batch (measured both ways)
-    auto kern = kv_lens ? (fp8 ? decode_gqa_kernel<true, false> : decode_gqa_kernel<false, false>)
-                        : (fp8 ? decode_gqa_kernel<true, true> : decode_gqa_kernel<false, true>);
+    // non-temporal loads throughout (ragged batch in 512-key pieces: 113.3 µs
+    // with the default policy, 107.4 with the hint)
+    auto kern = fp8 ? decode_gqa_kernel<true, true> : decode_gqa_kernel<false, true>;
     kern<<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const char *)k, (const char *)v, (uint16_t *)o, lse, Hq,
         Hkv, Hq / Hkv, kv_len, kv_cap, scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part,

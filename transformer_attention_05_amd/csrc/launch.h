@@ -14,7 +14,7 @@ struct GqaPlan {
     size_t ws_ml, ws_part, ws_total;  // workspace byte offsets / size
 };
 // fp8: plan for an E4M3 cache (more, shorter splits)
-bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p, bool fp8);
+bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p, bool fp8, bool ragged = false);
 // kv_lens: NULL (every sequence holds kv_len keys) or a device array of B
 // per-sequence lengths, each clamped to [0, kv_len] by the kernel.
 // fp8: the caches hold OCP FP8 E4M3 codes (one byte per element) instead of bf16.
