@@ -203,8 +203,9 @@ attn_status attn_decode_gqa(const void *q, const void *k_cache,
                             size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace attn_decode_gqa, attn_decode_gqa_fp8 and
- * attn_decode_gqa_ragged need for this shape (0 if invalid); one size serves
- * all three (the E4M3 cache is split into more pieces). */
+ * attn_decode_gqa_ragged need for this shape (kv_len: the longest sequence
+ * for a ragged batch; 0 if invalid); one size serves all three (the plans
+ * differ: a ragged batch is cut into pieces of at most 768 keys). */
 size_t attn_decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int kv_len,
                                        int D);
 
@@ -257,10 +258,11 @@ attn_status attn_decode_gqa_fp8(const void *q, const void *k_cache,
  *            clamped to [0, max_kv_len]. A sequence of length 0 attends to
  *            nothing: its O is 0 and its LSE is −∞ (the empty sums).
  *   max_kv_len  the longest length in the batch (or any bound of it, at
- *            most kv_cap): it fixes the split of the cache and the
- *            workspace size, attn_decode_gqa_workspace_bytes(B, Hq, Hkv,
- *            max_kv_len, D). Work for splits past a sequence's length is
- *            skipped.
+ *            most kv_cap): it fixes the split of the cache (the uniform
+ *            call's split, or pieces of at most 768 keys when that is finer,
+ *            so short sequences do not leave CUs idle) and the workspace
+ *            size, attn_decode_gqa_workspace_bytes(B, Hq, Hkv, max_kv_len,
+ *            D). Work for splits past a sequence's length is skipped.
  *
  * Errors as for attn_decode_gqa with max_kv_len in the place of kv_len;
  * kv_lens NULL → ATTN_ERR_NULL_POINTER.
