@@ -7,10 +7,12 @@
 // Decomposition. Workgroup (split, hkv, b) owns keys
 // [split·split_keys, min(kv_len, (split+1)·split_keys)) of one K/V head and
 // all G = Hq/Hkv query heads that share it, so each K/V byte is loaded once
-// and used G times. The split count aims at one workgroup per CU for a bf16
-// cache and two for an E4M3 one (one round, no tail). Its four waves take 32-key chunks in turn and
-// software-pipeline them: the K and V loads of a wave's next chunk are in
-// flight while the current chunk is computed.
+// and used G times. The split count aims at one round of about 256
+// workgroups, one per CU, for either cache type (no tail); a ragged batch is
+// cut into pieces of at most 768 keys instead when that is finer. The four
+// waves of a workgroup take 32-key chunks in turn and software-pipeline them:
+// the K and V loads of a wave's next chunk are in flight while the current
+// chunk is computed.
 //
 // Per 32-key wave chunk:
 //   * Sᵀ = K·qᵀ on v_mfma_f32_16x16x32_bf16, keys as MFMA rows, the
