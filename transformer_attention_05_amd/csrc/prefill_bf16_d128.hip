@@ -26,10 +26,6 @@
 //               p = 2^(s·scale·log2 e − m) in one FMA + v_exp_f32, with the
 //               running max m and the rescale of ℓ and O by 2^(m_old − m_new)
 //               ("05 · Tích vô hướng…", §6), skipped when no lane's max moved.
-//               (ATTN_PF_LAZY=1 builds a variant whose reference max moves
-//               only when the running max outgrows it by more than 8, with O
-//               normalised by the sum of the bf16 weights it was built from:
-//               equal at 4K keys, ≈2.5 % slower at 32K.)
 //   Oᵀ += Vᵀ·Pᵀ P rounded to bf16 in registers (the Sᵀ accumulator layout is
 //               the B-operand layout); the Vᵀ operand comes straight from the
 //               row-major V tile through ds_read_b64_tr_b16.
@@ -53,71 +49,38 @@
 namespace attn {
 namespace {
 
-// Compile-time choices (the defaults are the measured best).
-#ifndef ATTN_PF_WAVES
-#define ATTN_PF_WAVES 8      // waves per workgroup (32 query rows each)
-#endif
-#ifndef ATTN_PF_NBUF
-#define ATTN_PF_NBUF 2       // K/V tile buffers in LDS (prefetch distance NBUF − 1)
-#endif
-#ifndef ATTN_PF_LAZY
-#define ATTN_PF_LAZY 0       // lazy reference max (1) or exact running max (0)
-#endif
-#ifndef ATTN_PF_SPLITMASK
-#define ATTN_PF_SPLITMASK 1  // separate code for diagonal tiles (1) or masks everywhere (0)
-#endif
-#ifndef ATTN_PF_VROWB
-#define ATTN_PF_VROWB 320    // V tile row stride in LDS (bytes)
-#endif
-#ifndef ATTN_PF_SCHED
-#define ATTN_PF_SCHED 0      // keep each 16-key step's transposed reads together
-#endif
-#ifndef ATTN_PF_PAIR
-#define ATTN_PF_PAIR 1       // bulk tiles two per barrier, ring of 4 tiles
-#endif
-#ifndef ATTN_PF_SWZ
-#define ATTN_PF_SWZ 1        // unpadded 256-byte tile rows with a chunk swizzle (else padded rows)
-#endif
-#ifndef ATTN_PF_BULK
-#define ATTN_PF_BULK 1       // separate loop for the tiles wholly visible to every wave
-#endif
-
-
-constexpr int NW = ATTN_PF_WAVES, NBUF = ATTN_PF_PAIR ? 4 : ATTN_PF_NBUF;
+// 8 waves of 32 query rows; a ring of four 64-key K/V tiles in unpadded,
+// swizzled 256-byte rows; the bulk tiles two per barrier. (Measured and not
+// kept: 4 waves, rings of 2, 3 and 5 tiles, padded rows of 272 and 320
+// bytes, one tile per barrier, masks evaluated on every tile, a lazy
+// reference max, sched_barrier groups of the transposed reads.)
+constexpr int NW = 8, NBUF = 4;
 constexpr int D = 128, BR = 32 * NW, BC = 64;
-constexpr int KROWB = ATTN_PF_SWZ ? 256 : 272;                 // LDS row strides (bytes)
-constexpr int VROWB = ATTN_PF_SWZ ? 256 : ATTN_PF_VROWB;
-constexpr int KSLOT = KROWB / 16, VSLOT = VROWB / 16;
-constexpr int KTILEB = BC * KROWB;        // 17 KiB
-constexpr int VTILEB = BC * VROWB;        // 18 KiB
+constexpr int ROWB = 256;                 // LDS row stride of the K and V tiles (bytes)
+constexpr int KTILEB = BC * ROWB;         // 16 KiB
+constexpr int VTILEB = BC * ROWB;         // 16 KiB
 constexpr int KLOADS = KTILEB / 1024, VLOADS = VTILEB / 1024;
 constexpr int KPW = (KLOADS + NW - 1) / NW, VPW = (VLOADS + NW - 1) / NW;
 constexpr int LOADS_MIN = KLOADS / NW + VLOADS / NW;  // loads every wave issues per tile
 constexpr int KS = D / 16, DB = D / 32;
 constexpr int kXcds = 8;
-constexpr float kLazy = 8.f;  // base-2 headroom before the reference max moves
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Global byte offset, within a K/V tile, of the 16 bytes that lane `lane` of
-// wave-wide direct load `idx` brings into LDS slot 64·idx + lane (rows of
-// `slots` 16-byte slots, the last slots of a row being padding). Rows past
-// `rows` (the end of the sequence) are clamped to the last valid row.
-// Swizzled rows (ATTN_PF_SWZ): 16-byte chunk c of tile row r sits at chunk
-// c ^ bswz(r). A score read takes one chunk of 16 rows per 16-lane phase of
-// ds_read_b128, a transposed value read 4 chunks of 4 consecutive rows per
-// 32-lane phase of ds_read_b64_tr_b16; the swizzle puts both on all 64 banks.
+// wave-wide direct load `idx` brings into LDS slot 64·idx + lane (a copy
+// fills 4 whole rows of 16 slots). Rows past `rows` (the end of the
+// sequence) are clamped to the last valid row. 16-byte chunk c of tile row r
+// sits at chunk c ^ bswz(r): a score read takes one chunk of 16 rows per
+// 16-lane phase of ds_read_b128, a transposed value read 4 chunks of 4
+// consecutive rows per 32-lane phase of ds_read_b64_tr_b16, and the swizzle
+// puts both on all 64 banks.
 __device__ __forceinline__ int bswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
-__device__ __forceinline__ uint32_t tile_src(int idx, int lane, int slots, int rows) {
+__device__ __forceinline__ uint32_t tile_src(int idx, int lane, int rows) {
     const int s = 64 * idx + lane;
-    if constexpr (ATTN_PF_SWZ) {  // a copy fills 4 whole rows
-        const int r = s / 16, c = (s % 16) ^ bswz(r);
-        return (uint32_t)(min(r, rows - 1) * (D * 2) + 16 * c);
-    }
-    const int r = min(s / slots, rows - 1);
-    const int c = min(s % slots, 15);       // pad slots repeat chunk 15
-    return (uint32_t)(r * (D * 2) + 16 * c);
+    const int r = s / 16, c = (s % 16) ^ bswz(r);
+    return (uint32_t)(min(r, rows - 1) * (D * 2) + 16 * c);
 }
 
 
@@ -183,9 +146,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     // this lane's source offsets for its wave's direct loads of a full tile
     uint32_t ksrc[KPW], vsrc[VPW];
 #pragma unroll
-    for (int t = 0; t < KPW; ++t) ksrc[t] = tile_src(min(wave + NW * t, KLOADS - 1), lane, KSLOT, BC);
+    for (int t = 0; t < KPW; ++t) ksrc[t] = tile_src(min(wave + NW * t, KLOADS - 1), lane, BC);
 #pragma unroll
-    for (int t = 0; t < VPW; ++t) vsrc[t] = tile_src(min(wave + NW * t, VLOADS - 1), lane, VSLOT, BC);
+    for (int t = 0; t < VPW; ++t) vsrc[t] = tile_src(min(wave + NW * t, VLOADS - 1), lane, BC);
 
     // Loads 0 .. NW·⌊LOADS/NW⌋ − 1 are spread evenly over the waves; the
     // remaining LOADS % NW go to the first waves.
@@ -207,10 +170,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         } else {  // last, partial tile: rows past the sequence repeat its last row
             for (int t = 0; t < KPW; ++t)
                 if (wave + NW * t < KLOADS)
-                    issue(kb + tile_src(wave + NW * t, lane, KSLOT, rows), &kt[buf][1024 * (wave + NW * t)]);
+                    issue(kb + tile_src(wave + NW * t, lane, rows), &kt[buf][1024 * (wave + NW * t)]);
             for (int t = 0; t < VPW; ++t)
                 if (wave + NW * t < VLOADS)
-                    issue(vb + tile_src(wave + NW * t, lane, VSLOT, rows), &vt[buf][1024 * (wave + NW * t)]);
+                    issue(vb + tile_src(wave + NW * t, lane, rows), &vt[buf][1024 * (wave + NW * t)]);
         }
     };
 
@@ -219,14 +182,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    // m_ref: the reference max the sums and the output are kept relative to;
-    // it trails the true running max by less than kLazy (base 2).
-    float m_ref = -INFINITY, l_run = 0.f, lq_run = 0.f;
+    // m_ref: the running max the sums and the output are kept relative to
+    float m_ref = -INFINITY, l_run = 0.f;
 
-    // per-lane LDS read offsets (bytes within a tile); the loops add constants
-    const int k_lane = col * KROWB + 16 * half;
+    // lane coordinates of the transposed V reads
     const int g = lane >> 4, e = (lane >> 2) & 3, cq = lane & 3;
-    const int v_lane = (4 * half + e) * VROWB + 32 * (g & 1) + 8 * cq;
 
     const int n_kt = min(kv_len - 1, q_off + q0 + BR - 1) / BC + 1;
     // key tiles [t_lo, t_hi) of this workgroup (a split's share, or all)
@@ -236,18 +196,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         t_lo = (int)((long)split * n_kt / S);
         t_hi = (int)((long)(split + 1) * n_kt / S);
     }
-    if (ATTN_PF_PAIR) {
-        // the first two tiles resident
-        for (int t = 0; t < 2; ++t)
-            if (t_lo + t < t_hi) load_tile(t_lo + t, t);
-        wait_vmcnt<0>();
-    } else {
-#pragma unroll
-        for (int t = 0; t < NBUF - 1; ++t)
-            if (t_lo + t < t_hi) load_tile(t_lo + t, t);
-        // the first tile resident: only the loads of later tiles may be outstanding
-        if (NBUF == 3 && t_hi - t_lo > 1) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
-    }
+    // the first two tiles resident
+    for (int t = 0; t < 2; ++t)
+        if (t_lo + t < t_hi) load_tile(t_lo + t, t);
+    wait_vmcnt<0>();
     regs_ready(qf);
     __syncthreads();
 
@@ -265,9 +217,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 a = ATTN_PF_SWZ
-                    ? *(const u32x4 *)(kb_ + (kb * 32 + col) * 256 + 16 * ((2 * ks + half) ^ bswz(col)))
-                    : *(const u32x4 *)(kb_ + k_lane + kb * 32 * KROWB + 32 * ks);
+                const u32x4 a =
+                    *(const u32x4 *)(kb_ + (kb * 32 + col) * ROWB + 16 * ((2 * ks + half) ^ bswz(col)));
                 sacc[kb] = mfma32x32x16(as<bf16x8>(a), qf[ks], sacc[kb]);
             }
         // ---- mask (key > query → −inf); lane's keys: kt0 + 32kb + 8(i/4) + 4half + i%4
@@ -286,14 +237,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
         const float m_tile = half_max(mx) * scale_log2;
-#if ATTN_PF_LAZY
-        // lazy rescale: move the reference only when the max outgrew it by
-        // more than kLazy, so 2^(s − m_ref) ≤ 2^kLazy (exact in real arithmetic:
-        // sums and output share the reference)
-        const bool move = m_tile > m_ref + kLazy;  // m_ref = −inf: first visible tile
-#else
-        const bool move = m_tile > m_ref;          // exact running max
-#endif
+        const bool move = m_tile > m_ref;  // m_ref = −inf: first visible tile
         if (__builtin_amdgcn_ballot_w64(move)) {
             const float m_new = move ? m_tile : m_ref;
             float alpha = exp2_fast(m_ref - m_new);  // 1 where not moved, 0 at first
@@ -302,7 +246,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
             // (reference −∞ on both sides), and their empty sums stay empty
             if (CHUNK && m_new == -INFINITY) alpha = 1.f;
             l_run *= alpha;
-            lq_run *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
             m_ref = m_new;
@@ -320,39 +263,29 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
             }
         l_run += ps;
         // ---- Pᵀ fragments: 16-key step mm uses S registers 8(mm%2)..+7 of block
-        // mm/2. With the lazy reference the largest weight is not 1, so lq sums
-        // the same bf16-rounded weights the product uses and O is normalised by
-        // it: O is then an exact weighted average of the weights it was built
-        // from (a one-hot row stays exact); the LSE uses the fp32 sum.
+        // mm/2 (the largest weight of a row is exactly 1: the running max
+        // defines the reference)
         bf16x8 pf[4];
-        float pq = 0.f;
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
             u32x4 wv;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < 4; ++t)
                 wv[t] = pack_bf16x2(sacc[mm / 2][8 * (mm % 2) + 2 * t], sacc[mm / 2][8 * (mm % 2) + 2 * t + 1]);
-                if (ATTN_PF_LAZY) pq = sum_bf16x2(wv[t], pq);
-            }
             pf[mm] = as<bf16x8>(wv);
         }
-        if (ATTN_PF_LAZY) lq_run += pq;
         // ---- Oᵀ += Vᵀ Pᵀ; A slot t ↔ key 16mm + 8(t/4) + 4half + t%4.
         // Lane 16g + 4e + c addresses V rows 16mm + 4half + e (and + 8),
         // columns 32db + 16(g&1) + 4c .. + 3.
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) {
-            if (ATTN_PF_SCHED && mm) __builtin_amdgcn_sched_barrier(0);  // keep each step's reads together
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const char *p1 = vb_ + v_lane + 16 * mm * VROWB + 64 * db, *p2 = p1 + 8 * VROWB;
-                if constexpr (ATTN_PF_SWZ) {
-                    // rows 16mm + 4half + e (+ 8): swizzle 4e + half (+ 2)
-                    const int low = 2 * (g & 1) + (cq >> 1);
-                    const char *r0 = vb_ + (16 * mm + 4 * half + e) * 256 + 64 * (db ^ e) + 8 * (cq & 1);
-                    p1 = r0 + 16 * (low ^ half);
-                    p2 = r0 + 8 * 256 + 16 * (low ^ (half + 2));
-                }
+                // rows 16mm + 4half + e (+ 8): swizzle 4e + half (+ 2)
+                const int low = 2 * (g & 1) + (cq >> 1);
+                const char *r0 = vb_ + (16 * mm + 4 * half + e) * ROWB + 64 * (db ^ e) + 8 * (cq & 1);
+                const char *p1 = r0 + 16 * (low ^ half);
+                const char *p2 = r0 + 8 * ROWB + 16 * (low ^ (half + 2));
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p1);
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p2);
                 const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -369,8 +302,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
     // forth every tile).
     // (in a ragged last query tile the waves past the last query run the
     // bulk tiles too; their rows are never written)
-    const int n_bulk = ATTN_PF_BULK ? (q_off + q0 + 1) / BC : 0;
-#if ATTN_PF_PAIR
+    const int n_bulk = (q_off + q0 + 1) / BC;
     // Bulk tiles two at a time, one barrier per pair: the next pair's copies
     // go into the two buffers the last barrier freed while this pair is
     // computed (ring of 4).
@@ -402,38 +334,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
         if (ahead) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
         __syncthreads();
     }
-#else
-    for (int j = t_lo; j < min(n_bulk, t_hi); ++j) {
-        const int cur = (j - t_lo) % NBUF;
-        const int jn = j + NBUF - 1;  // tile to prefetch
-        if (jn < t_hi) load_tile(jn, (jn - t_lo) % NBUF);
-        tile_step(kt[cur], vt[cur], j * BC, std::false_type{});
-        if (NBUF == 3 && jn < t_hi) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
-        __syncthreads();
-    }
-    // Tail: the tiles around the diagonal, classified per wave.
-    for (int j = max(n_bulk, t_lo); j < t_hi; ++j) {
-        const int cur = (j - t_lo) % NBUF;
-        const int jn = j + NBUF - 1;  // tile to prefetch
-        if (jn < t_hi) load_tile(jn, (jn - t_lo) % NBUF);
-        const int kt0 = j * BC;
-#if ATTN_PF_SPLITMASK
-        if (wrow0 < N && kt0 + BC - 1 <= wrow0 + q_off)  // wholly visible to the wave
-            tile_step(kt[cur], vt[cur], kt0, std::false_type{});
-        else if (wrow0 < N && kt0 <= wrow1 + q_off)      // crosses the wave's diagonal
-            tile_step(kt[cur], vt[cur], kt0, std::true_type{});
-#else
-        if (wrow0 < N && kt0 <= wrow1 + q_off) tile_step(kt[cur], vt[cur], kt0, std::true_type{});
-#endif
-        // tile j+1 resident before the barrier; newer prefetches may stay in flight
-        if (NBUF == 3 && jn < t_hi) wait_vmcnt<LOADS_MIN>(); else wait_vmcnt<0>();
-        __syncthreads();
-    }
 
-#endif
-
-    // ---- epilogue: O = Oᵀ/ℓq, one rounding; LSE (natural log) from the fp32 sum
-    const float l_tot = half_sum(l_run), lq_tot = half_sum(lq_run);
+    // ---- epilogue: O = Oᵀ/ℓ, one rounding; LSE (natural log) from the fp32 sum
+    const float l_tot = half_sum(l_run);
     if (CHUNK && S > 1) {
         // partial of this key range: Õ relative to m_ref (rows that saw no
         // key here: m = −∞, sums and Õ zero), merged through the LSE later
@@ -449,12 +352,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_d128_kernel(
                     __builtin_nontemporal_store(w4, (f32x4 *)(prow + db * 32 + 8 * gg + 4 * half));
                 }
             if (half == 0)
-                *(float4 *)(ws_ml + 4 * slot) = make_float4(m_ref, l_tot, ATTN_PF_LAZY ? lq_tot : l_tot, 0.f);
+                *(float4 *)(ws_ml + 4 * slot) = make_float4(m_ref, l_tot, l_tot, 0.f);
         }
         return;
     }
     if (qrow < N) {
-        const float inv = 1.f / (ATTN_PF_LAZY ? lq_tot : l_tot);
+        const float inv = 1.f / l_tot;
         uint16_t *orow = o + ((size_t)bhq * N + qrow) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
