@@ -65,12 +65,7 @@ namespace {
 // Workgroups per launch the split aims at: one per CU, for a bf16 and for
 // an E4M3 cache (both measured best of 256 / 512 / 1024 once the next
 // chunk's loads stay in flight during compute).
-#ifndef ATTN_GQA_TARGET_BF16
-#define ATTN_GQA_TARGET_BF16 256
-#endif
-#ifndef ATTN_GQA_TARGET_FP8
-#define ATTN_GQA_TARGET_FP8 256
-#endif
+constexpr long kTargetGroups = 256;
 // Ragged batches: the host knows only the longest length, and a split sized
 // for it leaves the shorter sequences' workgroups idle. Their keys are cut
 // into pieces of at most this many keys (the uniform split when that is
@@ -103,19 +98,13 @@ template <> struct Chunk<true> {
     u32x4 v[4];     // row 8·i + lane/8, E4M3 bytes d = 16·(lane%8) .. + 15
 };
 
-#ifndef ATTN_GQA_XCD
-#define ATTN_GQA_XCD 1  // a group's splits, and its merge rows, on one XCD
-#endif
-// Cache loads, with the non-temporal hint when NT (every byte is read once).
-template <bool NT>
+// Cache loads carry the non-temporal hint (every cache byte is read once).
 __device__ __forceinline__ u32x4 ld_cache(const char *p) {
-    if constexpr (NT) return __builtin_nontemporal_load((const u32x4 *)p);
-    else return *(const u32x4 *)p;
+    return __builtin_nontemporal_load((const u32x4 *)p);
 }
 
 // One wave's chunk of 32 keys from w0 (rows past key_end repeat its last).
 // kb, vb: the (b, hkv) cache rows, kD elements of 2 (bf16) or 1 (E4M3) bytes.
-template <bool NT>
 __device__ __forceinline__ void load_chunk(Chunk<false> &c, const char *kb, const char *vb,
                                            int w0, int key_end, int hcol, int quad, int)
 {
@@ -124,15 +113,14 @@ __device__ __forceinline__ void load_chunk(Chunk<false> &c, const char *kb, cons
         const int key = min(w0 + 16 * blk + hcol, key_end - 1);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            c.k[blk][s] = ld_cache<NT>(kb + 2 * ((size_t)key * kD + 32 * s + 8 * quad));
+            c.k[blk][s] = ld_cache(kb + 2 * ((size_t)key * kD + 32 * s + 8 * quad));
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int key = min(w0 + 4 * i + quad, key_end - 1);
-        c.v[i] = ld_cache<NT>(vb + 2 * ((size_t)key * kD + 8 * hcol));
+        c.v[i] = ld_cache(vb + 2 * ((size_t)key * kD + 8 * hcol));
     }
 }
-template <bool NT>
 __device__ __forceinline__ void load_chunk(Chunk<true> &c, const char *kb, const char *vb,
                                            int w0, int key_end, int hcol, int quad, int lane)
 {
@@ -141,12 +129,12 @@ __device__ __forceinline__ void load_chunk(Chunk<true> &c, const char *kb, const
         const int key = min(w0 + 16 * blk + hcol, key_end - 1);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            c.k[blk][h] = ld_cache<NT>(kb + (size_t)key * kD + 32 * quad + 16 * h);
+            c.k[blk][h] = ld_cache(kb + (size_t)key * kD + 32 * quad + 16 * h);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int key = min(w0 + 8 * i + (lane >> 3), key_end - 1);
-        c.v[i] = ld_cache<NT>(vb + (size_t)key * kD + 16 * (lane & 7));
+        c.v[i] = ld_cache(vb + (size_t)key * kD + 16 * (lane & 7));
     }
 }
 
@@ -167,7 +155,7 @@ __device__ __forceinline__ bf16x8 k_operand(const Chunk<true> &c, int blk, int s
     return as<bf16x8>(u32x4{a[0], a[1], b[0], b[1]});
 }
 
-template <bool FP8, bool NT>
+template <bool FP8>
 __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     const uint16_t *__restrict__ q, const char *__restrict__ kc,
     const char *__restrict__ vc, uint16_t *__restrict__ o, float *__restrict__ lse,
@@ -314,14 +302,14 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(
     // issued, and then also waits for the next chunk when it was.
     const int first = key_begin + wave * kWaveKeys;
     Chunk<FP8> ca, cb;
-    if (first < key_end) load_chunk<NT>(ca, kbase, vbase, first, key_end, hcol, quad, lane);
+    if (first < key_end) load_chunk(ca, kbase, vbase, first, key_end, hcol, quad, lane);
     for (int w0 = first; w0 < key_end; w0 += 2 * kChunk) {
         const int w1 = w0 + kChunk;
-        load_chunk<NT>(cb, kbase, vbase, w1, key_end, hcol, quad, lane);
+        load_chunk(cb, kbase, vbase, w1, key_end, hcol, quad, lane);
         compute(ca, w0);
         if (w1 >= key_end) break;
         const int w2 = w1 + kChunk;
-        load_chunk<NT>(ca, kbase, vbase, w2, key_end, hcol, quad, lane);
+        load_chunk(ca, kbase, vbase, w2, key_end, hcol, quad, lane);
         compute(cb, w1);
     }
 
@@ -371,8 +359,7 @@ bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p, bool fp8, bool rag
     if (G > 16) return false;
     const long groups = (long)B * Hkv;
     const int chunks = (kv_len + kChunk - 1) / kChunk;
-    const long target = fp8 ? ATTN_GQA_TARGET_FP8 : ATTN_GQA_TARGET_BF16;
-    int want = (int)((target + groups - 1) / groups);
+    int want = (int)((kTargetGroups + groups - 1) / groups);
     if (ragged) want = max(want, (kv_len + kRaggedSplitKeys - 1) / kRaggedSplitKeys);
     int s = want < 1 ? 1 : (want < chunks ? want : chunks);
     if (s > kMaxSplits) s = kMaxSplits;
@@ -396,10 +383,11 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
     float *ws_ml = (float *)(w + p.ws_ml);
     float *ws_part = (float *)(w + p.ws_part);
     const dim3 grid(p.splits, Hkv, B), block(256);
-    const int xcd = ATTN_GQA_XCD && (B * Hkv) % 8 == 0;
+    // a group's splits, and its merge rows, on one XCD (group count a multiple of 8)
+    const int xcd = (B * Hkv) % 8 == 0;
     // non-temporal loads throughout (ragged batch in 512-key pieces: 113.3 µs
     // with the default policy, 107.4 with the hint)
-    auto kern = fp8 ? decode_gqa_kernel<true, true> : decode_gqa_kernel<false, true>;
+    auto kern = fp8 ? decode_gqa_kernel<true> : decode_gqa_kernel<false>;
     kern<<<grid, block, 0, st>>>(
         (const uint16_t *)q, (const char *)k, (const char *)v, (uint16_t *)o, lse, Hq,
         Hkv, Hq / Hkv, kv_len, kv_cap, scale * kLog2e, p.splits, p.split_keys, ws_ml, ws_part,

@@ -141,23 +141,15 @@ typedef __attribute__((address_space(3))) i32x2 lds_v2i32;
 // copy_to_lds16_sv: addressed as a wave-uniform base plus a per-lane 32-bit
 // byte offset (the scalar-base form of the instruction), so a full tile's
 // copies need no per-lane address arithmetic.
-#ifndef ATTN_MLA_NT
-#define ATTN_MLA_NT 1  // tile copies with the non-temporal hint (every cache byte is read once)
-#endif
+// Both forms carry the non-temporal hint: every cache byte is read once.
 __device__ __forceinline__ void copy_to_lds16_sv(const void *base, uint32_t off, const void *lds_block) {
     const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_char *)lds_block;
-    if constexpr (ATTN_MLA_NT)
-        asm volatile("global_load_lds_dwordx4 %0, %1 nt" :: "v"(off), "s"(base), "{m0}"(m0) : "memory");
-    else
-        asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(base), "{m0}"(m0) : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" :: "v"(off), "s"(base), "{m0}"(m0) : "memory");
 }
 // the per-lane-address form, for partial tiles
 __device__ __forceinline__ void copy_to_lds16_v(const void *src, const void *lds_block) {
     const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_char *)lds_block;
-    if constexpr (ATTN_MLA_NT)
-        asm volatile("global_load_lds_dwordx4 %0, off nt" :: "v"(src), "{m0}"(m0) : "memory");
-    else
-        asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m0) : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, off nt" :: "v"(src), "{m0}"(m0) : "memory");
 }
 
 // Physical 16-byte chunk holding logical chunk c of tile row r (an involution).
