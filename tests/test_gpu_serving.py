@@ -101,7 +101,12 @@ def _check_ragged(o, lse, o_ref, lse_ref, lens, what):
     (32, 8, [4096, 17, 1000, 2048, 0, 3, 4095, 128], 4096, 4096),
     (4, 1, [10, 20], 1000, 1000),                  # max_kv_len only a bound
     (16, 1, [255, 256, 257, 64, 65, 63], 257, 260),
-    (24, 8, [1, 1, 1], 1, 8)])                      # a single split
+    (24, 8, [1, 1, 1], 1, 8),                       # a single split
+    # 256 (b, K/V head) groups: the plan is 3 pieces of at most 768 keys,
+    # lengths on and around the piece boundaries
+    (8, 8, [0, 1, 767, 768, 769, 1535, 1536, 1537, 2000, 483, 1352, 184, 428, 635, 619, 1818,
+            1599, 1831, 1992, 157, 284, 1736, 157, 332, 361, 1828, 719, 527, 339, 917, 1178,
+            1601], 2000, 2048)])
 def test_decode_gqa_ragged_matches_oracle(gpu, Hq, Hkv, lens, max_len, kv_cap):
     B = len(lens)
     w = workloads.gen_decode_gqa(B, Hq, Hkv, D=128, kv_cap=kv_cap, kv_lens=lens, seed=B + Hq)
