@@ -272,10 +272,12 @@ def bench_workload(torch, attn, workloads, name, steps, warmup, dev, plain=False
                 work_per_call=(nbytes if unit == "GB/s" else flops))
 
 
-# sources of each workload kind's kernels: a counter summary counts only while
-# they are unchanged
+# sources of each workload kind's kernels (paths under csrc/): a counter
+# summary counts only while they are unchanged. The GQA decode also names
+# build.py, which gives its bf16 unit a compile option of its own.
 KIND_SRCS = {
-    "decode_gqa": ("decode_gqa.hip", "merge.hip", "common.h", "ragged.h"),
+    "decode_gqa": ("decode_gqa_kernel.h", "decode_gqa.hip", "decode_gqa_fp8.hip", "merge.hip",
+                   "common.h", "ragged.h", "../build.py"),
     "decode_mla": ("decode_mla.hip", "merge.hip", "common.h", "ragged.h"),
     "prefill": ("prefill_bf16_d128.hip", "prefill_bf16.hip", "prefill_f32.hip", "common.h"),
     "prefill_chunked": ("prefill_bf16_d128.hip", "merge.hip", "common.h"),

@@ -23,16 +23,26 @@ LIB = os.path.join(PKG, "libattn.so")
 PROBE_LIB = os.path.join(PKG, "libattn_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.cpp", "decode_gqa.hip", "prefill_bf16.hip", "prefill_f32.hip",
-           "prefill_bf16_d128.hip", "prefill_bwd_d128.hip", "decode_mla.hip", "merge.hip"]
+SOURCES = ["attn_api.cpp", "decode_gqa.hip", "decode_gqa_fp8.hip", "prefill_bf16.hip",
+           "prefill_f32.hip", "prefill_bf16_d128.hip", "prefill_bwd_d128.hip", "decode_mla.hip",
+           "merge.hip"]
 FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
+# Per-unit options. The bf16 GQA decode kernel is scheduled by LLVM's max-ILP
+# machine scheduler: it issues the chunk's V rows to LDS after one wait for
+# the chunk and the transposed operand reads ahead of the P·V products,
+# where the default schedule interleaves them with a wait per load. Measured
+# against the default in one process (graph replay, bit-identical output):
+# Llama-3-8B call 25.15 → 24.65 µs, ragged 8K batch 103.2 → 102.7 µs. The
+# E4M3 instantiation (15.0 → 15.5 µs), the MLA decode (174 → 235 µs, it
+# spills) and the prefill (4k 567 → 576 µs) keep the default.
+EXTRA_FLAGS = {"decode_gqa.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (r.stdout + r.stderr).splitlines()
             if "packed-fp32-ops" not in l and l.strip()]

@@ -10,10 +10,11 @@ namespace attn {
 // ---- GQA decode ----------------------------------------------------------
 struct GqaPlan {
     int splits;      // workgroups per (batch, K/V head)
-    int split_keys;  // keys per split (multiple of the 256-key chunk)
+    int split_keys;  // keys per split (multiple of the 128-key workgroup step)
     size_t ws_ml, ws_part, ws_total;  // workspace byte offsets / size
 };
-// fp8: plan for an E4M3 cache (more, shorter splits)
+// fp8: plan for an E4M3 cache; ragged: a batch with per-sequence lengths
+// (pieces of at most 768 keys when that is finer than the uniform split)
 bool gqa_plan(int B, int Hq, int Hkv, int kv_len, GqaPlan *p, bool fp8, bool ragged = false);
 // kv_lens: NULL (every sequence holds kv_len keys) or a device array of B
 // per-sequence lengths, each clamped to [0, kv_len] by the kernel.
@@ -22,6 +23,12 @@ hipError_t launch_decode_gqa(const GqaPlan &p, const void *q, const void *k, con
                              void *o, float *lse, int B, int Hq, int Hkv, int kv_len,
                              int kv_cap, float scale, void *ws, hipStream_t s,
                              const int *kv_lens, bool fp8);
+// The E4M3 split kernel alone (decode_gqa_fp8.hip); xcd: the XCD remap of
+// the workgroup ids is on.
+hipError_t launch_decode_gqa_split_fp8(const GqaPlan &p, const void *q, const void *k,
+                                       const void *v, void *o, float *lse, int B, int Hq,
+                                       int Hkv, int kv_len, int kv_cap, float scale, void *ws,
+                                       hipStream_t s, const int *kv_lens, int xcd);
 
 // ---- causal prefill ------------------------------------------------------
 hipError_t launch_prefill_bf16(const void *q, const void *k, const void *v, void *o,
