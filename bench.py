@@ -358,12 +358,12 @@ def summarize_counters(fetch_db: str, write_db: str, name: str) -> dict:
         "hbm_bytes_per_call": round(total),
         "algorithmic_bytes_per_call": algo,
         "traffic_over_algorithmic": None if not algo else round(total / algo, 4),
-        "commands": ["rocprofv3 --pmc FETCH_SIZE -d gpurun_out/ctr/%s/fetch -o fetch -- python3 -u "
+        "commands": ["rocprofv3 --pmc FETCH_SIZE -d prof/ctr/%s/fetch -o fetch -- python3 -u "
                      "bench.py --counters --only %s" % (name, name),
-                     "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/ctr/%s/write -o write -- python3 -u "
+                     "rocprofv3 --pmc WRITE_SIZE -d prof/ctr/%s/write -o write -- python3 -u "
                      "bench.py --counters --only %s" % (name, name),
-                     "python3 bench.py --summarize-counters gpurun_out/ctr/%s/fetch/fetch_results.db "
-                     "gpurun_out/ctr/%s/write/write_results.db --only %s" % (name, name, name)],
+                     "python3 bench.py --summarize-counters prof/ctr/%s/fetch/fetch_results.db "
+                     "prof/ctr/%s/write/write_results.db --only %s" % (name, name, name)],
     }
 
 
