@@ -513,6 +513,7 @@ def ceilings(torch, dev):
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.attn_probe_stream_read.argtypes = [vp, sz, i, vp, vp]
     lib.attn_probe_valu.argtypes = [i, i, i, vp, vp, vp]
+    lib.attn_probe_stream_ranges.argtypes = [vp, sz, i, i, i, vp, vp]
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     out = {}
@@ -534,6 +535,28 @@ def ceilings(torch, dev):
             best = max(best, (gbs, blocks))
         out["stream_read_%dMiB_GBs" % mib] = round(best[0], 1)
         out["stream_read_%dMiB_blocks" % mib] = best[1]
+        if mib == 128:
+            # each workgroup streams its own range, as a decode split does:
+            # µs per 128 MiB by workgroups x threads x loads per batch per lane
+            ranges = {}
+            for blocks, threads, inflight in ((64, 256, 32), (64, 1024, 8), (128, 256, 32),
+                                              (128, 1024, 8), (256, 256, 8), (256, 256, 16),
+                                              (256, 256, 32)):
+                def go(k):
+                    rc = lib.attn_probe_stream_ranges(vp(bufs[k % 3].data_ptr()), nbytes, blocks,
+                                                      threads, inflight, vp(sink.data_ptr()), st)
+                    assert rc == 0, rc
+                for k in range(3):
+                    go(k)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 12
+                e0.record()
+                for r in range(reps):
+                    go(r)
+                e1.record()
+                torch.cuda.synchronize()
+                ranges["%dx%dx%d" % (blocks, threads, inflight)] = round(e0.elapsed_time(e1) * 1e3 / reps, 1)
+            out["stream_ranges_128MiB_us"] = ranges
         del bufs
     blocks, iters = 1024, 4096
     res = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
@@ -546,7 +569,9 @@ def ceilings(torch, dev):
         waves_per_simd = blocks * 4 / 1024.0  # 256 CUs x 4 SIMDs
         out["cycles_per_wave_op_%s" % key] = round(per_wave / (iters * 8) / waves_per_simd, 2)
     out["note"] = ("stream read: best over 256..4096 workgroups, 16-byte non-temporal loads, "
-                   "rotating three buffers; cycles: 16 waves per CU, eight independent chains per "
+                   "rotating three buffers; stream ranges: workgroups x threads x 16-byte loads "
+                   "per lane issued as one batch, each workgroup reading its own contiguous range; "
+                   "cycles: 16 waves per CU, eight independent chains per "
                    "lane, per 2^x (or FMA) per SIMD")
     return out
 

@@ -6,6 +6,10 @@
 //     of the caller's size. Its best rate over a few grid sizes is the read
 //     bandwidth a decode kernel can hope for on this GPU (the 8 TB/s HBM
 //     figure is the interface peak; a read-only kernel reaches less).
+//   * attn_probe_stream_ranges: the same read with each workgroup streaming
+//     its own contiguous range, as one split of a decode does, with a given
+//     number of workgroups, threads per workgroup and loads per batch: how
+//     the rate depends on the CUs in use and on the bytes in flight.
 //   * attn_probe_valu: per-wave timing (shader clock) of long runs of
 //     independent v_exp_f32 (the transcendental unit the online softmax's
 //     2^x uses), of fp32 FMAs, and of a software 2^x built from FMAs
@@ -35,6 +39,37 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restric
     }
     for (; i < n16; i += stride) {
         const u32x4 v = src[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; almost never stores
+}
+
+// Workgroup b reads elements [b·per, (b + 1)·per) of src in batches of U
+// loads of 16 bytes per lane (T threads); every load of a batch is issued
+// before any of them is used, so a lane has up to U in flight and the batch
+// drains before the next one starts. One workgroup per CU is the use case:
+// the waves per SIMD are pinned to T / 256, which leaves the compiler the
+// registers for a whole batch (with only the launch bound it trades them for
+// occupancy and keeps about a dozen loads in flight).
+template <int T, int U>
+__global__ __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(T / 256, T / 256)))
+void stream_ranges_kernel(const u32x4 *__restrict__ src, size_t per, uint32_t *__restrict__ sink)
+{
+    const u32x4 *p = src + (size_t)blockIdx.x * per;
+    size_t i = threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (size_t)(U - 1) * T < per; i += (size_t)U * T) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + (size_t)u * T);
+        // the scheduler would otherwise interleave the uses and their waits
+        // with the loads
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (; i < per; i += T) {
+        const u32x4 v = p[i];
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
     if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; almost never stores
@@ -91,6 +126,27 @@ extern "C" {
 int attn_probe_stream_read(const void *src, size_t nbytes, int blocks, void *sink, hipStream_t st)
 {
     stream_read_kernel<4><<<blocks, 256, 0, st>>>((const u32x4 *)src, nbytes / 16, (uint32_t *)sink);
+    return (int)hipGetLastError();
+}
+
+// Reads nbytes (a multiple of 16·blocks) from src, workgroup b streaming the
+// b-th of `blocks` equal contiguous ranges with `threads` threads in batches
+// of `batch` 16-byte loads per lane, each batch issued whole before it is
+// used. (threads, batch) is one of (256, 8), (256, 16), (256, 32),
+// (1024, 8); anything else returns hipErrorInvalidValue and launches
+// nothing. Returns a hipError_t code.
+int attn_probe_stream_ranges(const void *src, size_t nbytes, int blocks, int threads, int batch,
+                             void *sink, hipStream_t st)
+{
+    if (blocks < 1 || nbytes % (16 * (size_t)blocks)) return (int)hipErrorInvalidValue;
+    const size_t per = nbytes / 16 / (size_t)blocks;
+    const u32x4 *s = (const u32x4 *)src;
+    uint32_t *k = (uint32_t *)sink;
+    if (threads == 256 && batch == 8) stream_ranges_kernel<256, 8><<<blocks, 256, 0, st>>>(s, per, k);
+    else if (threads == 256 && batch == 16) stream_ranges_kernel<256, 16><<<blocks, 256, 0, st>>>(s, per, k);
+    else if (threads == 256 && batch == 32) stream_ranges_kernel<256, 32><<<blocks, 256, 0, st>>>(s, per, k);
+    else if (threads == 1024 && batch == 8) stream_ranges_kernel<1024, 8><<<blocks, 1024, 0, st>>>(s, per, k);
+    else return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
 }
 
