@@ -514,6 +514,8 @@ def ceilings(torch, dev):
     lib.attn_probe_stream_read.argtypes = [vp, sz, i, vp, vp]
     lib.attn_probe_valu.argtypes = [i, i, i, vp, vp, vp]
     lib.attn_probe_stream_ranges.argtypes = [vp, sz, i, i, i, vp, vp]
+    lib.attn_probe_mfma_valu.argtypes = [i, i, i, i, vp, vp, vp]
+    lib.attn_probe_lds_read.argtypes = [i, i, i, i, vp, vp, vp]
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     out = {}
@@ -568,11 +570,45 @@ def ceilings(torch, dev):
         per_wave = cyc.double().mean().item()
         waves_per_simd = blocks * 4 / 1024.0  # 256 CUs x 4 SIMDs
         out["cycles_per_wave_op_%s" % key] = round(per_wave / (iters * 8) / waves_per_simd, 2)
+    # one wave per SIMD: shader-clock cycles per step of MFMAs (32x32x16 bf16)
+    # plus independent fp32 FMAs
+    blocks, iters = 1024, 2000
+    res = torch.empty(blocks * 64, dtype=torch.float32, device=dev)
+    cyc = torch.zeros(blocks, dtype=torch.int64, device=dev)
+    steps = {}
+    for mf, nv in ((1, 0), (1, 4), (1, 8), (1, 16), (2, 8), (2, 16), (0, 8), (0, 16)):
+        for r in range(2):
+            rc = lib.attn_probe_mfma_valu(mf, nv, blocks, iters, vp(res.data_ptr()), vp(cyc.data_ptr()), st)
+            assert rc == 0, rc
+        torch.cuda.synchronize()
+        steps["%d_mfma_%d_fma" % (mf, nv)] = round(cyc.double().median().item() / (iters * 4), 1)
+    out["cycles_per_step_one_wave"] = steps
+    # LDS read rate per CU, one workgroup of 8 or 16 waves per CU
+    blocks, iters = 256, 4096
+    lds = {}
+    for kind, key, nbytes in ((0, "ds_read_b128", 16), (1, "ds_read_b64_tr_b16", 8)):
+        for threads in (512, 1024):
+            res = torch.empty(blocks * threads, dtype=torch.int32, device=dev)
+            cyc = torch.zeros(blocks * threads // 64, dtype=torch.int64, device=dev)
+            for r in range(2):
+                rc = lib.attn_probe_lds_read(kind, threads, blocks, iters, vp(res.data_ptr()),
+                                             vp(cyc.data_ptr()), st)
+                assert rc == 0, rc
+            torch.cuda.synchronize()
+            waves = threads // 64
+            # a workgroup's waves start together after its fill; its slowest
+            # wave spans the CU's reads
+            span = cyc.double().view(blocks, waves).max(dim=1).values.median().item()
+            lds["%s_%dwaves" % (key, waves)] = round(waves * iters * 8 * 64 * nbytes / span, 1)
+    out["lds_read_bytes_per_clock_per_cu"] = lds
     out["note"] = ("stream read: best over 256..4096 workgroups, 16-byte non-temporal loads, "
                    "rotating three buffers; stream ranges: workgroups x threads x 16-byte loads "
                    "per lane issued as one batch, each workgroup reading its own contiguous range; "
                    "cycles: 16 waves per CU, eight independent chains per "
-                   "lane, per 2^x (or FMA) per SIMD")
+                   "lane, per 2^x (or FMA) per SIMD; one-wave steps: MFMAs into four "
+                   "accumulators and FMAs in eight chains, median over 1024 waves; LDS reads: "
+                   "eight per wave in flight, conflict-free addresses, bytes of all the CU's waves "
+                   "over its slowest wave's cycles, median over CUs")
     return out
 
 

@@ -10,6 +10,14 @@
 //     its own contiguous range, as one split of a decode does, with a given
 //     number of workgroups, threads per workgroup and loads per batch: how
 //     the rate depends on the CUs in use and on the bytes in flight.
+//   * attn_probe_mfma_valu: can one wave hide its own vector work under its
+//     matrix work? Shader-clock cycles per step of MF 32×32×16 bf16 MFMAs
+//     (independent accumulators) and NV fp32 FMAs (independent chains), one
+//     wave per SIMD.
+//   * attn_probe_lds_read: LDS read rate per CU of ds_read_b128 (16 bytes per
+//     lane) and of the transposing ds_read_b64_tr_b16 (8 bytes per lane), on
+//     conflict-free addresses, with 8 or 16 waves per CU and eight reads in
+//     flight per wave.
 //   * attn_probe_valu: per-wave timing (shader clock) of long runs of
 //     independent v_exp_f32 (the transcendental unit the online softmax's
 //     2^x uses), of fp32 FMAs, and of a software 2^x built from FMAs
@@ -22,6 +30,10 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int UNROLL>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restrict__ src, size_t n16,
@@ -73,6 +85,92 @@ void stream_ranges_kernel(const u32x4 *__restrict__ src, size_t per, uint32_t *_
         acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
     if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads; almost never stores
+}
+
+// One wave per workgroup; each step issues MF MFMAs (32×32×16 bf16 into four
+// independent accumulators, round robin) and NV FMAs (eight independent
+// chains). cyc[b]: the wave's shader-clock cycles over `iters` × 4 steps.
+template <int MF, int NV>
+__global__ __launch_bounds__(64) void mfma_valu_kernel(float *__restrict__ out,
+                                                       unsigned long long *__restrict__ cyc, int iters)
+{
+    const int lane = threadIdx.x;
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * (float)(lane + i));
+        b[i] = (__bf16)(0.002f * (float)(lane - i));
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[k][i] = 0.f;
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = 1.0f + 0.01f * (float)(lane + k);
+    const unsigned long long t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+            for (int f = 0; f < MF; ++f)
+                acc[(m + f) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[(m + f) & 3], 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) x[v & 7] = fmaf(x[v & 7], 0.999f, 0.0001f);
+        }
+    }
+    const unsigned long long t1 = __builtin_readcyclecounter();
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += acc[k][i];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += x[k];
+    out[(size_t)blockIdx.x * 64 + lane] = s;
+    if (lane == 0) cyc[blockIdx.x] = t1 - t0;
+}
+
+// LDS read rate. The workgroup fills a 64 KiB buffer, then each wave issues
+// `iters` rounds of eight reads (all eight issued before any is used) at
+// conflict-free addresses: KIND 0 ds_read_b128, lane l at byte 16·l of a
+// 1 KiB slot; KIND 1 ds_read_b64_tr_b16, lane l at byte 8·l of a 512-byte
+// slot (64 slots either way, all inside the buffer). cyc[w]: wave w's
+// shader-clock cycles over the rounds.
+template <int KIND, int T>
+__global__ __launch_bounds__(T) void lds_read_kernel(uint32_t *__restrict__ out,
+                                                     unsigned long long *__restrict__ cyc, int iters)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t buf[65536 / 4];
+    for (int i = threadIdx.x; i < 65536 / 4; i += T) buf[i] = (uint32_t)i * 2654435761u;
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const char *base = (const char *)buf;
+    constexpr int SLOT = KIND == 0 ? 1024 : 512, BYTES = KIND == 0 ? 16 : 8;
+    uint32_t acc = 0;
+    const unsigned long long t0 = __builtin_readcyclecounter();
+    for (int it = 0; it < iters; ++it) {
+        u32x4 v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int off = ((it * 8 + r + wave) & 63) * SLOT + BYTES * lane;
+            if constexpr (KIND == 0) {
+                v[r] = *(const u32x4 *)(base + off);
+            } else {
+                const i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(const_cast<char *>(base) + off));
+                const uint32_t *w = (const uint32_t *)&t;
+                v[r] = u32x4{w[0], w[1], 0u, 0u};
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc ^= v[r][0] ^ v[r][1] ^ v[r][2] ^ v[r][3];
+    }
+    const unsigned long long t1 = __builtin_readcyclecounter();
+    out[(size_t)blockIdx.x * T + threadIdx.x] = acc;
+    if (lane == 0) cyc[(size_t)blockIdx.x * (T / 64) + wave] = t1 - t0;
 }
 
 // 2^x from FMAs: x = n + f with n = rint(x), f in [−½, ½]; 2^f by a degree-6
@@ -146,6 +244,36 @@ int attn_probe_stream_ranges(const void *src, size_t nbytes, int blocks, int thr
     else if (threads == 256 && batch == 16) stream_ranges_kernel<256, 16><<<blocks, 256, 0, st>>>(s, per, k);
     else if (threads == 256 && batch == 32) stream_ranges_kernel<256, 32><<<blocks, 256, 0, st>>>(s, per, k);
     else if (threads == 1024 && batch == 8) stream_ranges_kernel<1024, 8><<<blocks, 1024, 0, st>>>(s, per, k);
+    else return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+}
+
+// mf MFMAs and nv FMAs per step, (mf, nv) one of (1, 0), (1, 4), (1, 8),
+// (1, 16), (2, 8), (2, 16), (0, 8), (0, 16); `blocks` one-wave workgroups
+// (1024 puts one wave on every SIMD); cyc[b] gets workgroup b's cycles over
+// iters × 4 steps, out one float per lane. Anything else returns
+// hipErrorInvalidValue and launches nothing.
+int attn_probe_mfma_valu(int mf, int nv, int blocks, int iters, float *out, unsigned long long *cyc,
+                         hipStream_t st)
+{
+#define ATTN_MV(M, N) \
+    if (mf == M && nv == N) { mfma_valu_kernel<M, N><<<blocks, 64, 0, st>>>(out, cyc, iters); return (int)hipGetLastError(); }
+    ATTN_MV(1, 0) ATTN_MV(1, 4) ATTN_MV(1, 8) ATTN_MV(1, 16) ATTN_MV(2, 8) ATTN_MV(2, 16) ATTN_MV(0, 8) ATTN_MV(0, 16)
+#undef ATTN_MV
+    return (int)hipErrorInvalidValue;
+}
+
+// kind 0: ds_read_b128, 1: ds_read_b64_tr_b16; threads 512 or 1024 (8 or 16
+// waves per workgroup, one workgroup per CU when blocks = 256). cyc gets one
+// entry per wave (blocks × threads / 64), out one word per thread. Anything
+// else returns hipErrorInvalidValue and launches nothing.
+int attn_probe_lds_read(int kind, int threads, int blocks, int iters, uint32_t *out,
+                        unsigned long long *cyc, hipStream_t st)
+{
+    if (kind == 0 && threads == 512) lds_read_kernel<0, 512><<<blocks, 512, 0, st>>>(out, cyc, iters);
+    else if (kind == 0 && threads == 1024) lds_read_kernel<0, 1024><<<blocks, 1024, 0, st>>>(out, cyc, iters);
+    else if (kind == 1 && threads == 512) lds_read_kernel<1, 512><<<blocks, 512, 0, st>>>(out, cyc, iters);
+    else if (kind == 1 && threads == 1024) lds_read_kernel<1, 1024><<<blocks, 1024, 0, st>>>(out, cyc, iters);
     else return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
 }
