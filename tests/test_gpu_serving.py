@@ -84,6 +84,20 @@ def test_prefill_chunked_4k_on_32k_workload_sampled_rows(gpu):
                "prefill_chunked_4k_on_32k")
 
 
+def test_prefill_chunked_512_on_32k_workload_sampled_rows(gpu):
+    """The short-chunk serving shape (a 512-token chunk after 32256 cached
+    tokens, 32/8 heads), which the launcher runs as key splits merged
+    through their log-sum-exp: every output finite; the oracle checks the
+    first, last and tile-boundary rows of every head."""
+    w = workloads.make("prefill_chunked_512_on_32k")
+    o, lse = _chunked(gpu, w)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    rows = [0, 1, 31, 32, 63, 64, 255, 256, 510, 511]
+    o_ref, lse_ref = oracle.prefill_chunked(w.q, w.k, w.v, w.kv_lens, w.scale, rows=rows)
+    check_bf16(host(o[:, :, rows]), o_ref, host(lse[:, :, rows]), lse_ref,
+               "prefill_chunked_512_on_32k")
+
+
 # ------------------------------------------------------------------ ragged GQA ---
 def _check_ragged(o, lse, o_ref, lse_ref, lens, what):
     """Empty sequences: O = 0 and LSE = −∞ exactly; the rest by the rule."""
@@ -220,6 +234,20 @@ def test_decode_mla_ragged_fp8_equals_bf16_copy(gpu):
     o16, l16 = gpu.attn_decode_mla_ragged(q, c16, kl, 4096, w.Dv, w.scale)
     torch.cuda.synchronize()
     assert _same(o8, o16) and _same(l8, l16)
+
+
+def test_decode_mla_ragged_fp8_32k_workload_sampled_heads(gpu):
+    """The E4M3 ragged batch as timed (16 sequences of 1024..32768 latent
+    rows): all outputs finite; the oracle, reading the same codes, checks 8
+    of the 128 heads of every sequence, one in each 16-head block."""
+    w = workloads.make("decode_mla_ragged_fp8_32k")
+    o, lse = gpu.attn_decode_mla_ragged_fp8(dev_bf16(w.q), _dev_u8(w.ckv), _lens(w.kv_lens),
+                                            w.kv_len, w.Dv, w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    hs = list(range(3, 128, 16))
+    o_ref, lse_ref = oracle.decode_mla_ragged(w.q[:, hs], w.ckv, w.kv_lens, w.Dv, w.scale)
+    check_bf16(host(o[:, hs]), o_ref, host(lse[:, hs]), lse_ref, "decode_mla_ragged_fp8_32k")
 
 
 # ------------------------------------------------------- one graph, new lengths ---
