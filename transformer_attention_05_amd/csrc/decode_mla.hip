@@ -55,7 +55,8 @@
 // term changes no bank; without it the compiler shares address registers
 // between the two 16-row halves and runs out of registers.)
 // Splits of the cache write fp32 (m, ℓ, λ, Õ) partials with streaming
-// (non-temporal) stores that do not stay dirty in L2; the shared merge kernel
+// (non-temporal) stores that do not stay dirty in L2, Õ staged through LDS so
+// that every store writes whole 128-byte lines; the shared merge kernel
 // combines them through their log-sum-exp. Rows at or past kv_len are never
 // read.
 // E4M3 cache (F8): the stored rows are the channel-balanced latent S·c, so
@@ -664,12 +665,39 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
     // the partial output Õ is stored in fp32, as accumulated: the merge
     // rounds the output once, and any value bf16 can hold fits
     if (own && quad == 0) *(float4 *)(ws_ml + 4 * rec(head)) = make_float4(m_ref, l_e, l_o, 0.f);
+    // Õ goes out one 16-head block at a time through LDS, so that each store
+    // instruction writes 1 KiB of one row (whole 128-byte lines): from the
+    // accumulators a lane holds 16 bytes of 16 different rows, and stored
+    // directly every instruction wrote 64 bytes per row. The block is staged
+    // as [head][512 channels] with 16-byte chunk c of row r at c ^ r, which
+    // keeps both the writes (16 rows × 4 chunks) and the row reads on all
+    // banks; two staging buffers (the tile ring and the LDS-held Q, both
+    // free now) alternate, so one barrier per block suffices.
+    wait_vmcnt<0>();   // no tile copy may still be landing in the ring
+    __syncthreads();   // every wave is done with the ring and its Q fragments
+    float *const stage[2] = {(float *)&tile[0][0], (float *)&q_lds[0][0][0]};
+    static_assert(sizeof(tile) >= 16 * MV * 4 && sizeof(q_lds) >= 16 * MV * 4, "staging");
 #pragma unroll
     for (int hb = 0; hb < MHB; ++hb) {
         if (hb >= nhb) break;
-        float *prow = ws_part + rec(hg * MH + 16 * hb + hcol) * MV + MDW * wave + 4 * quad;
+        float *buf = stage[hb & 1];
 #pragma unroll
-        for (int db = 0; db < MDBW; ++db) __builtin_nontemporal_store(oacc[db][hb], (f32x4 *)(prow + 16 * db));
+        for (int db = 0; db < MDBW; ++db) {
+            const int c = (MDW / 4) * wave + 4 * db + quad;  // chunk of row hcol
+            *(f32x4 *)(buf + hcol * MV + 4 * (c ^ hcol)) = oacc[db][hb];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rr = 0; rr < 16 / MW; ++rr) {
+            const int r = (16 / MW) * wave + rr;
+            float *prow = ws_part + rec(hg * MH + 16 * hb + r) * MV;
+#pragma unroll
+            for (int h = 0; h < MV / 256; ++h) {
+                const int c = 64 * h + lane;
+                const f32x4 v = *(const f32x4 *)(buf + r * MV + 4 * (c ^ r));
+                __builtin_nontemporal_store(v, (f32x4 *)(prow + 4 * c));
+            }
+        }
     }
 }
 
