@@ -54,11 +54,13 @@
 // (8 rows × 32 B per 32-lane phase) over all 64 LDS banks. (The row / 16
 // term changes no bank; without it the compiler shares address registers
 // between the two 16-row halves and runs out of registers.)
-// Splits of the cache write fp32 (m, ℓ, λ, Õ) partials with streaming
-// (non-temporal) stores that do not stay dirty in L2, Õ staged through LDS so
-// that every store writes whole 128-byte lines; the shared merge kernel
-// combines them through their log-sum-exp. Rows at or past kv_len are never
-// read.
+// Splits of the cache write fp32 (m, ℓ, λ, Õ) partials, Õ staged through LDS
+// so that every store writes whole 128-byte lines; the shared merge kernel
+// combines them through their log-sum-exp. The stores take the default cache
+// policy: with whole lines written, the merge then finds part of the records
+// on chip (measured against non-temporal stores in one process: 32K call
+// 183.3 → 180.0 µs, ragged batch 111.7 → 110.3 µs). Rows at or past kv_len
+// are never read.
 // E4M3 cache (F8): the stored rows are the channel-balanced latent S·c, so
 // every channel fits E4M3's range ("MLA 矩阵乘法吸收的数值稳定性治理", §二.1).
 // Tiles of 32 rows × 576 B are copied the same way; a score operand is
@@ -695,7 +697,7 @@ __global__ __launch_bounds__(MTHREADS, 1) void decode_mla_kernel(
             for (int h = 0; h < MV / 256; ++h) {
                 const int c = 64 * h + lane;
                 const f32x4 v = *(const f32x4 *)(buf + r * MV + 4 * (c ^ r));
-                __builtin_nontemporal_store(v, (f32x4 *)(prow + 4 * c));
+                *(f32x4 *)(prow + 4 * c) = v;
             }
         }
     }
