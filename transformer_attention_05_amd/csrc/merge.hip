@@ -38,9 +38,7 @@ __device__ __forceinline__ void merge_row(const float4 *__restrict__ mr, size_t 
                                           int t)
 {
     // splits are taken SPT at a time with every load of a pass in flight at
-    // once (one memory round trip when splits <= SPT); each record is read
-    // once, so its loads carry the non-temporal hint (MLA 32K call 180.0 →
-    // 179.7 µs, ragged batch 110.3 → 109.9 µs); across passes the
+    // once (one memory round trip when splits <= SPT); across passes the
     // running max grows and earlier sums are rescaled, like the online
     // softmax itself
     float M = -INFINITY, l = 0.f, lam = 0.f, acc[CPT];
@@ -55,7 +53,7 @@ __device__ __forceinline__ void merge_row(const float4 *__restrict__ mr, size_t 
             st[u] = mr[(size_t)s * mstride];
             const float *pr = pr_ + (size_t)s * pstride;
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) x[u][c] = __builtin_nontemporal_load(pr + c);
+            for (int c = 0; c < CPT; ++c) x[u][c] = pr[c];
         }
         float Mn = M;
 #pragma unroll
